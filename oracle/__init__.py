@@ -1,0 +1,17 @@
+"""CPU oracle for safetensors -> bf16 weight materialisation.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product path (the HIP library and its Python
+binding) never imports, links or calls anything here, and nothing here imports the product.
+
+Parity status: every function is pinned by the not-gpu tests (format round trips against the
+safetensors library, brute-force code tables against torch's float8 decoding, rounding against
+torch's bfloat16 cast, closed forms with power-of-two scales, index-mapping tests with
+position-coded scales, worked witnesses).  One reading has no external pin: the nibble order
+of packed e2m1 bytes (element 2k in the low nibble), which no library available here decodes;
+it is pinned only by its closed-form self-consistency tests ("parity unpinned" beyond that).
+"""
+from .st_oracle import (  # noqa: F401
+    OracleError, Entry, Header, Output, parse_header, validate_layout, classify, plan,
+    e4m3_value, e2m1_value, E4M3, E2M1, bf16_rne, decode, materialize,
+)
