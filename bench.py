@@ -1,0 +1,215 @@
+"""Benchmark of the grouped materialise kernel on one MI355X.
+
+One step = one st_materialize launch over every descriptor of a seeded synthetic checkpoint whose
+blob is already resident in HBM (staging is measured separately).  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--all] [--no-cpu]
+
+Default workload: the scaled-FP8 DiT-style checkpoint (57 blocks of e4m3fn weights with per-tensor
+fp32 scales plus bf16 vectors).  ``--all`` adds the other four checkpoint families to the line
+under "formats".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import tempfile
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "materialise GB/s (read+write) and % of HBM peak per checkpoint format"
+
+WORKLOADS = {
+    1: "tiny mixed blob: 2 bf16 [256,256], 2 fp32 [512], 2 e4m3fn [384,256] + fp32 scale, 2 fp16 [64,1000], unaligned",
+    2: "scaled-FP8 DiT checkpoint: 57 blocks of e4m3fn [3072,3072]x4, [12288,3072], [3072,12288] with fp32 "
+       "per-tensor scale_weight, 7 bf16 [3072] vectors per block",
+    3: "block-FP8 LLM checkpoint: 28 layers, hidden 4096, e4m3fn q/k/v/o [4096,4096], gate/up [12288,4096], "
+       "down [4096,12288] with fp32 128x128 weight_scale_inv grids, bf16 embedding [151936,4096] and norms",
+    4: "NVFP4 checkpoint: 40 layers of [25600,5120] and [5120,25600] packed e2m1 with e4m3fn scale per 16 "
+       "elements and fp32 global scale",
+    5: "many-small-tensor stress blob: 20,000 tensors of 64 B - 64 KB, bf16/fp16/fp32/scaled-e4m3fn, unaligned",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--all", action="store_true", help="also measure the other checkpoint families")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--unit-scale", type=int, default=0)
+    ap.add_argument("--tmpdir", default=None)
+    ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
+    return ap.parse_args()
+
+
+def gen(k, d):
+    import synth
+    path = os.path.join(d, f"synthetic_c{k}.safetensors")
+    t0 = time.perf_counter()
+    last = [t0]
+
+    def progress(done, total):
+        now = time.perf_counter()
+        if now - last[0] > 10 or done == total:
+            last[0] = now
+            log(f"[bench] generating config {k}: {done}/{total} tensor groups, {now - t0:.0f}s")
+
+    synth.write_config(k, path, progress=progress)
+    dt = time.perf_counter() - t0
+    log(f"[bench] generated config {k}: {os.path.getsize(path) / 1e9:.3f} GB in {dt:.1f}s")
+    return path, dt
+
+
+def sampled_parity(path, ix, ck, rng, per_output=64):
+    """GPU outputs at random flat indices (plus first and last) against the oracle computed
+    element by element on the same indices."""
+    import torch
+    import oracle
+    mm = np.memmap(path, dtype=np.uint8, mode="r")
+    h, outs = oracle.plan(mm)
+    data = mm[h.data_offset:]
+    checked = 0
+    for o in outs:
+        if o.numel == 0:
+            continue
+        idx = np.unique(np.concatenate([[0, o.numel - 1], rng.integers(0, o.numel, per_output)]))
+        want = oracle.decode(o, data, idx)
+        t = ck.tensors[o.name].reshape(-1)
+        got = t[torch.from_numpy(idx).to(t.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+        if not np.array_equal(got, want):
+            return False, checked, o.name
+        checked += len(idx)
+    return True, checked, None
+
+
+def cpu_baseline(path, budget_s):
+    """The oracle as it stands, single-threaded NumPy, on whole outputs in file order until the
+    time budget is spent; GB/s over the same algorithmic bytes (bytes read + bf16 bytes written)."""
+    import oracle
+    mm = np.memmap(path, dtype=np.uint8, mode="r")
+    h, outs = oracle.plan(mm)
+    data = mm[h.data_offset:]
+    nbytes = 0
+    done = 0
+    t0 = time.perf_counter()
+    with np.errstate(invalid="ignore", over="ignore"):
+        for o in outs:
+            oracle.decode(o, data)
+            nbytes += (o.src.end - o.src.begin) + (o.scale.end - o.scale.begin if o.scale else 0) + \
+                (o.scale2.end - o.scale2.begin if o.scale2 else 0) + 2 * o.numel
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {len(outs)} outputs in file order ({nbytes / 1e9:.3f} GB of traffic) "
+                      f"decoded by the single-threaded NumPy oracle in {dt:.1f}s"}
+
+
+def measure(k, d, args, rng):
+    import torch
+    import device_checkpoint_dequantisation_amd as st
+    path, gen_s = gen(k, d)
+    t0 = time.perf_counter()
+    ix = st.SafeTensorIndex.open(path, args.unit_scale)
+    index_ms = (time.perf_counter() - t0) * 1e3
+    dev = torch.device("cuda:0")
+    ck = st.DeviceCheckpoint(ix, None, dev)
+    pinned = torch.empty(512 << 20, dtype=torch.uint8, pin_memory=True)
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    read_s = st.stage_file(path, ix, ck.blob, pinned, side)
+    side.synchronize()
+    stage_s = time.perf_counter() - t0
+    del pinned
+    traffic = ix.traffic_bytes
+    log(f"[bench] config {k}: {ix.num_outputs} outputs, traffic {traffic / 1e9:.3f} GB, index {index_ms:.1f} ms, "
+        f"staged {ix.data_size / 1e9:.3f} GB in {stage_s:.2f}s (reads {read_s:.2f}s)")
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        ck.materialize(stream, args.grid)
+    torch.cuda.synchronize()
+    ok, checked, bad = sampled_parity(path, ix, ck, rng)
+    log(f"[bench] sampled parity vs oracle: {'ok' if ok else 'MISMATCH in ' + str(bad)} ({checked} elements)")
+    # timed region: K back-to-back launches, wall clock + per-launch HIP events on the same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        ck.materialize(stream, args.grid)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in evs])
+    res = {
+        "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
+        "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
+        "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min()), "index_ms": index_ms,
+        "stage": {"file_to_pinned_GBps": ix.data_size / read_s / 1e9 if read_s > 0 else None,
+                  "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)"},
+        "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
+    }
+    res["GBps"] = traffic / (res["ms_per_step"] * 1e-3) / 1e9
+    res["kernel_GBps"] = traffic / (res["kernel_ms_mean"] * 1e-3) / 1e9
+    del ck
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the materialise path is "
+              f"per-GPU independent and is not sharded in this build)", file=sys.stderr)
+        sys.exit(2)
+    rng = np.random.default_rng(0)
+    d = args.tmpdir or tempfile.mkdtemp(prefix="stmat_bench_")
+    configs = [args.config] + ([k for k in (1, 2, 3, 4, 5) if k != args.config] if args.all else [])
+    results = {}
+    cpu = None
+    for k in configs:
+        results[k] = measure(k, d, args, rng)
+        if k == args.config and not args.no_cpu:
+            cpu = cpu_baseline(results[k]["path"], args.cpu_seconds)
+            log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+        if not args.keep:
+            os.remove(results[k]["path"])
+    r = results[args.config]
+    line = {
+        "metric": METRIC, "value": round(r["GBps"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "read_bytes": r["read"], "written_bytes": r["written"],
+                   "outputs": r["outputs"], "hbm_peak_frac": round(r["GBps"] / HBM_PEAK_GBPS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(r["kernel_GBps"], 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(r["kernel_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "kernel_ms": {"mean": round(r["kernel_ms_mean"], 4), "median": round(r["kernel_ms_median"], 4),
+                      "min": round(r["kernel_ms_min"], 4)},
+        "staging": r["stage"], "index_build_ms": round(r["index_ms"], 2), "parity": r["parity"],
+    }
+    if args.all:
+        line["formats"] = {
+            f"c{k}": {"GBps": round(v["GBps"], 2), "hbm_peak_frac": round(v["GBps"] / HBM_PEAK_GBPS, 4),
+                      "kernel_ms_mean": round(v["kernel_ms_mean"], 4), "traffic_bytes": v["traffic"],
+                      "parity": v["parity"], "staging": v["stage"]} for k, v in results.items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+"""stmat: materialise safetensors checkpoint weights as bf16 tensors on an MI355X.
+
+Python binding of libstmat.so (include/stmat.h).  It only marshals arguments: the header index,
+the descriptor plan, staging and the decode all run in the library; torch provides device
+memory and streams.
+
+    idx = SafeTensorIndex.open(path)           # metadata only, no tensor bytes read
+    ckpt = DeviceCheckpoint(idx, path)         # VRAM pre-check, blob + outputs, staging
+    ckpt.materialize()                         # one grouped kernel launch
+    ckpt.tensors["model.layers.0.mlp.up_proj.weight"]   # bf16 torch tensor on the GPU
+
+or simply ``load(path)`` -> {name: bf16 tensor}.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import json
+import os
+from dataclasses import dataclass
+
+from ._lib import DTYPES, KINDS, Desc, OutputInfo, PlanOpts, StError, TensorMeta, check, lib  # noqa: F401
+
+__all__ = ["SafeTensorIndex", "DeviceCheckpoint", "load", "materialize", "stage_file", "StError", "KINDS"]
+
+
+@dataclass(frozen=True)
+class TensorEntry:
+    name: str
+    dtype: str
+    shape: tuple
+    begin: int
+    end: int
+
+
+@dataclass(frozen=True)
+class OutputEntry:
+    name: str
+    kind: str
+    shape: tuple
+    numel: int
+    tensor: int
+    scale: int
+    scale2: int
+    offset: int      # byte offset in the output arena
+
+
+class SafeTensorIndex:
+    """Metadata-only index of one safetensors file (the header alone is read)."""
+
+    def __init__(self, handle: int):
+        self._h = C.c_void_p(handle)
+
+    @classmethod
+    def open(cls, path: str, unit_log2_scale: int = 0) -> "SafeTensorIndex":
+        h = C.c_void_p()
+        opts = PlanOpts(unit_log2_scale, 0)
+        check(lib().st_index_open(os.fsencode(path), C.byref(opts), C.byref(h)), f"st_index_open({path})")
+        return cls(h.value)
+
+    @classmethod
+    def from_bytes(cls, buf: bytes, file_size: int | None = None, unit_log2_scale: int = 0) -> "SafeTensorIndex":
+        """Index from the leading bytes of a file (at least 8 + N) of ``file_size`` bytes
+        (default: ``buf`` is the whole file)."""
+        h = C.c_void_p()
+        opts = PlanOpts(unit_log2_scale, 0)
+        size = len(buf) if file_size is None else file_size
+        raw = C.create_string_buffer(bytes(buf), len(buf))
+        check(lib().st_index_build(raw, len(buf), size, C.byref(opts), C.byref(h)), "st_index_build")
+        return cls(h.value)
+
+    def close(self):
+        if self._h and self._h.value:
+            lib().st_index_free(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- sizes
+    @property
+    def data_offset(self) -> int:
+        return lib().st_index_data_offset(self._h)
+
+    @property
+    def data_size(self) -> int:
+        return lib().st_index_data_size(self._h)
+
+    @property
+    def blob_bytes(self) -> int:
+        return lib().st_index_blob_bytes(self._h)
+
+    @property
+    def arena_bytes(self) -> int:
+        return lib().st_index_output_arena_bytes(self._h)
+
+    @property
+    def traffic_bytes(self) -> int:
+        return lib().st_index_traffic_bytes(self._h)
+
+    @property
+    def device_bytes(self) -> int:
+        return lib().st_index_device_bytes(self._h)
+
+    @property
+    def metadata(self) -> dict:
+        return json.loads(lib().st_index_metadata_json(self._h).decode("utf-8"))
+
+    # ---- entries
+    def __len__(self) -> int:
+        return lib().st_index_count(self._h)
+
+    def tensor(self, i: int) -> TensorEntry:
+        m = TensorMeta()
+        check(lib().st_index_tensor(self._h, i, C.byref(m)), "st_index_tensor")
+        return TensorEntry(m.name.decode("utf-8"), DTYPES[m.dtype], tuple(m.shape[: m.ndim]), m.begin, m.end)
+
+    def tensors(self) -> list:
+        return [self.tensor(i) for i in range(len(self))]
+
+    def find(self, name: str) -> int:
+        return lib().st_index_find(self._h, name.encode("utf-8"))
+
+    @property
+    def num_outputs(self) -> int:
+        return lib().st_index_num_outputs(self._h)
+
+    def output(self, k: int) -> OutputEntry:
+        o = OutputInfo()
+        check(lib().st_index_output(self._h, k, C.byref(o)), "st_index_output")
+        return OutputEntry(o.name.decode("utf-8"), KINDS[o.kind], tuple(o.shape[: o.ndim]), o.numel, o.tensor,
+                           o.scale, o.scale2, lib().st_index_output_offset(self._h, k))
+
+    def outputs(self) -> list:
+        return [self.output(k) for k in range(self.num_outputs)]
+
+    def keys(self) -> list:
+        """Output (weight) names, in output order; metadata only."""
+        return [self.output(k).name for k in range(self.num_outputs)]
+
+    # ---- descriptor tables
+    def descs(self):
+        """(bytes of the full descriptor table, number of descriptors, total work units)."""
+        n, nb, units = C.c_size_t(), C.c_size_t(), C.c_uint64()
+        p = lib().st_index_descs(self._h, C.byref(n), C.byref(nb), C.byref(units))
+        return (C.string_at(p, nb.value) if nb.value else b""), n.value, units.value
+
+    def descs_subset(self, sel):
+        """Self-contained table for outputs ``sel`` (descriptor j writes outs[j])."""
+        k = len(sel)
+        arr = (C.c_uint32 * max(1, k))(*sel)
+        dst = (Desc * max(1, k))()
+        units = C.c_uint64()
+        check(lib().st_index_descs_subset(self._h, arr, k, dst, C.sizeof(dst), C.byref(units)), "st_index_descs_subset")
+        return C.string_at(dst, k * C.sizeof(Desc)), k, units.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> float:
+    """Copy the file's data section into ``blob`` (device uint8 tensor of index.blob_bytes) through
+    the pinned uint8 host tensor ``pinned`` on ``side_stream``; returns seconds spent reading."""
+    secs = C.c_double()
+    check(lib().st_stage_file(os.fsencode(path), index._h, C.c_void_p(blob.data_ptr()), C.c_void_p(pinned.data_ptr()),
+                              pinned.numel(), C.c_void_p(side_stream.cuda_stream), None, C.byref(secs)),
+          "st_stage_file")
+    return secs.value
+
+
+def materialize(blob, descs, n: int, outs, stream=None, grid: int = 0):
+    """Enqueue the grouped kernel: ``blob``, ``descs`` (n * 64 bytes) and ``outs`` (n device
+    pointers, int64) are device tensors."""
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(blob.device)
+    check(lib().st_materialize_grid(C.c_void_p(blob.data_ptr()), C.c_void_p(descs.data_ptr()), n,
+                                    C.c_void_p(outs.data_ptr()), grid, C.c_void_p(s.cuda_stream)), "st_materialize")
+
+
+class DeviceCheckpoint:
+    """A checkpoint staged on one GPU: the blob, the descriptor table and a bf16 output arena in
+    which every output starts on a 256-byte boundary."""
+
+    def __init__(self, index: SafeTensorIndex, path: str | None = None, device="cuda", pinned_mb: int = 256,
+                 check_vram: bool = True):
+        torch = _torch()
+        self.index = index
+        self.device = torch.device(device)
+        if self.device.type != "cuda":
+            raise ValueError("DeviceCheckpoint needs a GPU device")
+        if check_vram:
+            free, total = torch.cuda.mem_get_info(self.device)
+            need = index.device_bytes
+            if need > free:
+                raise MemoryError(f"checkpoint needs {need} bytes of device memory; {free} of {total} are free")
+        self.blob = torch.empty(index.blob_bytes, dtype=torch.uint8, device=self.device)
+        table, n, units = index.descs()
+        self.n = n
+        self.total_units = units
+        self.descs = torch.frombuffer(bytearray(table or b"\0" * 64), dtype=torch.uint8).to(self.device)
+        self.arena = torch.empty(max(1, index.arena_bytes // 2), dtype=torch.bfloat16, device=self.device)
+        outs = index.outputs()
+        base = self.arena.data_ptr()
+        self.outs = torch.tensor([base + o.offset for o in outs] or [0], dtype=torch.int64).to(self.device)
+        self.tensors = {}
+        for o in outs:
+            start = o.offset // 2
+            self.tensors[o.name] = self.arena[start: start + o.numel].view(o.shape)
+        self.stage_seconds_read = None
+        if path is not None:
+            self.stage(path, pinned_mb)
+
+    def stage(self, path: str, pinned_mb: int = 256):
+        torch = _torch()
+        pinned = torch.empty(max(2, pinned_mb) << 20, dtype=torch.uint8, pin_memory=True)
+        side = torch.cuda.Stream(self.device)
+        self.stage_seconds_read = stage_file(path, self.index, self.blob, pinned, side)
+        side.synchronize()
+        del pinned
+
+    def load_bytes(self, data_section: bytes):
+        """Stage from bytes already in host memory (tests): the data section only."""
+        torch = _torch()
+        assert len(data_section) == self.index.data_size
+        if data_section:
+            host = torch.frombuffer(bytearray(data_section), dtype=torch.uint8)
+            self.blob[: len(data_section)].copy_(host)
+
+    def materialize(self, stream=None, grid: int = 0):
+        if self.n:
+            materialize(self.blob, self.descs, self.n, self.outs, stream, grid)
+        return self.tensors
+
+
+def load(path: str, device="cuda", unit_log2_scale: int = 0) -> dict:
+    """Every output of the checkpoint at ``path`` as a bf16 tensor on ``device``."""
+    idx = SafeTensorIndex.open(path, unit_log2_scale)
+    ck = DeviceCheckpoint(idx, path, device)
+    out = ck.materialize()
+    _torch().cuda.current_stream(ck.device).synchronize()
+    return out

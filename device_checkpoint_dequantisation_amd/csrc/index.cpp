@@ -1,0 +1,797 @@
+// Host side of libstmat: the metadata-only safetensors index and the descriptor planner.
+//
+// The pages ("Disk tier safetensors streaming design audit", "FastSageTensors capability
+// audit" and "Strategy summary / Streaming safetensors mapping") describe an index built from
+// the header alone: per tensor a dtype, a shape and data_offsets, with tensors loaded on demand.
+// This file parses the safetensors header (8-byte little-endian length N, then N bytes of JSON)
+// with its own strict JSON reader, checks that the offsets tile the data section, pairs quantised
+// weights with their scale tensors and plans the work-unit table the grouped kernel consumes.
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+#include "st_internal.h"
+
+// ---------------------------------------------------------------------------------- errors
+
+static thread_local std::string g_err;
+
+extern "C" const char* st_last_error(void) { return g_err.c_str(); }
+
+st_status st_fail(st_status code, const char* fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+static void st_clear() { g_err.clear(); }
+
+namespace {
+
+// ---------------------------------------------------------------------------------- dtypes
+
+struct DtypeInfo {
+    const char* name;
+    uint32_t bits;
+};
+const DtypeInfo kDtypes[] = {
+    {"BOOL", 8}, {"U8", 8},   {"I8", 8},   {"F8_E4M3", 8}, {"F8_E5M2", 8}, {"F8_E8M0", 8}, {"I16", 16},
+    {"U16", 16}, {"F16", 16}, {"BF16", 16}, {"I32", 32},   {"U32", 32},    {"F32", 32},    {"I64", 64},
+    {"U64", 64}, {"F64", 64}, {"F4", 4},   {"F6_E2M3", 6}, {"F6_E3M2", 6},
+};
+constexpr int kNumDtypes = sizeof(kDtypes) / sizeof(kDtypes[0]);
+
+int dtype_of(const std::string& s) {
+    for (int i = 0; i < kNumDtypes; ++i)
+        if (s == kDtypes[i].name) return i;
+    return -1;
+}
+
+// ---------------------------------------------------------------------------------- JSON
+
+struct JVal {
+    enum Type : uint8_t { Null, Bool, Int, BigInt, Float, Str, Arr, Obj } t = Null;
+    bool b = false;
+    int64_t i = 0;  // Int: value (may be negative)
+    std::string s;
+    std::vector<JVal> a;
+    std::vector<std::pair<std::string, JVal>> o;
+};
+
+// Strict UTF-8 check (no overlongs, no encoded surrogates, nothing above U+10FFFF).
+bool valid_utf8(const unsigned char* p, size_t n) {
+    size_t i = 0;
+    while (i < n) {
+        unsigned c = p[i];
+        if (c < 0x80) { ++i; continue; }
+        size_t len;
+        uint32_t cp, min;
+        if ((c & 0xE0) == 0xC0) { len = 2; cp = c & 0x1F; min = 0x80; }
+        else if ((c & 0xF0) == 0xE0) { len = 3; cp = c & 0x0F; min = 0x800; }
+        else if ((c & 0xF8) == 0xF0) { len = 4; cp = c & 0x07; min = 0x10000; }
+        else return false;
+        if (i + len > n) return false;
+        for (size_t k = 1; k < len; ++k) {
+            unsigned d = p[i + k];
+            if ((d & 0xC0) != 0x80) return false;
+            cp = (cp << 6) | (d & 0x3F);
+        }
+        if (cp < min || cp > 0x10FFFF || (cp >= 0xD800 && cp <= 0xDFFF)) return false;
+        i += len;
+    }
+    return true;
+}
+
+class JsonReader {
+   public:
+    JsonReader(const char* p, size_t n) : p_(p), end_(p + n) {}
+
+    st_status parse(JVal& out) {
+        ws();
+        st_status r = value(out, 0);
+        if (r) return r;
+        ws();
+        if (p_ != end_) return err("unexpected data after the JSON value");
+        return ST_OK;
+    }
+
+   private:
+    const char* p_;
+    const char* end_;
+    const char* begin_ = p_;
+
+    st_status err(const char* what) {
+        return st_fail(ST_E_JSON, "header is not valid JSON: %s at byte %zu", what, size_t(p_ - begin_));
+    }
+    void ws() {
+        while (p_ < end_ && (*p_ == ' ' || *p_ == '\t' || *p_ == '\n' || *p_ == '\r')) ++p_;
+    }
+    bool lit(const char* s) {
+        size_t n = strlen(s);
+        if (size_t(end_ - p_) < n || memcmp(p_, s, n) != 0) return false;
+        p_ += n;
+        return true;
+    }
+
+    st_status value(JVal& v, int depth) {
+        if (depth > 64) return err("nesting deeper than 64");
+        if (p_ >= end_) return err("unexpected end");
+        char c = *p_;
+        if (c == '{') return object(v, depth);
+        if (c == '[') return array(v, depth);
+        if (c == '"') { v.t = JVal::Str; return string(v.s); }
+        if (c == '-' || (c >= '0' && c <= '9')) return number(v);
+        if (lit("true")) { v.t = JVal::Bool; v.b = true; return ST_OK; }
+        if (lit("false")) { v.t = JVal::Bool; v.b = false; return ST_OK; }
+        if (lit("null")) { v.t = JVal::Null; return ST_OK; }
+        return err("unexpected character");
+    }
+
+    st_status object(JVal& v, int depth) {
+        v.t = JVal::Obj;
+        ++p_;
+        ws();
+        if (p_ < end_ && *p_ == '}') { ++p_; return ST_OK; }
+        std::unordered_map<std::string, size_t> seen;
+        for (;;) {
+            ws();
+            if (p_ >= end_ || *p_ != '"') return err("expected a string key");
+            std::string key;
+            if (st_status r = string(key)) return r;
+            if (!seen.emplace(key, v.o.size()).second)
+                return st_fail(ST_E_JSON, "duplicate key \"%s\" in header", key.c_str());
+            ws();
+            if (p_ >= end_ || *p_ != ':') return err("expected ':'");
+            ++p_;
+            ws();
+            v.o.emplace_back(std::move(key), JVal());
+            if (st_status r = value(v.o.back().second, depth + 1)) return r;
+            ws();
+            if (p_ < end_ && *p_ == ',') { ++p_; continue; }
+            if (p_ < end_ && *p_ == '}') { ++p_; return ST_OK; }
+            return err("expected ',' or '}'");
+        }
+    }
+
+    st_status array(JVal& v, int depth) {
+        v.t = JVal::Arr;
+        ++p_;
+        ws();
+        if (p_ < end_ && *p_ == ']') { ++p_; return ST_OK; }
+        for (;;) {
+            ws();
+            v.a.emplace_back();
+            if (st_status r = value(v.a.back(), depth + 1)) return r;
+            ws();
+            if (p_ < end_ && *p_ == ',') { ++p_; continue; }
+            if (p_ < end_ && *p_ == ']') { ++p_; return ST_OK; }
+            return err("expected ',' or ']'");
+        }
+    }
+
+    static int hex(char c) {
+        if (c >= '0' && c <= '9') return c - '0';
+        if (c >= 'a' && c <= 'f') return c - 'a' + 10;
+        if (c >= 'A' && c <= 'F') return c - 'A' + 10;
+        return -1;
+    }
+    bool u4(uint32_t& cp) {
+        if (end_ - p_ < 4) return false;
+        cp = 0;
+        for (int k = 0; k < 4; ++k) {
+            int h = hex(p_[k]);
+            if (h < 0) return false;
+            cp = cp * 16 + uint32_t(h);
+        }
+        p_ += 4;
+        return true;
+    }
+    static void put_utf8(std::string& s, uint32_t cp) {
+        if (cp < 0x80) s += char(cp);
+        else if (cp < 0x800) { s += char(0xC0 | (cp >> 6)); s += char(0x80 | (cp & 0x3F)); }
+        else if (cp < 0x10000) {
+            s += char(0xE0 | (cp >> 12)); s += char(0x80 | ((cp >> 6) & 0x3F)); s += char(0x80 | (cp & 0x3F));
+        } else {
+            s += char(0xF0 | (cp >> 18)); s += char(0x80 | ((cp >> 12) & 0x3F));
+            s += char(0x80 | ((cp >> 6) & 0x3F)); s += char(0x80 | (cp & 0x3F));
+        }
+    }
+
+    st_status string(std::string& s) {
+        ++p_;  // opening quote
+        for (;;) {
+            if (p_ >= end_) return err("unterminated string");
+            unsigned char c = (unsigned char)*p_;
+            if (c == '"') { ++p_; break; }
+            if (c < 0x20) return err("control character in string");
+            if (c != '\\') { s += char(c); ++p_; continue; }
+            ++p_;
+            if (p_ >= end_) return err("unterminated escape");
+            char e = *p_++;
+            switch (e) {
+                case '"': s += '"'; break;
+                case '\\': s += '\\'; break;
+                case '/': s += '/'; break;
+                case 'b': s += '\b'; break;
+                case 'f': s += '\f'; break;
+                case 'n': s += '\n'; break;
+                case 'r': s += '\r'; break;
+                case 't': s += '\t'; break;
+                case 'u': {
+                    uint32_t cp;
+                    if (!u4(cp)) return err("bad \\u escape");
+                    if (cp >= 0xDC00 && cp <= 0xDFFF)
+                        return st_fail(ST_E_JSON, "string with an unpaired surrogate in header");
+                    if (cp >= 0xD800 && cp <= 0xDBFF) {
+                        uint32_t lo;
+                        if (end_ - p_ < 6 || p_[0] != '\\' || p_[1] != 'u')
+                            return st_fail(ST_E_JSON, "string with an unpaired surrogate in header");
+                        p_ += 2;
+                        if (!u4(lo)) return err("bad \\u escape");
+                        if (lo < 0xDC00 || lo > 0xDFFF)
+                            return st_fail(ST_E_JSON, "string with an unpaired surrogate in header");
+                        cp = 0x10000 + ((cp - 0xD800) << 10) + (lo - 0xDC00);
+                    }
+                    put_utf8(s, cp);
+                    break;
+                }
+                default: return err("invalid escape");
+            }
+        }
+        return ST_OK;
+    }
+
+    st_status number(JVal& v) {
+        const char* start = p_;
+        bool neg = false;
+        if (*p_ == '-') { neg = true; ++p_; }
+        if (p_ >= end_ || !(*p_ >= '0' && *p_ <= '9')) return err("bad number");
+        bool big = false;
+        uint64_t mag = 0;
+        if (*p_ == '0') ++p_;
+        else
+            while (p_ < end_ && *p_ >= '0' && *p_ <= '9') {
+                uint64_t d = uint64_t(*p_ - '0');
+                if (mag > (UINT64_MAX - d) / 10) big = true;
+                else mag = mag * 10 + d;
+                ++p_;
+            }
+        bool is_float = false;
+        if (p_ < end_ && *p_ == '.') {
+            ++p_;
+            if (p_ >= end_ || !(*p_ >= '0' && *p_ <= '9')) return err("bad number");
+            while (p_ < end_ && *p_ >= '0' && *p_ <= '9') ++p_;
+            is_float = true;
+        }
+        if (p_ < end_ && (*p_ == 'e' || *p_ == 'E')) {
+            ++p_;
+            if (p_ < end_ && (*p_ == '+' || *p_ == '-')) ++p_;
+            if (p_ >= end_ || !(*p_ >= '0' && *p_ <= '9')) return err("bad number");
+            while (p_ < end_ && *p_ >= '0' && *p_ <= '9') ++p_;
+            is_float = true;
+        }
+        (void)start;
+        if (is_float) { v.t = JVal::Float; return ST_OK; }
+        if (big || mag > uint64_t(INT64_MAX) + (neg ? 1 : 0)) { v.t = JVal::BigInt; return ST_OK; }
+        v.t = JVal::Int;
+        v.i = neg ? int64_t(0 - mag) : int64_t(mag);
+        return ST_OK;
+    }
+};
+
+// ---------------------------------------------------------------------------------- index
+
+struct Tensor {
+    std::string name;
+    int dtype;
+    std::vector<int64_t> shape;
+    uint64_t begin, end;
+    uint64_t numel;
+};
+
+struct Output {
+    uint32_t tensor;
+    int64_t scale = -1, scale2 = -1;
+    st_kind kind;
+    std::vector<int64_t> shape;
+    uint64_t numel;
+};
+
+bool ends_with(const std::string& s, const char* suf) {
+    size_t n = strlen(suf);
+    return s.size() >= n && memcmp(s.data() + s.size() - n, suf, n) == 0;
+}
+
+const char* const kScaleSuffixes[] = {".scale_weight", ".weight_scale_inv", ".weight_scale_2", ".weight_scale"};
+
+bool is_scale_name(const std::string& s) {
+    for (const char* suf : kScaleSuffixes)
+        if (ends_with(s, suf)) return true;
+    return false;
+}
+
+std::string shape_str(const std::vector<int64_t>& sh) {
+    std::string s = "[";
+    for (size_t i = 0; i < sh.size(); ++i) s += (i ? "," : "") + std::to_string(sh[i]);
+    return s + "]";
+}
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct st_index {
+    uint64_t header_len = 0;   // N
+    uint64_t data_size = 0;
+    std::string metadata_json = "{}";
+    std::vector<Tensor> tensors;
+    std::unordered_map<std::string, uint32_t> by_name;
+    std::vector<Output> outputs;
+    std::vector<uint64_t> out_offset;  // arena offsets
+    uint64_t arena_bytes = 0;
+    std::vector<st_desc> descs;
+    uint64_t total_units = 0;
+    uint32_t unit_log2_scale = 0;
+};
+
+namespace {
+
+std::string json_quote(const std::string& s) {
+    std::string o = "\"";
+    for (unsigned char c : s) {
+        if (c == '"' || c == '\\') { o += '\\'; o += char(c); }
+        else if (c < 0x20) { char b[8]; snprintf(b, sizeof b, "\\u%04x", c); o += b; }
+        else o += char(c);
+    }
+    return o + "\"";
+}
+
+st_status check_name(const std::string& s) {
+    if (s.find('\0') != std::string::npos) return st_fail(ST_E_JSON, "string with a NUL character in header");
+    return ST_OK;
+}
+
+bool is_scalar(const Tensor& t) { return t.shape.empty() || (t.shape.size() == 1 && t.shape[0] == 1); }
+
+st_status read_int(const JVal& v, const std::string& name, const char* field, int64_t& out) {
+    if (v.t != JVal::Int || v.i < 0)
+        return st_fail(ST_E_SHAPE, "%s: %s must hold non-negative integers below 2^63", name.c_str(), field);
+    out = v.i;
+    return ST_OK;
+}
+
+st_status parse_entries(st_index& ix, const JVal& root) {
+    if (root.t != JVal::Obj) return st_fail(ST_E_JSON, "header is not a JSON object");
+    ix.tensors.reserve(root.o.size());
+    for (const auto& kv : root.o) {
+        const std::string& name = kv.first;
+        const JVal& val = kv.second;
+        if (st_status r = check_name(name)) return r;
+        if (name == "__metadata__") {
+            if (val.t != JVal::Obj) return st_fail(ST_E_JSON, "__metadata__ must map strings to strings");
+            std::string m = "{";
+            for (size_t i = 0; i < val.o.size(); ++i) {
+                if (val.o[i].second.t != JVal::Str) return st_fail(ST_E_JSON, "__metadata__ must map strings to strings");
+                if (check_name(val.o[i].first) || check_name(val.o[i].second.s))
+                    return st_fail(ST_E_JSON, "string with a NUL character in header");
+                m += (i ? "," : "") + json_quote(val.o[i].first) + ":" + json_quote(val.o[i].second.s);
+            }
+            ix.metadata_json = m + "}";
+            continue;
+        }
+        if (val.t != JVal::Obj || val.o.size() != 3)
+            return st_fail(ST_E_SHAPE, "%s: entry must have exactly dtype, shape, data_offsets", name.c_str());
+        const JVal *dt = nullptr, *sh = nullptr, *of = nullptr;
+        for (const auto& f : val.o) {
+            if (f.first == "dtype") dt = &f.second;
+            else if (f.first == "shape") sh = &f.second;
+            else if (f.first == "data_offsets") of = &f.second;
+        }
+        if (!dt || !sh || !of)
+            return st_fail(ST_E_SHAPE, "%s: entry must have exactly dtype, shape, data_offsets", name.c_str());
+        Tensor t;
+        t.name = name;
+        t.dtype = dt->t == JVal::Str ? dtype_of(dt->s) : -1;
+        if (t.dtype < 0)
+            return st_fail(ST_E_DTYPE, "%s: unknown dtype %s", name.c_str(), dt->t == JVal::Str ? dt->s.c_str() : "(not a string)");
+        if (sh->t != JVal::Arr) return st_fail(ST_E_SHAPE, "%s: shape must be a list of non-negative integers", name.c_str());
+        if (sh->a.size() > ST_MAX_NDIM) return st_fail(ST_E_SHAPE, "%s: more than %d dimensions", name.c_str(), ST_MAX_NDIM);
+        for (const JVal& d : sh->a) {
+            int64_t x;
+            if (st_status r = read_int(d, name, "shape", x)) return r;
+            t.shape.push_back(x);
+        }
+        if (of->t != JVal::Arr || of->a.size() != 2)
+            return st_fail(ST_E_OFFSETS, "%s: data_offsets must be two non-negative integers", name.c_str());
+        int64_t b, e;
+        if (read_int(of->a[0], name, "data_offsets", b) || read_int(of->a[1], name, "data_offsets", e))
+            return st_fail(ST_E_OFFSETS, "%s: data_offsets must be two non-negative integers", name.c_str());
+        if (b > e) return st_fail(ST_E_OFFSETS, "%s: data_offsets begin %lld > end %lld", name.c_str(), (long long)b, (long long)e);
+        t.begin = uint64_t(b);
+        t.end = uint64_t(e);
+        // numel * bits must equal the span; any zero dimension makes numel 0 whatever the others.
+        bool zero = false;
+        for (int64_t d : t.shape) zero |= d == 0;
+        unsigned __int128 numel = 1;
+        bool overflow = false;
+        if (!zero)
+            for (int64_t d : t.shape) {
+                numel *= uint64_t(d);
+                if (numel > (unsigned __int128)UINT64_MAX) { overflow = true; break; }
+            }
+        if (zero) numel = 0;
+        unsigned __int128 bits = numel * kDtypes[t.dtype].bits;
+        if (overflow || bits % 8 != 0 || bits / 8 != (unsigned __int128)(t.end - t.begin))
+            return st_fail(ST_E_SHAPE, "%s: %s%s needs %s bytes, offsets span %llu", name.c_str(), kDtypes[t.dtype].name,
+                           shape_str(t.shape).c_str(),
+                           overflow ? "more than 2^64" : (bits % 8 ? "a fractional number of" : std::to_string((uint64_t)(bits / 8)).c_str()),
+                           (unsigned long long)(t.end - t.begin));
+        t.numel = uint64_t(numel);
+        ix.by_name.emplace(name, uint32_t(ix.tensors.size()));
+        ix.tensors.push_back(std::move(t));
+    }
+    return ST_OK;
+}
+
+st_status check_layout(const st_index& ix) {
+    std::vector<uint32_t> order(ix.tensors.size());
+    for (uint32_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](uint32_t a, uint32_t b) {
+        const Tensor &x = ix.tensors[a], &y = ix.tensors[b];
+        return x.begin != y.begin ? x.begin < y.begin : x.end < y.end;
+    });
+    uint64_t pos = 0;
+    for (uint32_t i : order) {
+        const Tensor& t = ix.tensors[i];
+        if (t.begin != pos)
+            return st_fail(ST_E_OFFSETS, "%s: data_offsets [%llu, %llu] %s byte %llu", t.name.c_str(),
+                           (unsigned long long)t.begin, (unsigned long long)t.end,
+                           t.begin < pos ? "overlaps" : "leaves a gap before", (unsigned long long)pos);
+        pos = t.end;
+    }
+    if (pos != ix.data_size)
+        return st_fail(ST_E_OFFSETS, "tensors cover %llu bytes but the data section has %llu",
+                       (unsigned long long)pos, (unsigned long long)ix.data_size);
+    return ST_OK;
+}
+
+const Tensor* find(const st_index& ix, const std::string& name, int64_t* idx = nullptr) {
+    auto it = ix.by_name.find(name);
+    if (it == ix.by_name.end()) return nullptr;
+    if (idx) *idx = it->second;
+    return &ix.tensors[it->second];
+}
+
+st_status classify(st_index& ix) {
+    std::vector<bool> used(ix.tensors.size(), false);
+    for (uint32_t ti = 0; ti < ix.tensors.size(); ++ti) {
+        const Tensor& t = ix.tensors[ti];
+        if (is_scale_name(t.name)) continue;
+        Output o;
+        o.tensor = ti;
+        o.shape = t.shape;
+        o.numel = t.numel;
+        const char* dn = kDtypes[t.dtype].name;
+        if (t.dtype == ST_DT_BF16) o.kind = ST_KIND_PASS_BF16;
+        else if (t.dtype == ST_DT_F16) o.kind = ST_KIND_CAST_F16;
+        else if (t.dtype == ST_DT_F32) o.kind = ST_KIND_CAST_F32;
+        else if (t.dtype == ST_DT_F8_E4M3) {
+            if (!ends_with(t.name, ".weight"))
+                return st_fail(ST_E_SCALE, "%s: float8 tensor without a scale (not named X.weight)", t.name.c_str());
+            std::string x = t.name.substr(0, t.name.size() - 7);
+            int64_t si = -1, bi = -1;
+            const Tensor* st = find(ix, x + ".scale_weight", &si);
+            const Tensor* sb = find(ix, x + ".weight_scale_inv", &bi);
+            if (st && sb) return st_fail(ST_E_SCALE, "%s: both scale_weight and weight_scale_inv present", t.name.c_str());
+            if (st) {
+                if (st->dtype != ST_DT_F32 || !is_scalar(*st))
+                    return st_fail(ST_E_SCALE, "%s: scale_weight must be an fp32 scalar, got %s%s", st->name.c_str(),
+                                   kDtypes[st->dtype].name, shape_str(st->shape).c_str());
+                o.kind = ST_KIND_FP8_TENSOR;
+                o.scale = si;
+            } else if (sb) {
+                if (t.shape.size() != 2)
+                    return st_fail(ST_E_SHAPE, "%s: block-scaled float8 weight must be 2-D, got %s", t.name.c_str(),
+                                   shape_str(t.shape).c_str());
+                int64_t gm = (t.shape[0] + 127) / 128, gn = (t.shape[1] + 127) / 128;
+                if (sb->dtype != ST_DT_F32 || sb->shape.size() != 2 || sb->shape[0] != gm || sb->shape[1] != gn)
+                    return st_fail(ST_E_SCALE, "%s: must be F32 [%lld,%lld], got %s%s", sb->name.c_str(), (long long)gm,
+                                   (long long)gn, kDtypes[sb->dtype].name, shape_str(sb->shape).c_str());
+                if (t.numel >= (uint64_t(1) << 32) || t.shape[1] >= (int64_t(1) << 32))
+                    return st_fail(ST_E_SHAPE, "%s: block-scaled float8 weights of 2^32 or more elements are not supported",
+                                   t.name.c_str());
+                o.kind = ST_KIND_FP8_BLOCK128;
+                o.scale = bi;
+            } else {
+                return st_fail(ST_E_SCALE, "%s: float8 weight has no scale_weight or weight_scale_inv", t.name.c_str());
+            }
+        } else if (t.dtype == ST_DT_U8 || t.dtype == ST_DT_F4) {
+            if (!ends_with(t.name, ".weight"))
+                return st_fail(ST_E_DTYPE, "%s: %s tensor is not an NVFP4 weight", t.name.c_str(), dn);
+            if (t.shape.size() != 2)
+                return st_fail(ST_E_SHAPE, "%s: NVFP4 weight must be 2-D, got %s", t.name.c_str(), shape_str(t.shape).c_str());
+            std::string x = t.name.substr(0, t.name.size() - 7);
+            int64_t m = t.shape[0];
+            int64_t k = t.dtype == ST_DT_U8 ? t.shape[1] * 2 : t.shape[1];
+            if (k % 16) return st_fail(ST_E_SHAPE, "%s: NVFP4 K=%lld is not a multiple of 16", t.name.c_str(), (long long)k);
+            int64_t bsi = -1, gi = -1;
+            const Tensor* bs = find(ix, x + ".weight_scale", &bsi);
+            const Tensor* g = find(ix, x + ".weight_scale_2", &gi);
+            if (!bs || !g)
+                return st_fail(ST_E_SCALE, "%s: NVFP4 weight needs weight_scale and weight_scale_2", t.name.c_str());
+            if (bs->dtype != ST_DT_F8_E4M3 || bs->shape.size() != 2 || bs->shape[0] != m || bs->shape[1] != k / 16)
+                return st_fail(ST_E_SCALE, "%s: must be F8_E4M3 [%lld,%lld], got %s%s", bs->name.c_str(), (long long)m,
+                               (long long)(k / 16), kDtypes[bs->dtype].name, shape_str(bs->shape).c_str());
+            if (g->dtype != ST_DT_F32 || !is_scalar(*g))
+                return st_fail(ST_E_SCALE, "%s: weight_scale_2 must be an fp32 scalar", g->name.c_str());
+            if (k >= (int64_t(1) << 32))
+                return st_fail(ST_E_SHAPE, "%s: NVFP4 K of 2^32 or more is not supported", t.name.c_str());
+            o.kind = ST_KIND_NVFP4;
+            o.shape = {m, k};
+            o.numel = uint64_t(m) * uint64_t(k);
+            o.scale = bsi;
+            o.scale2 = gi;
+        } else {
+            return st_fail(ST_E_DTYPE, "%s: dtype %s cannot be materialised as bf16", t.name.c_str(), dn);
+        }
+        if (o.scale >= 0) used[size_t(o.scale)] = true;
+        if (o.scale2 >= 0) used[size_t(o.scale2)] = true;
+        ix.outputs.push_back(std::move(o));
+    }
+    for (uint32_t ti = 0; ti < ix.tensors.size(); ++ti)
+        if (is_scale_name(ix.tensors[ti].name) && !used[ti])
+            return st_fail(ST_E_SCALE, "%s: scale tensor with no matching weight", ix.tensors[ti].name.c_str());
+    std::stable_sort(ix.outputs.begin(), ix.outputs.end(), [&](const Output& a, const Output& b) {
+        const Tensor &x = ix.tensors[a.tensor], &y = ix.tensors[b.tensor];
+        return x.begin != y.begin ? x.begin < y.begin : x.name < y.name;
+    });
+    return ST_OK;
+}
+
+st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64_t unit_begin, uint64_t* units) {
+    st_desc d;
+    memset(&d, 0, sizeof d);
+    const Tensor& t = ix.tensors[o.tensor];
+    d.src = t.begin;
+    d.scale = o.scale >= 0 ? ix.tensors[size_t(o.scale)].begin : 0;
+    d.scale2 = o.scale2 >= 0 ? ix.tensors[size_t(o.scale2)].begin : 0;
+    d.numel = o.numel;
+    d.unit_begin = unit_begin;
+    d.out = out_slot;
+    d.kind = uint8_t(o.kind);
+    d.unit_shift = uint8_t(stk::step_shift(o.kind) + ix.unit_log2_scale);
+    if (o.kind == ST_KIND_FP8_BLOCK128) {
+        uint32_t n = uint32_t(o.shape[1]);
+        d.cols = n;
+        d.grid_cols = (n + 127) / 128;
+        if (n) {
+            d.div_magic = stk::div_magic(n);
+            d.div_shift = uint8_t(stk::div_shift(n));
+        }
+    } else if (o.kind == ST_KIND_NVFP4) {
+        d.cols = uint32_t(o.shape[1]);
+    }
+    *units = (o.numel + (uint64_t(1) << d.unit_shift) - 1) >> d.unit_shift;
+    return d;
+}
+
+st_status plan(st_index& ix) {
+    uint64_t pos = 0, unit = 0;
+    ix.out_offset.resize(ix.outputs.size());
+    ix.descs.resize(ix.outputs.size());
+    for (size_t k = 0; k < ix.outputs.size(); ++k) {
+        ix.out_offset[k] = pos;
+        pos = round_up(pos + ix.outputs[k].numel * 2, 256);
+        uint64_t units;
+        ix.descs[k] = make_desc(ix, ix.outputs[k], uint32_t(k), unit, &units);
+        unit += units;
+    }
+    if (ix.outputs.size() >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "more than 2^32 outputs");
+    ix.arena_bytes = pos;
+    ix.total_units = unit;
+    return ST_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------- C ABI
+
+extern "C" st_status st_header_size(const void* first8, uint64_t* header_bytes) {
+    st_clear();
+    if (!first8 || !header_bytes) return st_fail(ST_E_ARG, "st_header_size: null pointer");
+    uint64_t n = 0;
+    const unsigned char* p = (const unsigned char*)first8;
+    for (int k = 7; k >= 0; --k) n = (n << 8) | p[k];
+    if (n > ST_HEADER_CAP)
+        return st_fail(ST_E_HEADER, "header length %llu exceeds the cap %llu", (unsigned long long)n, ST_HEADER_CAP);
+    *header_bytes = 8 + n;
+    return ST_OK;
+}
+
+extern "C" st_status st_index_build(const void* header_bytes, uint64_t header_len, uint64_t file_size,
+                                    const st_plan_opts* opts, st_index** out) {
+    st_clear();
+    if (!out) return st_fail(ST_E_ARG, "st_index_build: out is null");
+    *out = nullptr;
+    if (!header_bytes && header_len) return st_fail(ST_E_ARG, "st_index_build: header_bytes is null");
+    if (opts && (opts->flags != 0 || opts->unit_log2_scale > 6))
+        return st_fail(ST_E_ARG, "st_plan_opts: flags must be 0 and unit_log2_scale at most 6 (got %u, %u)", opts->flags,
+                       opts->unit_log2_scale);
+    if (header_len < 8 || file_size < 8)
+        return st_fail(ST_E_HEADER, "file shorter than the 8-byte header length (%llu bytes)",
+                       (unsigned long long)std::min(header_len, file_size));
+    uint64_t hb;
+    if (st_status r = st_header_size(header_bytes, &hb)) return r;
+    uint64_t n = hb - 8;
+    if (hb > file_size)
+        return st_fail(ST_E_HEADER, "header length %llu runs past the end of the file (%llu bytes)", (unsigned long long)n,
+                       (unsigned long long)file_size);
+    if (hb > header_len)
+        return st_fail(ST_E_ARG, "st_index_build: %llu header bytes given, the header needs %llu",
+                       (unsigned long long)header_len, (unsigned long long)hb);
+    const char* text = (const char*)header_bytes + 8;
+    if (!valid_utf8((const unsigned char*)text, n)) return st_fail(ST_E_HEADER, "header is not UTF-8");
+    std::unique_ptr<st_index> ix(new (std::nothrow) st_index);
+    if (!ix) return st_fail(ST_E_NOMEM, "out of host memory");
+    ix->header_len = n;
+    ix->data_size = file_size - hb;
+    ix->unit_log2_scale = opts ? opts->unit_log2_scale : 0;
+    try {
+        JVal root;
+        if (st_status r = JsonReader(text, n).parse(root)) return r;
+        if (st_status r = parse_entries(*ix, root)) return r;
+        if (st_status r = check_layout(*ix)) return r;
+        if (st_status r = classify(*ix)) return r;
+        if (st_status r = plan(*ix)) return r;
+    } catch (const std::bad_alloc&) {
+        return st_fail(ST_E_NOMEM, "out of host memory while indexing the header");
+    }
+    *out = ix.release();
+    return ST_OK;
+}
+
+extern "C" st_status st_index_open(const char* path, const st_plan_opts* opts, st_index** out) {
+    st_clear();
+    if (!out) return st_fail(ST_E_ARG, "st_index_open: out is null");
+    *out = nullptr;
+    if (!path) return st_fail(ST_E_ARG, "st_index_open: path is null");
+    int fd = open(path, O_RDONLY | O_CLOEXEC);
+    if (fd < 0) return st_fail(ST_E_IO, "cannot open %s", path);
+    struct stat sb;
+    if (fstat(fd, &sb) != 0) { close(fd); return st_fail(ST_E_IO, "cannot stat %s", path); }
+    uint64_t size = uint64_t(sb.st_size);
+    unsigned char first[8];
+    if (size < 8 || pread(fd, first, 8, 0) != 8) {
+        close(fd);
+        return st_fail(ST_E_HEADER, "file shorter than the 8-byte header length (%llu bytes)", (unsigned long long)size);
+    }
+    uint64_t hb;
+    if (st_status r = st_header_size(first, &hb)) { close(fd); return r; }
+    if (hb > size) {
+        close(fd);
+        return st_fail(ST_E_HEADER, "header length %llu runs past the end of the file (%llu bytes)",
+                       (unsigned long long)(hb - 8), (unsigned long long)size);
+    }
+    std::vector<char> buf;
+    try { buf.resize(hb); } catch (const std::bad_alloc&) { close(fd); return st_fail(ST_E_NOMEM, "out of host memory"); }
+    uint64_t got = 0;
+    while (got < hb) {
+        ssize_t r = pread(fd, buf.data() + got, hb - got, off_t(got));
+        if (r <= 0) { close(fd); return st_fail(ST_E_IO, "read of %s header failed", path); }
+        got += uint64_t(r);
+    }
+    close(fd);
+    return st_index_build(buf.data(), hb, size, opts, out);
+}
+
+extern "C" void st_index_free(st_index* idx) { delete idx; }
+
+extern "C" uint64_t st_index_data_offset(const st_index* idx) { return idx ? 8 + idx->header_len : 0; }
+extern "C" uint64_t st_index_data_size(const st_index* idx) { return idx ? idx->data_size : 0; }
+extern "C" uint64_t st_index_blob_bytes(const st_index* idx) {
+    return idx ? std::max<uint64_t>(256, round_up(idx->data_size, 256)) : 0;
+}
+extern "C" size_t st_index_count(const st_index* idx) { return idx ? idx->tensors.size() : 0; }
+
+extern "C" st_status st_index_tensor(const st_index* idx, size_t i, st_tensor_meta* out) {
+    st_clear();
+    if (!idx || !out) return st_fail(ST_E_ARG, "st_index_tensor: null pointer");
+    if (i >= idx->tensors.size()) return st_fail(ST_E_ARG, "st_index_tensor: index %zu out of range (%zu)", i, idx->tensors.size());
+    const Tensor& t = idx->tensors[i];
+    memset(out, 0, sizeof *out);
+    out->name = t.name.c_str();
+    out->dtype = t.dtype;
+    out->ndim = int32_t(t.shape.size());
+    for (size_t d = 0; d < t.shape.size(); ++d) out->shape[d] = t.shape[d];
+    out->begin = t.begin;
+    out->end = t.end;
+    return ST_OK;
+}
+
+extern "C" int64_t st_index_find(const st_index* idx, const char* name) {
+    if (!idx || !name) return -1;
+    int64_t i = -1;
+    return find(*idx, name, &i) ? i : -1;
+}
+
+extern "C" const char* st_index_metadata_json(const st_index* idx) { return idx ? idx->metadata_json.c_str() : "{}"; }
+
+extern "C" size_t st_index_num_outputs(const st_index* idx) { return idx ? idx->outputs.size() : 0; }
+
+extern "C" st_status st_index_output(const st_index* idx, size_t k, st_output_info* out) {
+    st_clear();
+    if (!idx || !out) return st_fail(ST_E_ARG, "st_index_output: null pointer");
+    if (k >= idx->outputs.size()) return st_fail(ST_E_ARG, "st_index_output: index %zu out of range (%zu)", k, idx->outputs.size());
+    const Output& o = idx->outputs[k];
+    memset(out, 0, sizeof *out);
+    out->name = idx->tensors[o.tensor].name.c_str();
+    out->kind = o.kind;
+    out->ndim = int32_t(o.shape.size());
+    for (size_t d = 0; d < o.shape.size(); ++d) out->shape[d] = o.shape[d];
+    out->numel = o.numel;
+    out->tensor = o.tensor;
+    out->scale = o.scale;
+    out->scale2 = o.scale2;
+    return ST_OK;
+}
+
+extern "C" uint64_t st_index_output_offset(const st_index* idx, size_t k) {
+    return idx && k < idx->out_offset.size() ? idx->out_offset[k] : 0;
+}
+extern "C" uint64_t st_index_output_arena_bytes(const st_index* idx) { return idx ? std::max<uint64_t>(256, idx->arena_bytes) : 0; }
+
+extern "C" uint64_t st_index_traffic_bytes(const st_index* idx) {
+    if (!idx) return 0;
+    uint64_t w = 0;
+    for (const Output& o : idx->outputs) w += o.numel * 2;
+    return idx->data_size + w;
+}
+
+extern "C" uint64_t st_index_device_bytes(const st_index* idx) {
+    if (!idx) return 0;
+    uint64_t n = idx->outputs.size();
+    return st_index_blob_bytes(idx) + round_up(n * sizeof(st_desc), 256) + round_up(n * sizeof(void*), 256) +
+           st_index_output_arena_bytes(idx);
+}
+
+extern "C" const st_desc* st_index_descs(const st_index* idx, size_t* n, size_t* bytes, uint64_t* total_units) {
+    if (!idx) return nullptr;
+    if (n) *n = idx->descs.size();
+    if (bytes) *bytes = idx->descs.size() * sizeof(st_desc);
+    if (total_units) *total_units = idx->total_units;
+    return idx->descs.data();
+}
+
+extern "C" st_status st_index_descs_subset(const st_index* idx, const uint32_t* sel, size_t k, st_desc* dst,
+                                           size_t dst_bytes, uint64_t* total_units) {
+    st_clear();
+    if (!idx || (k && (!sel || !dst))) return st_fail(ST_E_ARG, "st_index_descs_subset: null pointer");
+    if (dst_bytes < k * sizeof(st_desc))
+        return st_fail(ST_E_ARG, "st_index_descs_subset: dst holds %zu bytes, %zu needed", dst_bytes, k * sizeof(st_desc));
+    uint64_t unit = 0;
+    for (size_t j = 0; j < k; ++j) {
+        if (sel[j] >= idx->outputs.size())
+            return st_fail(ST_E_ARG, "st_index_descs_subset: output %u out of range (%zu)", sel[j], idx->outputs.size());
+        uint64_t units;
+        dst[j] = make_desc(*idx, idx->outputs[sel[j]], uint32_t(j), unit, &units);
+        unit += units;
+    }
+    if (total_units) *total_units = unit;
+    return ST_OK;
+}

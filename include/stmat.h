@@ -1,0 +1,218 @@
+/*
+ * stmat — materialise safetensors checkpoint weights as bf16 on an MI355X (gfx950).
+ *
+ * C ABI of libstmat.so.  Plain pointers and sizes only; no C++ or framework types cross it.
+ * Streams and events are HIP handles (hipStream_t / hipEvent_t) passed as void*.
+ *
+ * The operation.  The pages ("Disk tier safetensors streaming design audit", sections
+ * "FastSageTensors capability audit" and "Strategy summary") describe a metadata-only index
+ * of a safetensors file (per tensor: dtype, shape, data_offsets; no tensor bytes read) and range
+ * reads of tensor bytes into pinned host memory followed by a copy to the GPU.  The serving
+ * document ("Resident Modal LLM Architecture", section "Current Backend Boundary") names the
+ * quantised checkpoint families whose weights must be turned into compute-dtype tensors: Qwen
+ * block-FP8 and NVIDIA ModelOpt NVFP4; the design audit ("Mandatory research audit") names
+ * ComfyUI's scaled-FP8 checkpoints.  This library implements that path:
+ *
+ *   st_index_build / st_index_open   header bytes -> index (host, metadata only)
+ *   st_stage_file                    file byte ranges -> pinned ring -> device blob (side stream)
+ *   st_materialize                   device blob + descriptor table -> bf16 outputs (one launch)
+ *
+ * Output element values (bit-exact definition; rounding is IEEE binary32 round-to-nearest-even
+ * for every multiply, then round-to-nearest-even to bfloat16; any NaN result is 0x7FC0;
+ * no subnormal flushing):
+ *   PASS_BF16     bf16 input bits copied unchanged
+ *   CAST_F16      bf16(float(h))
+ *   CAST_F32      bf16(x)
+ *   FP8_TENSOR    bf16(e4m3(w) * s)                 X.weight F8_E4M3 + X.scale_weight F32 []
+ *   FP8_BLOCK128  bf16(e4m3(w[i,j]) * S[i/128,j/128]) X.weight F8_E4M3 [M,N] +
+ *                                                  X.weight_scale_inv F32 [ceil(M/128),ceil(N/128)]
+ *   NVFP4         bf16((e2m1(q[i,j]) * e4m3(bs[i,j/16])) * g)
+ *                 X.weight U8 [M,K/2] (element 2k in the low nibble of byte k) or F4 [M,K] +
+ *                 X.weight_scale F8_E4M3 [M,K/16] + X.weight_scale_2 F32 []
+ * e4m3 is OCP E4M3 "fn" (bias 7, no infinities, NaN at S.1111.111); e2m1 is OCP-MX E2M1.
+ *
+ * Errors.  Every call returns ST_OK (0) or a negative st_status; nothing throws across the ABI.
+ * st_last_error() then names the tensor, the field and the measured values.
+ */
+#ifndef STMAT_H
+#define STMAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum st_status {
+    ST_OK = 0,
+    ST_E_ARG = -1,      /* null pointer, size too small, bad option */
+    ST_E_IO = -2,       /* open/read/stat failed, file shorter than the header says */
+    ST_E_HEADER = -3,   /* header length field: too short, over the cap, past end of file, not UTF-8 */
+    ST_E_JSON = -4,     /* header is not a JSON object, duplicate key, bad string */
+    ST_E_DTYPE = -5,    /* unknown dtype, or a dtype that cannot be materialised */
+    ST_E_SHAPE = -6,    /* bad shape, span != numel * itemsize, rank, NVFP4 K % 16, size limits */
+    ST_E_OFFSETS = -7,  /* offsets overlap, leave a gap, or do not end at the end of the file */
+    ST_E_SCALE = -8,    /* missing, orphaned, ambiguous or mis-shaped scale tensor */
+    ST_E_NOMEM = -9,    /* host allocation failed */
+    ST_E_HIP = -10      /* a HIP runtime call failed (launch, copy, event) */
+} st_status;
+
+/* safetensors dtype strings, in this order: BOOL U8 I8 F8_E4M3 F8_E5M2 F8_E8M0 I16 U16 F16
+ * BF16 I32 U32 F32 I64 U64 F64 F4 F6_E2M3 F6_E3M2 */
+typedef enum st_dtype {
+    ST_DT_BOOL = 0, ST_DT_U8, ST_DT_I8, ST_DT_F8_E4M3, ST_DT_F8_E5M2, ST_DT_F8_E8M0,
+    ST_DT_I16, ST_DT_U16, ST_DT_F16, ST_DT_BF16, ST_DT_I32, ST_DT_U32, ST_DT_F32,
+    ST_DT_I64, ST_DT_U64, ST_DT_F64, ST_DT_F4, ST_DT_F6_E2M3, ST_DT_F6_E3M2
+} st_dtype;
+
+typedef enum st_kind {
+    ST_KIND_PASS_BF16 = 0, ST_KIND_CAST_F16 = 1, ST_KIND_CAST_F32 = 2,
+    ST_KIND_FP8_TENSOR = 3, ST_KIND_FP8_BLOCK128 = 4, ST_KIND_NVFP4 = 5
+} st_kind;
+
+#define ST_MAX_NDIM 8
+#define ST_HEADER_CAP 100000000ull   /* largest accepted JSON header, bytes */
+#define ST_BLOB_ALIGN 256            /* required alignment of the device blob */
+#define ST_OUT_ALIGN 16              /* required alignment of every output pointer */
+
+/* One header entry (a tensor as stored).  begin/end are relative to the data section. */
+typedef struct st_tensor_meta {
+    const char* name;        /* NUL-terminated UTF-8, valid for the index's lifetime */
+    int32_t dtype;           /* st_dtype */
+    int32_t ndim;
+    int64_t shape[ST_MAX_NDIM];
+    uint64_t begin, end;
+} st_tensor_meta;
+
+/* One bf16 output (a weight after scale pairing), in output order. */
+typedef struct st_output_info {
+    const char* name;        /* the weight tensor's name */
+    int32_t kind;            /* st_kind */
+    int32_t ndim;
+    int64_t shape[ST_MAX_NDIM];  /* logical bf16 shape (NVFP4: [M, K]) */
+    uint64_t numel;
+    int64_t tensor;          /* header-entry index of the weight */
+    int64_t scale;           /* header-entry index of its scale tensor, or -1 */
+    int64_t scale2;          /* header-entry index of the NVFP4 global scale, or -1 */
+} st_output_info;
+
+/* Device descriptor: one per output, 64 bytes, built on the host, uploaded by the caller.
+ * Offsets are bytes from the start of the blob (= the file's data section). */
+typedef struct st_desc {
+    uint64_t src;            /* weight bytes */
+    uint64_t scale;          /* FP8_TENSOR fp32 scale / FP8_BLOCK128 fp32 grid / NVFP4 e4m3 block scales */
+    uint64_t scale2;         /* NVFP4 fp32 global scale */
+    uint64_t numel;          /* output elements */
+    uint64_t unit_begin;     /* index of this output's first work unit in the table */
+    uint32_t out;            /* index into the outs[] pointer array */
+    uint32_t cols;           /* FP8_BLOCK128: N, NVFP4: K, otherwise 0 */
+    uint32_t grid_cols;      /* FP8_BLOCK128: ceil(N / 128) */
+    uint32_t div_magic;      /* FP8_BLOCK128: multiplier of the exact division by N */
+    uint8_t kind;            /* st_kind */
+    uint8_t unit_shift;      /* a work unit is 2^unit_shift output elements */
+    uint8_t div_shift;       /* FP8_BLOCK128: shift of the exact division by N */
+    uint8_t reserved0;
+    uint32_t reserved1;
+} st_desc;                   /* 64 bytes */
+
+/* Planning options; pass NULL for the defaults. */
+typedef struct st_plan_opts {
+    uint32_t unit_log2_scale;  /* work unit = (kind's wave step) << this; 0..6, default 0 */
+    uint32_t flags;            /* reserved, must be 0 */
+} st_plan_opts;
+
+typedef struct st_index st_index;   /* opaque, host memory, owned by the library */
+
+/* Human-readable description of the last error on the calling thread ("" if none).  Valid
+ * until the next stmat call on the same thread. */
+const char* st_last_error(void);
+
+/* From the first 8 bytes of a file, the number of bytes the header occupies (8 + N).
+ * Fails with ST_E_HEADER if N exceeds ST_HEADER_CAP. */
+st_status st_header_size(const void* first8, uint64_t* header_bytes);
+
+/* Build the metadata-only index from the first header_len bytes of a safetensors file of
+ * file_size bytes (header_len >= 8 + N; extra bytes are ignored).  Parses and validates the
+ * header, checks that the data_offsets tile the data section exactly, pairs quantised weights
+ * with their scales, and plans the device descriptor table.  No tensor byte is read.
+ * Fails (and sets *out = NULL) on any malformed header; see st_status. */
+st_status st_index_build(const void* header_bytes, uint64_t header_len, uint64_t file_size,
+                         const st_plan_opts* opts, st_index** out);
+
+/* st_index_build on the header of the file at `path` (reads only 8 + N bytes). */
+st_status st_index_open(const char* path, const st_plan_opts* opts, st_index** out);
+
+void st_index_free(st_index* idx);
+
+uint64_t st_index_data_offset(const st_index* idx);   /* 8 + N: file offset of the data section */
+uint64_t st_index_data_size(const st_index* idx);     /* bytes of the data section */
+/* Bytes to allocate for the device blob: data size rounded up to a multiple of 256.  The
+ * kernel reads whole aligned 16-byte words, so the padding must be present. */
+uint64_t st_index_blob_bytes(const st_index* idx);
+size_t st_index_count(const st_index* idx);           /* header entries (tensors) */
+st_status st_index_tensor(const st_index* idx, size_t i, st_tensor_meta* out);
+/* Index of the header entry called `name`, or -1. */
+int64_t st_index_find(const st_index* idx, const char* name);
+/* The header's __metadata__ as a JSON object text ("{}" if absent); valid for the index's lifetime. */
+const char* st_index_metadata_json(const st_index* idx);
+
+size_t st_index_num_outputs(const st_index* idx);
+st_status st_index_output(const st_index* idx, size_t k, st_output_info* out);
+/* Byte offset of output k inside one output arena in which every output starts on a
+ * 256-byte boundary, and the arena's total size. */
+uint64_t st_index_output_offset(const st_index* idx, size_t k);
+uint64_t st_index_output_arena_bytes(const st_index* idx);
+/* Bytes read + bytes written by materialising every output (the data section plus 2 bytes
+ * per output element). */
+uint64_t st_index_traffic_bytes(const st_index* idx);
+/* Device memory the whole load needs: blob + descriptor table + pointer array + arena.
+ * Compare with the free device memory before allocating; the requirement is arithmetic. */
+uint64_t st_index_device_bytes(const st_index* idx);
+
+/* The full descriptor table (one st_desc per output, in output order, out = k), host memory
+ * owned by the index.  *n = descriptors, *bytes = n * sizeof(st_desc), *total_units = work
+ * units in the table (any of the three pointers may be NULL). */
+const st_desc* st_index_descs(const st_index* idx, size_t* n, size_t* bytes, uint64_t* total_units);
+
+/* A self-contained table for a subset of outputs: sel[0..k) are output indices (any order,
+ * no repeats needed); descriptor j gets out = j, so outs[j] must point to output sel[j].
+ * dst must hold k * sizeof(st_desc) bytes.  Used for on-demand loads of single tensors. */
+st_status st_index_descs_subset(const st_index* idx, const uint32_t* sel, size_t k,
+                                st_desc* dst, size_t dst_bytes, uint64_t* total_units);
+
+/* Stage the data section of the file at `path` into `blob_dev` (device memory of at least
+ * st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned).  Reads the file in chunks into the
+ * caller's pinned host buffer `pinned` (pinned_bytes >= 2 MiB; it is split into a ring of
+ * chunks) and copies each chunk with hipMemcpyAsync on `side_stream`; records `done_event`
+ * (may be NULL) on that stream after the last copy.  Returns once every read is done and every
+ * copy is enqueued; the pinned buffer must stay allocated until done_event completes.
+ * If `seconds_read` is not NULL it receives
+ * the wall time spent in file reads (for a file -> pinned rate). */
+st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, void* pinned,
+                        size_t pinned_bytes, void* side_stream, void* done_event,
+                        double* seconds_read);
+
+/* Enqueue the grouped materialise kernel on `stream` (hipStream_t; NULL = default stream).
+ *   blob   device copy of the data section (st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned)
+ *   descs  device copy of n st_desc (from st_index_descs or st_index_descs_subset)
+ *   outs   device array of bf16 output pointers, each ST_OUT_ALIGN-aligned and large enough
+ *          for its output's numel elements; descriptor d writes outs[descs[d].out]
+ * One persistent launch covers every descriptor.  Only enqueues: it never allocates, copies or
+ * synchronises; kernel faults surface at the caller's next synchronisation.  Returns ST_E_ARG
+ * for null pointers (n > 0) and ST_E_HIP if the launch fails.  n == 0 is a no-op. */
+st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs,
+                         void* stream);
+
+/* st_materialize with an explicit number of workgroups (0 = the library's persistent default,
+ * a multiple of the device's compute units).  Workgroups beyond the table's work exit at once. */
+st_status st_materialize_grid(const void* blob, const void* descs, size_t n, void* const* outs,
+                              uint32_t grid, void* stream);
+
+/* The library's default persistent grid (workgroups of 256 threads) on the current device. */
+uint32_t st_default_grid(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STMAT_H */

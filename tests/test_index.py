@@ -1,0 +1,217 @@
+"""Host-side tests of libstmat (no GPU): exported symbols, the C index against the oracle's
+parse and classification, descriptor-table invariants, and malformed-input rejection."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import device_checkpoint_dequantisation_amd as st
+from device_checkpoint_dequantisation_amd import _lib
+from tests.st_files import f32_bytes, make_file, raw_header_file
+from tests.test_oracle_format import BAD
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "stmat.h")).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    declared = set(re.findall(r"\b(st_[a-z_0-9]+)\s*\(", text))
+    assert declared, "no declarations found"
+    lib = C.CDLL(_lib.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} is declared in stmat.h but not exported"
+    assert declared == set(_lib.SIGNATURES), "Python signatures out of sync with stmat.h"
+
+
+def _index(buf):
+    return st.SafeTensorIndex.from_bytes(buf)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_index_matches_oracle_on_configs(k):
+    buf = synth.config_bytes(k, small=True)
+    h, outs = oracle.plan(buf)
+    ix = _index(buf)
+    assert ix.data_offset == h.data_offset and ix.data_size == h.data_size
+    ents = ix.tensors()
+    assert [e.name for e in ents] == list(h.entries)
+    for e in ents:
+        o = h.entries[e.name]
+        assert (e.dtype, e.shape, e.begin, e.end) == (o.dtype, o.shape, o.begin, o.end)
+    couts = ix.outputs()
+    assert [c.name for c in couts] == [o.name for o in outs]
+    for c, o in zip(couts, outs):
+        assert c.kind == o.kind and c.shape == o.shape and c.numel == o.numel
+        assert ents[c.tensor].name == o.src.name
+        assert (ents[c.scale].name if c.scale >= 0 else None) == (o.scale.name if o.scale else None)
+        assert (ents[c.scale2].name if c.scale2 >= 0 else None) == (o.scale2.name if o.scale2 else None)
+    assert ix.metadata == h.metadata
+    assert ix.traffic_bytes == h.data_size + 2 * sum(o.numel for o in outs)
+
+
+def test_tiny_traffic_is_the_documented_figure():
+    ix = _index(synth.config_bytes(1))
+    assert ix.data_size == 718_856 and ix.traffic_bytes == 718_856 + 913_408
+
+
+STEP_SHIFT = {"PASS_BF16": 12, "CAST_F16": 12, "CAST_F32": 11, "FP8_TENSOR": 12, "FP8_BLOCK128": 12, "NVFP4": 12}
+
+
+def _descs(table: bytes):
+    return np.frombuffer(table, dtype=np.dtype([(n, t) for n, t in [
+        ("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u8"),
+        ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"), ("div_magic", "<u4"), ("kind", "u1"),
+        ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1"), ("r1", "<u4")]]))
+
+
+@pytest.mark.parametrize("scale", [0, 2])
+def test_descriptor_table_invariants(scale):
+    buf = synth.config_bytes(3, small=True)
+    ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=scale)
+    table, n, units = ix.descs()
+    d = _descs(table)
+    outs = ix.outputs()
+    ents = ix.tensors()
+    assert n == len(outs) == len(d)
+    pos = 0
+    for k, (row, o) in enumerate(zip(d, outs)):
+        assert row["out"] == k and row["numel"] == o.numel and _lib.KINDS[row["kind"]] == o.kind
+        assert row["src"] == ents[o.tensor].begin
+        if o.scale >= 0:
+            assert row["scale"] == ents[o.scale].begin
+        if o.scale2 >= 0:
+            assert row["scale2"] == ents[o.scale2].begin
+        assert row["unit_shift"] == STEP_SHIFT[o.kind] + scale
+        assert row["unit_begin"] == pos
+        pos += -(-o.numel // (1 << int(row["unit_shift"])))
+        if o.kind == "FP8_BLOCK128":
+            assert row["cols"] == o.shape[1] and row["grid_cols"] == -(-o.shape[1] // 128)
+    assert pos == units
+    # arena: 256-byte aligned, disjoint, in order
+    offs = [o.offset for o in outs]
+    assert all(x % 256 == 0 for x in offs)
+    assert all(offs[i] + 2 * outs[i].numel <= offs[i + 1] for i in range(len(offs) - 1))
+    assert ix.arena_bytes >= offs[-1] + 2 * outs[-1].numel
+    assert ix.blob_bytes % 256 == 0 and ix.blob_bytes >= ix.data_size
+    assert ix.device_bytes >= ix.blob_bytes + ix.arena_bytes + 64 * n
+
+
+@pytest.mark.parametrize("cols", [1, 2, 3, 7, 100, 127, 128, 129, 200, 300, 4096, 12288, 65535, 999983, 2 ** 31 - 1,
+                                  2 ** 31, 2 ** 31 + 1, 2 ** 32 - 1])
+def test_block_division_constants_give_exact_quotients(cols):
+    # The planner stores (magic, shift) for dividing a 32-bit element index by the width N; the
+    # quotient rule is checked against exact integer division on edge and random numerators.
+    hdr = ('{"w.weight":{"dtype":"F8_E4M3","shape":[%d,%d],"data_offsets":[0,0]},'
+           '"w.weight_scale_inv":{"dtype":"F32","shape":[%d,%d],"data_offsets":[0,0]}}')
+    # a zero-row weight keeps the file empty while the planner still derives the constants
+    f = raw_header_file(hdr % (0, cols, 0, -(-cols // 128)))
+    d = _descs(_index(f).descs()[0])[0]
+    m, l = int(d["div_magic"]), int(d["div_shift"])
+    rng = np.random.default_rng(cols)
+    ns = [0, 1, cols - 1, cols, cols + 1, 2 ** 32 - 1, 2 ** 32 - 2, (2 ** 32 - 1) // cols * cols,
+          (2 ** 32 - 1) // cols * cols - 1] + rng.integers(0, 2 ** 32, 2000).tolist()
+    for n in ns:
+        n %= 2 ** 32
+        t = (m * n) >> 32
+        q = n if l == 0 else (t + ((n - t) >> 1)) >> (l - 1)
+        assert q == n // cols, (cols, n)
+
+
+def test_subset_table_is_self_contained():
+    buf = synth.config_bytes(5, small=True)
+    ix = _index(buf)
+    full = _descs(ix.descs()[0])
+    sel = [7, 3, 100, 3]
+    table, k, units = ix.descs_subset(sel)
+    d = _descs(table)
+    assert k == 4
+    pos = 0
+    for j, s in enumerate(sel):
+        assert d[j]["out"] == j and d[j]["src"] == full[s]["src"] and d[j]["numel"] == full[s]["numel"]
+        assert d[j]["unit_begin"] == pos
+        pos += -(-int(d[j]["numel"]) // (1 << int(d[j]["unit_shift"])))
+    assert units == pos
+    with pytest.raises(st.StError):
+        ix.descs_subset([10 ** 6])
+
+
+@pytest.mark.parametrize("case", sorted(BAD))
+def test_index_rejects_what_the_oracle_rejects(case):
+    with pytest.raises(st.StError):
+        _index(BAD[case])
+
+
+def test_header_size_and_open(tmp_path):
+    buf = synth.config_bytes(1)
+    p = tmp_path / "c1.safetensors"
+    p.write_bytes(buf)
+    ix = st.SafeTensorIndex.open(str(p))
+    assert ix.data_offset == oracle.parse_header(buf).data_offset
+    n = C.c_uint64()
+    assert _lib.lib().st_header_size(buf[:8], C.byref(n)) == 0 and n.value == ix.data_offset
+    with pytest.raises(st.StError):
+        st.SafeTensorIndex.open(str(tmp_path / "missing.safetensors"))
+    (tmp_path / "trunc.safetensors").write_bytes(buf[:100])
+    with pytest.raises(st.StError):
+        st.SafeTensorIndex.open(str(tmp_path / "trunc.safetensors"))
+
+
+def test_errors_name_the_tensor():
+    f = make_file([("w.weight", "F8_E4M3", (4,), b"\0" * 4)])
+    with pytest.raises(st.StError, match=r"ST_E_SCALE.*w\.weight"):
+        _index(f)
+
+
+def test_bad_options_rejected():
+    with pytest.raises(st.StError):
+        st.SafeTensorIndex.from_bytes(raw_header_file("{}"), unit_log2_scale=9)
+
+
+def _mutations(buf: bytes, rng, count):
+    n = int.from_bytes(buf[:8], "little")
+    hdr = bytearray(buf[8:8 + n])
+    data = buf[8 + n:]
+    for _ in range(count):
+        h = bytearray(hdr)
+        for _ in range(int(rng.integers(1, 4))):
+            op = int(rng.integers(3))
+            i = int(rng.integers(len(h)))
+            if op == 0:
+                h[i] = int(rng.choice(list(b'{}[]":,0123456789-.eE \\u')))
+            elif op == 1:
+                del h[i]
+            else:
+                h.insert(i, int(rng.choice(list(b'{}[]":,09-'))))
+        yield len(h).to_bytes(8, "little") + bytes(h) + data
+
+
+def test_random_header_mutations_accept_and_reject_alike():
+    # The C reader and the oracle must agree on acceptance for corrupted headers and, when both
+    # accept, on the parsed entries.
+    base = make_file([("a.weight", "F8_E4M3", (2, 3), b"\x01" * 6), ("a.scale_weight", "F32", (), f32_bytes(0.5)),
+                      ("b", "BF16", (2,), b"\0" * 4), ("c", "F16", (1, 1), b"\0\0")], metadata={"x": "y"})
+    rng = np.random.default_rng(11)
+    agree = accepted = 0
+    for m in _mutations(base, rng, 600):
+        try:
+            h, outs = oracle.plan(m)
+            ok_o = True
+        except oracle.OracleError:
+            ok_o = False
+        try:
+            ix = _index(m)
+            ok_c = True
+        except st.StError:
+            ok_c = False
+        assert ok_o == ok_c, m[8:]
+        agree += 1
+        if ok_c:
+            accepted += 1
+            assert [e.name for e in ix.tensors()] == list(h.entries)
+            assert [o.name for o in ix.outputs()] == [o.name for o in outs]
+    assert agree == 600
