@@ -48,7 +48,6 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also measure the other checkpoint families")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
-    ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--unit-scale", type=int, default=0)
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
@@ -141,7 +140,7 @@ def measure(k, d, args, rng):
         f"staged {ix.data_size / 1e9:.3f} GB in {stage_s:.2f}s (reads {read_s:.2f}s)")
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        ck.materialize(stream, args.grid)
+        ck.materialize(stream)
     torch.cuda.synchronize()
     ok, checked, bad = sampled_parity(path, ix, ck, rng)
     log(f"[bench] sampled parity vs oracle: {'ok' if ok else 'MISMATCH in ' + str(bad)} ({checked} elements)")
@@ -151,7 +150,7 @@ def measure(k, d, args, rng):
     t0 = time.perf_counter()
     for a, b in evs:
         a.record(stream)
-        ck.materialize(stream, args.grid)
+        ck.materialize(stream)
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -140,21 +140,23 @@ class SafeTensorIndex:
         """Output (weight) names, in output order; metadata only."""
         return [self.output(k).name for k in range(self.num_outputs)]
 
-    # ---- descriptor tables
-    def descs(self):
-        """(bytes of the full descriptor table, number of descriptors, total work units)."""
-        n, nb, units = C.c_size_t(), C.c_size_t(), C.c_uint64()
-        p = lib().st_index_descs(self._h, C.byref(n), C.byref(nb), C.byref(units))
-        return (C.string_at(p, nb.value) if nb.value else b""), n.value, units.value
+    # ---- work tables
+    def table(self):
+        """(bytes of the work table for every output, work units = the n st_materialize takes)."""
+        nb, units = C.c_size_t(), C.c_uint64()
+        p = lib().st_index_table(self._h, C.byref(nb), C.byref(units))
+        return C.string_at(p, nb.value), units.value
 
-    def descs_subset(self, sel):
-        """Self-contained table for outputs ``sel`` (descriptor j writes outs[j])."""
+    def table_subset(self, sel):
+        """Self-contained work table for outputs ``sel`` (descriptor j writes outs[j])."""
         k = len(sel)
         arr = (C.c_uint32 * max(1, k))(*sel)
-        dst = (Desc * max(1, k))()
-        units = C.c_uint64()
-        check(lib().st_index_descs_subset(self._h, arr, k, dst, C.sizeof(dst), C.byref(units)), "st_index_descs_subset")
-        return C.string_at(dst, k * C.sizeof(Desc)), k, units.value
+        nb, units = C.c_size_t(), C.c_uint64()
+        check(lib().st_index_table_subset(self._h, arr, k, None, 0, C.byref(nb), C.byref(units)), "st_index_table_subset")
+        dst = C.create_string_buffer(nb.value)
+        check(lib().st_index_table_subset(self._h, arr, k, dst, nb.value, C.byref(nb), C.byref(units)),
+              "st_index_table_subset")
+        return dst.raw[: nb.value], units.value
 
 
 def _torch():
@@ -172,13 +174,13 @@ def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> 
     return secs.value
 
 
-def materialize(blob, descs, n: int, outs, stream=None, grid: int = 0):
-    """Enqueue the grouped kernel: ``blob``, ``descs`` (n * 64 bytes) and ``outs`` (n device
-    pointers, int64) are device tensors."""
+def materialize(blob, table, units: int, outs, stream=None):
+    """Enqueue the grouped kernel: ``blob`` (the staged data section), ``table`` (a work table) and
+    ``outs`` (device pointers, int64) are device tensors; ``units`` is the table's work-unit count."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
-    check(lib().st_materialize_grid(C.c_void_p(blob.data_ptr()), C.c_void_p(descs.data_ptr()), n,
-                                    C.c_void_p(outs.data_ptr()), grid, C.c_void_p(s.cuda_stream)), "st_materialize")
+    check(lib().st_materialize(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
+                               C.c_void_p(outs.data_ptr()), C.c_void_p(s.cuda_stream)), "st_materialize")
 
 
 class DeviceCheckpoint:
@@ -198,10 +200,9 @@ class DeviceCheckpoint:
             if need > free:
                 raise MemoryError(f"checkpoint needs {need} bytes of device memory; {free} of {total} are free")
         self.blob = torch.empty(index.blob_bytes, dtype=torch.uint8, device=self.device)
-        table, n, units = index.descs()
-        self.n = n
-        self.total_units = units
-        self.descs = torch.frombuffer(bytearray(table or b"\0" * 64), dtype=torch.uint8).to(self.device)
+        table, units = index.table()
+        self.units = units
+        self.table = torch.frombuffer(bytearray(table), dtype=torch.uint8).to(self.device)
         self.arena = torch.empty(max(1, index.arena_bytes // 2), dtype=torch.bfloat16, device=self.device)
         outs = index.outputs()
         base = self.arena.data_ptr()
@@ -230,9 +231,9 @@ class DeviceCheckpoint:
             host = torch.frombuffer(bytearray(data_section), dtype=torch.uint8)
             self.blob[: len(data_section)].copy_(host)
 
-    def materialize(self, stream=None, grid: int = 0):
-        if self.n:
-            materialize(self.blob, self.descs, self.n, self.outs, stream, grid)
+    def materialize(self, stream=None):
+        if self.units:
+            materialize(self.blob, self.table, self.units, self.outs, stream)
         return self.tensors
 
 

@@ -29,11 +29,20 @@ class OutputInfo(C.Structure):
 class Desc(C.Structure):
     _fields_ = [("src", C.c_uint64), ("scale", C.c_uint64), ("scale2", C.c_uint64), ("numel", C.c_uint64),
                 ("unit_begin", C.c_uint64), ("out", C.c_uint32), ("cols", C.c_uint32), ("grid_cols", C.c_uint32),
-                ("div_magic", C.c_uint32), ("kind", C.c_uint8), ("unit_shift", C.c_uint8), ("div_shift", C.c_uint8),
-                ("reserved0", C.c_uint8), ("reserved1", C.c_uint32)]
+                ("div_magic", C.c_uint32), ("meta", C.c_uint32), ("reserved", C.c_uint32)]
 
 
 assert C.sizeof(Desc) == 64
+
+
+class TableHeader(C.Structure):
+    _fields_ = [("magic", C.c_uint32), ("n_desc", C.c_uint32), ("units", C.c_uint64), ("desc_offset", C.c_uint64),
+                ("map_offset", C.c_uint64), ("bytes", C.c_uint64), ("reserved", C.c_uint64 * 3)]
+
+
+assert C.sizeof(TableHeader) == 64
+TABLE_MAGIC = 0x324D5453
+UNITS_PER_GROUP = 4
 
 
 class PlanOpts(C.Structure):
@@ -60,14 +69,12 @@ SIGNATURES = {
     "st_index_output_arena_bytes": (C.c_uint64, [C.c_void_p]),
     "st_index_traffic_bytes": (C.c_uint64, [C.c_void_p]),
     "st_index_device_bytes": (C.c_uint64, [C.c_void_p]),
-    "st_index_descs": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
-    "st_index_descs_subset": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_void_p, C.c_size_t,
-                                        C.POINTER(C.c_uint64)]),
+    "st_index_table": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
+    "st_index_table_subset": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_void_p, C.c_size_t,
+                                        C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
     "st_stage_file": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                                 C.POINTER(C.c_double)]),
     "st_materialize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
-    "st_materialize_grid": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32, C.c_void_p]),
-    "st_default_grid": (C.c_uint32, []),
 }
 
 _lib = None

@@ -19,7 +19,9 @@ COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"
 # Device code: IEEE semantics (no contraction, no fast-math, fp32 subnormals kept) and no
 # packed-fp32 instructions.
 DEVICE = ["-O3", f"--offload-arch={ARCH}", "-ffp-contract=off", "-fno-fast-math",
-          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # kernel arguments arrive in SGPRs instead of through a scalar load
+          "-mllvm", "-amdgpu-kernarg-preload-count=8"]
 
 
 def _run(cmd, verbose):

@@ -345,7 +345,7 @@ struct st_index {
     std::vector<Output> outputs;
     std::vector<uint64_t> out_offset;  // arena offsets
     uint64_t arena_bytes = 0;
-    std::vector<st_desc> descs;
+    std::vector<unsigned char> table;  // header + descriptors + unit map
     uint64_t total_units = 0;
     uint32_t unit_log2_scale = 0;
 };
@@ -574,37 +574,72 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     d.numel = o.numel;
     d.unit_begin = unit_begin;
     d.out = out_slot;
-    d.kind = uint8_t(o.kind);
-    d.unit_shift = uint8_t(stk::step_shift(o.kind) + ix.unit_log2_scale);
+    const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
+    uint32_t div_shift = 0;
     if (o.kind == ST_KIND_FP8_BLOCK128) {
         uint32_t n = uint32_t(o.shape[1]);
         d.cols = n;
         d.grid_cols = (n + 127) / 128;
         if (n) {
             d.div_magic = stk::div_magic(n);
-            d.div_shift = uint8_t(stk::div_shift(n));
+            div_shift = stk::div_shift(n);
         }
     } else if (o.kind == ST_KIND_NVFP4) {
         d.cols = uint32_t(o.shape[1]);
     }
-    *units = (o.numel + (uint64_t(1) << d.unit_shift) - 1) >> d.unit_shift;
+    d.meta = uint32_t(o.kind) | unit_shift << 8 | div_shift << 16;
+    *units = (o.numel + (uint64_t(1) << unit_shift) - 1) >> unit_shift;
     return d;
 }
 
+// Work table for outputs sel[0..k): header, descriptors (descriptor j writes outs[j]) and the
+// map from each group of ST_UNITS_PER_GROUP units to the descriptor holding its first unit.
+std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out) {
+    std::vector<st_desc> descs(k);
+    std::vector<uint64_t> units(k);
+    uint64_t pos = 0;
+    for (size_t j = 0; j < k; ++j) {
+        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units[j]);
+        pos += units[j];
+    }
+    const uint64_t groups = (pos + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
+    st_table_header h;
+    memset(&h, 0, sizeof h);
+    h.magic = ST_TABLE_MAGIC;
+    h.n_desc = uint32_t(k);
+    h.units = pos;
+    h.map_offset = sizeof(st_table_header);
+    h.desc_offset = stk::table_desc_offset(groups);
+    h.bytes = h.desc_offset + k * sizeof(st_desc);
+    std::vector<unsigned char> t(h.bytes, 0);
+    memcpy(t.data(), &h, sizeof h);
+    if (k) memcpy(t.data() + h.desc_offset, descs.data(), k * sizeof(st_desc));
+    uint32_t* map = reinterpret_cast<uint32_t*>(t.data() + h.map_offset);
+    size_t d = 0;
+    for (uint64_t g = 0; g < groups; ++g) {
+        const uint64_t u = g * ST_UNITS_PER_GROUP;
+        while (descs[d].unit_begin + units[d] <= u) ++d;  // skips outputs with no units
+        map[g] = uint32_t(d);
+    }
+    *units_out = pos;
+    return t;
+}
+
 st_status plan(st_index& ix) {
-    uint64_t pos = 0, unit = 0;
+    if (ix.outputs.size() >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "more than 2^32 outputs");
+    uint64_t pos = 0;
     ix.out_offset.resize(ix.outputs.size());
-    ix.descs.resize(ix.outputs.size());
     for (size_t k = 0; k < ix.outputs.size(); ++k) {
         ix.out_offset[k] = pos;
         pos = round_up(pos + ix.outputs[k].numel * 2, 256);
-        uint64_t units;
-        ix.descs[k] = make_desc(ix, ix.outputs[k], uint32_t(k), unit, &units);
-        unit += units;
     }
-    if (ix.outputs.size() >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "more than 2^32 outputs");
     ix.arena_bytes = pos;
-    ix.total_units = unit;
+    std::vector<uint32_t> all(ix.outputs.size());
+    for (size_t k = 0; k < all.size(); ++k) all[k] = uint32_t(k);
+    ix.table = build_table(ix, all.data(), all.size(), &ix.total_units);
+    if (ix.total_units / ST_UNITS_PER_GROUP >= (uint64_t(1) << 31))
+        return st_fail(ST_E_SHAPE, "checkpoint needs %llu work units; at most 2^33 are supported",
+                       (unsigned long long)ix.total_units);
     return ST_OK;
 }
 
@@ -766,32 +801,36 @@ extern "C" uint64_t st_index_traffic_bytes(const st_index* idx) {
 extern "C" uint64_t st_index_device_bytes(const st_index* idx) {
     if (!idx) return 0;
     uint64_t n = idx->outputs.size();
-    return st_index_blob_bytes(idx) + round_up(n * sizeof(st_desc), 256) + round_up(n * sizeof(void*), 256) +
+    return st_index_blob_bytes(idx) + round_up(idx->table.size(), 256) + round_up(n * sizeof(void*), 256) +
            st_index_output_arena_bytes(idx);
 }
 
-extern "C" const st_desc* st_index_descs(const st_index* idx, size_t* n, size_t* bytes, uint64_t* total_units) {
+extern "C" const void* st_index_table(const st_index* idx, size_t* bytes, uint64_t* units) {
     if (!idx) return nullptr;
-    if (n) *n = idx->descs.size();
-    if (bytes) *bytes = idx->descs.size() * sizeof(st_desc);
-    if (total_units) *total_units = idx->total_units;
-    return idx->descs.data();
+    if (bytes) *bytes = idx->table.size();
+    if (units) *units = idx->total_units;
+    return idx->table.data();
 }
 
-extern "C" st_status st_index_descs_subset(const st_index* idx, const uint32_t* sel, size_t k, st_desc* dst,
-                                           size_t dst_bytes, uint64_t* total_units) {
+extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t k, void* dst,
+                                           size_t dst_bytes, size_t* bytes, uint64_t* units) {
     st_clear();
-    if (!idx || (k && (!sel || !dst))) return st_fail(ST_E_ARG, "st_index_descs_subset: null pointer");
-    if (dst_bytes < k * sizeof(st_desc))
-        return st_fail(ST_E_ARG, "st_index_descs_subset: dst holds %zu bytes, %zu needed", dst_bytes, k * sizeof(st_desc));
-    uint64_t unit = 0;
-    for (size_t j = 0; j < k; ++j) {
+    if (!idx || (k && !sel)) return st_fail(ST_E_ARG, "st_index_table_subset: null pointer");
+    for (size_t j = 0; j < k; ++j)
         if (sel[j] >= idx->outputs.size())
-            return st_fail(ST_E_ARG, "st_index_descs_subset: output %u out of range (%zu)", sel[j], idx->outputs.size());
-        uint64_t units;
-        dst[j] = make_desc(*idx, idx->outputs[sel[j]], uint32_t(j), unit, &units);
-        unit += units;
+            return st_fail(ST_E_ARG, "st_index_table_subset: output %u out of range (%zu)", sel[j], idx->outputs.size());
+    uint64_t u = 0;
+    std::vector<unsigned char> t;
+    try {
+        t = build_table(*idx, sel, k, &u);
+    } catch (const std::bad_alloc&) {
+        return st_fail(ST_E_NOMEM, "out of host memory");
     }
-    if (total_units) *total_units = unit;
+    if (bytes) *bytes = t.size();
+    if (units) *units = u;
+    if (!dst) return ST_OK;
+    if (dst_bytes < t.size())
+        return st_fail(ST_E_ARG, "st_index_table_subset: dst holds %zu bytes, %zu needed", dst_bytes, t.size());
+    memcpy(dst, t.data(), t.size());
     return ST_OK;
 }

@@ -1,5 +1,5 @@
-// The grouped materialise kernel: one persistent launch turns every descriptor's bytes in the
-// device blob into bf16 outputs.
+// The grouped materialise kernel: one launch turns every descriptor's bytes in the device blob
+// into bf16 outputs.
 //
 // What it computes is fixed by the checkpoint formats the pages name ("Resident Modal LLM
 // Architecture", "Current Backend Boundary": Qwen block-FP8, ModelOpt NVFP4; "Disk tier
@@ -7,127 +7,152 @@
 // OCP E4M3 / OCP-MX E2M1 codes, one IEEE binary32 round-to-nearest-even multiply per scale and a
 // round-to-nearest-even narrowing to bfloat16 (NaN -> 0x7FC0, no subnormal flushing).
 //
-// Shape of the work.  The path is a memory-bound elementwise codec (1-6 bytes of HBM traffic
-// per element, a handful of VALU operations), so there is no matrix-core work here: the design
-// goals are full 16-byte coalesced HBM accesses, enough bytes in flight per CU, and balance.
-//  * Work units.  Each output is cut into units of 2^unit_shift elements; descriptors carry the
-//    prefix sum of units.  Units are sized per kind to move 10-16 KB of HBM traffic each.
-//  * Persistent, interleaved schedule.  The grid holds a fixed number of workgroups of 4 waves;
-//    wave w takes units w, w + W, w + 2W, ... (W = waves in the grid), so every wave samples
-//    all tensors evenly and tiny tensors are spread one unit per wave.  A wave keeps its current
-//    descriptor and finds the next one by a forward binary search over the unit prefix.
-//  * Chunks.  Within a unit, lane l of a wave handles chunks l, l + 64, ... of 8-32 elements.
-//    A wave step issues every chunk's loads before decoding any of them.
-//  * Unaligned sources.  Tensors may start at any byte.  Loads are always whole, aligned 16-byte
-//    words; a source offset r = src mod 16 (uniform per tensor) is undone in registers with
-//    v_alignbyte over the two words a chunk straddles.  The four dword offsets are separate
-//    template instances selected once per unit.
-//  * Tails, NaN codes, scales that could overflow when folded, odd block-FP8 widths and
-//    misaligned outputs go through an exact per-element path.
+// Shape of the work.  This is a memory-bound elementwise codec (2.6-6 bytes of HBM traffic per
+// element, a handful of VALU operations per element), so there is no matrix-core work; what
+// matters on gfx950 is how the HBM traffic is issued:
+//  * One wavefront per work unit, one-shot.  A unit is 512-2048 elements of one output (about
+//    1-2 KB read, 1-4 KB written).  Each wavefront loads its unit, decodes, stores and exits.
+//    Measured on MI355X, one-shot wavefronts sustain ~20% more read+write bandwidth than any
+//    persistent loop tried (grid-stride, contiguous ranges, software-pipelined), because a
+//    persistent wavefront's next loads wait behind its own outstanding stores (vmcnt counts both).
+//  * Lane-contiguous stores.  Lane l writes 16-byte output words o*64 + l, so every store
+//    instruction of a wavefront covers 1 KB of contiguous output; lanes read whatever input bytes
+//    their output words need (4, 8, 16 or 32 bytes).
+//  * XCD-contiguous order.  The hardware hands workgroup b to XCD b mod 8; workgroups are
+//    renumbered so each XCD streams through one contiguous eighth of the work.
+//  * Tiny tensors.  Units are numbered consecutively across outputs and a workgroup's four
+//    wavefronts take four consecutive units, whatever output they belong to, so small tensors are
+//    packed at wavefront granularity.  A per-workgroup map gives the descriptor of the group's
+//    first unit; a wavefront walks forward at most three descriptors.
+//  * Unaligned sources.  A tensor may start at any byte.  Loads are always naturally aligned
+//    words; the offset r of the source within a word (the same for every lane of a unit) is
+//    removed in registers with v_alignbyte over the two words the bytes straddle.
+//  * Decoding uses gfx950's conversion instructions (fp8 and fp4 to fp32, fp32 to bf16), each
+//    checked exhaustively against the exact decoding on the device; one fp32 multiply per scale.
+//  * Tails, NaN inputs, non-finite scales, block-FP8 widths not a multiple of 16 and misaligned
+//    outputs go through an exact per-element path written from the definitions alone.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
+#include <cstddef>
 
 #include "st_internal.h"
 
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
-constexpr uint32_t kBlock = 256;            // threads per workgroup (4 waves)
-constexpr uint32_t kWavesPerBlock = kBlock / stk::kWave;
+// Wave-uniform reads of data the kernel never writes (work table, output pointers, scalar
+// scales) go through the constant address space, so they become scalar loads.
+template <class T>
+__device__ __forceinline__ T ld_uniform(const void* p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) T*>(reinterpret_cast<uintptr_t>(p));
+}
 
-// ------------------------------------------------------------------------- memory helpers
+constexpr uint32_t kBlock = 256;  // threads per workgroup: ST_UNITS_PER_GROUP wavefronts
+static_assert(kBlock == ST_UNITS_PER_GROUP * stk::kWave, "one wavefront per unit");
+constexpr uint32_t kMaxGridX = 1u << 22;  // keeps gridDim.x * 256 below 2^32
 
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
-__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
+// ------------------------------------------------------------------------- small helpers
 
 __device__ __forceinline__ uint32_t ld_u8(const uint8_t* p) { return *p; }
 __device__ __forceinline__ uint32_t ld_u16_any(const uint8_t* p) { return uint32_t(p[0]) | uint32_t(p[1]) << 8; }
 __device__ __forceinline__ uint32_t ld_u32_any(const uint8_t* p) {
     return uint32_t(p[0]) | uint32_t(p[1]) << 8 | uint32_t(p[2]) << 16 | uint32_t(p[3]) << 24;
 }
-__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
-__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
-
-// Bytes [r, r + 16) of the 32-byte little-endian sequence a|b, with r = 4 * Q + sh.
-template <int Q>
-__device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, uint32_t sh) {
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    u32x4 o;
-    o.x = __builtin_amdgcn_alignbyte(w[Q + 1], w[Q + 0], sh);
-    o.y = __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], sh);
-    o.z = __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], sh);
-    o.w = __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], sh);
-    return o;
+// fp32 at p, where `aligned` says whether p is 4-byte aligned (uniform per descriptor)
+__device__ __forceinline__ float ld_f32(const uint8_t* p, bool aligned) {
+    return aligned ? *reinterpret_cast<const float*>(p) : __builtin_bit_cast(float, ld_u32_any(p));
 }
-
-// ------------------------------------------------------------------------- arithmetic
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+// A wave-uniform fp32 at any byte address: the aligned dword(s) around it, by scalar loads.
+__device__ __forceinline__ float ld_scalar_f32(const uint8_t* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t r = a & 3u;
+    const uint32_t lo = ld_uniform<uint32_t>(reinterpret_cast<const void*>(a - r));
+    if (r == 0) return __builtin_bit_cast(float, lo);
+    const uint32_t hi = ld_uniform<uint32_t>(reinterpret_cast<const void*>(a - r + 4));
+    return __builtin_bit_cast(float, uint32_t((uint64_t(hi) << 32 | lo) >> (8 * r)));
+}
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // Upper 16 bits = bf16 of f rounded to nearest, ties to even (f not NaN).
 __device__ __forceinline__ uint32_t rne_hi(float f) {
     const uint32_t u = as_u32(f);
     return u + 0x7FFFu + ((u >> 16) & 1u);
 }
-// Two bf16 (a at the lower address) packed in one dword; inputs not NaN.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return __builtin_amdgcn_perm(rne_hi(b), rne_hi(a), 0x07060302u);
-}
 __device__ __forceinline__ uint32_t bf16_canon(float f) { return f != f ? 0x7FC0u : rne_hi(f) >> 16; }
 
 __device__ __forceinline__ float h2f(uint32_t h16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
 }
-
-// e4m3 code -> its value times 2^-8, exactly, by moving the code's exponent and mantissa into
-// an fp16 exponent/mantissa field (subnormal codes land on fp16 subnormals).  NaN codes are not
-// handled here.
+// Exact path decoding.  e4m3 code -> its value times 2^-8, exactly: the code's exponent and
+// mantissa fields are moved into an fp16's (subnormal codes land on fp16 subnormals).
 __device__ __forceinline__ float e4m3_x2m8(uint32_t c) { return h2f(((c & 0x7Fu) << 7) | ((c & 0x80u) << 8)); }
 // e2m1 code -> its value times 2^-14, exactly (same construction with a 2-bit exponent).
 __device__ __forceinline__ float e2m1_x2m14(uint32_t n) { return h2f(((n & 7u) << 9) | ((n & 8u) << 12)); }
-
 __device__ __forceinline__ float e4m3_exact(uint32_t c) {
     return (c & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : e4m3_x2m8(c) * 256.0f;
 }
 __device__ __forceinline__ float e2m1_exact(uint32_t n) { return e2m1_x2m14(n) * 16384.0f; }
-
-// A scale s can absorb the 2^8 of e4m3_x2m8 exactly unless s * 256 overflows; for NaN or
-// infinite s the result is NaN or infinite either way, but those take the exact path so the NaN
-// comes out canonical.
-__device__ __forceinline__ bool foldable(float s) { return __builtin_fabsf(s) < 0x1p119f; }
 
 // True if any byte of x is an e4m3 NaN code (0x7F or 0xFF).
 __device__ __forceinline__ bool has_nan_code(uint32_t x) {
     return (((x & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0;
 }
 
-// ------------------------------------------------------------------------- exact element path
+// gfx950 conversion instructions used on the fast path.  Each was checked exhaustively on the
+// device against the exact decoding above: v_cvt_pk_f32_fp8 on every pair of e4m3 codes (it
+// decodes OCP e4m3fn), v_cvt_scalef32_pk_f32_fp4 with scale 1.0 on every byte, and
+// v_cvt_pk_bf16_f32 on all 2^32 fp32 patterns (round to nearest even, subnormals kept; it keeps
+// NaN payloads, so the fast path never hands it a NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {  // a at the lower address
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// e4m3 codes in bytes 0,1 (HI: 2,3) of x -> exact fp32 values
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2(uint32_t x) { return __builtin_amdgcn_cvt_pk_f32_fp8(x, HI); }
+// e2m1 codes in byte P of x (low nibble first) -> exact fp32 values
+template <int P>
+__device__ __forceinline__ f32x2 fp4x2(uint32_t x) { return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, P); }
+__device__ __forceinline__ bool finite(float s) { return __builtin_fabsf(s) <= 3.4028234663852886e38f; }
+
+// ------------------------------------------------------------------------- descriptors
 
 struct Desc {
     uint64_t src, scale, scale2, numel, unit_begin;
     uint32_t out, cols, grid_cols, div_magic, kind, unit_shift, div_shift;
 };
 
-__device__ __forceinline__ Desc load_desc(const st_desc* __restrict__ descs, uint32_t d) {
-    const st_desc& s = descs[d];
+// The 64-byte descriptor in one scalar load.
+__device__ __forceinline__ Desc load_desc(const st_desc* d) {
+    const u32x16 w = ld_uniform<u32x16>(d);
     Desc r;
-    r.src = s.src;
-    r.scale = s.scale;
-    r.scale2 = s.scale2;
-    r.numel = s.numel;
-    r.unit_begin = s.unit_begin;
-    r.out = s.out;
-    r.cols = s.cols;
-    r.grid_cols = s.grid_cols;
-    r.div_magic = s.div_magic;
-    r.kind = s.kind;
-    r.unit_shift = s.unit_shift;
-    r.div_shift = s.div_shift;
+    r.src = uint64_t(w[1]) << 32 | w[0];
+    r.scale = uint64_t(w[3]) << 32 | w[2];
+    r.scale2 = uint64_t(w[5]) << 32 | w[4];
+    r.numel = uint64_t(w[7]) << 32 | w[6];
+    r.unit_begin = uint64_t(w[9]) << 32 | w[8];
+    r.out = w[10];
+    r.cols = w[11];
+    r.grid_cols = w[12];
+    r.div_magic = w[13];
+    r.kind = w[14] & 0xFFu;
+    r.unit_shift = (w[14] >> 8) & 0xFFu;
+    r.div_shift = (w[14] >> 16) & 0xFFu;
     return r;
+}
+static_assert(offsetof(st_desc, meta) == 14 * 4, "descriptor layout");
+__device__ __forceinline__ uint64_t units_of(const Desc& D) {
+    return (D.numel + (uint64_t(1) << D.unit_shift) - 1) >> D.unit_shift;
 }
 
 // bf16 bits of element e of descriptor D, straight from the definition, byte by byte.
-__device__ __noinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob, Desc D, uint64_t e) {
+__device__ __forceinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob, const Desc& D, uint64_t e) {
     const uint8_t* s = blob + D.src;
     switch (D.kind) {
         case ST_KIND_PASS_BF16: return ld_u16_any(s + 2 * e);
@@ -151,303 +176,291 @@ __device__ __noinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob, De
     }
 }
 
-__device__ __noinline__ void chunk_exact(const uint8_t* __restrict__ blob, Desc D, uint16_t* __restrict__ out, uint64_t e,
-                            uint32_t n) {
-    for (uint32_t k = 0; k < n; ++k) out[e + k] = uint16_t(elem_exact(blob, D, e + k));
-}
-
 // ------------------------------------------------------------------------- per-kind chunks
 //
-// Each Kind describes one chunk: IN = source bytes per chunk (a multiple of 16), CH = elements,
-// load geometry and the fast decode.  `fast` returns false when the chunk must take the exact
-// path (NaN codes, unfoldable or non-finite scales, block straddles).
+// A Kind decodes one chunk of CE elements (CE/8 16-byte output words, stored adjacently) from IB
+// input bytes, fetched as naturally aligned LG-byte words.  `fast` returns false when the chunk
+// must take the exact path.  CH = chunks per lane per step; chunk c of a step belongs to lane
+// c % 64.
 
-struct UnitCtx {
+// Per-unit context.  The scale is only loaded here; deciding whether it folds, and whether the
+// output pointer is usable, happens in the decode, after the data loads have been issued.
+struct Ctx {
     const uint8_t* blob;
     Desc D;
-    uint16_t* out;
-    float s;          // FP8_TENSOR: scale * 256 (foldable) ; NVFP4: global scale
-    bool exact_all;   // every chunk takes the exact path
+    float s;         // FP8_TENSOR: the per-tensor scale; NVFP4: the global scale
+    bool scale_al;   // the descriptor's scale data is 4-byte aligned
+    uintptr_t out;   // output address
 };
 
+// A usable output is a bf16 address; a 16-byte aligned one takes the vector stores.
+__device__ __forceinline__ bool out_ok(const Ctx& c) { return (c.out & 1u) == 0; }
+__device__ __forceinline__ bool out_fast(const Ctx& c) { return (c.out & 15u) == 0; }
+
 struct KPass {
-    static constexpr uint32_t CH = stk::kChunkPass, IN = 16, STEPS = stk::kStepsPass, SRC_SHIFT = 1;
-    __device__ static __forceinline__ bool fast(const UnitCtx&, const u32x4* in, uint64_t, uint32_t, u32x4* o) {
-        o[0] = in[0];
+    static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
+        o[0] = u32x4{in[0], in[1], in[2], in[3]};
         return true;
     }
 };
 
 struct KF16 {
-    static constexpr uint32_t CH = stk::kChunkPass, IN = 16, STEPS = stk::kStepsPass, SRC_SHIFT = 1;
-    __device__ static __forceinline__ bool fast(const UnitCtx&, const u32x4* in, uint64_t, uint32_t, u32x4* o) {
-        const u32x4 x = in[0];
-        // fp16 NaN: exponent all ones and a non-zero mantissa, in either half of a dword
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
         bool nan = false;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) nan |= (w[k] & 0x7FFFu) > 0x7C00u || (w[k] & 0x7FFF0000u) > 0x7C000000u;
+        for (int k = 0; k < 4; ++k) nan |= (in[k] & 0x7FFFu) > 0x7C00u || (in[k] & 0x7FFF0000u) > 0x7C000000u;
         if (nan) return false;
         uint32_t r[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = pack_bf16(h2f(w[k] & 0xFFFFu), h2f(w[k] >> 16));
+        for (int k = 0; k < 4; ++k) r[k] = cvt_bf16x2(h2f(in[k] & 0xFFFFu), h2f(in[k] >> 16));
         o[0] = u32x4{r[0], r[1], r[2], r[3]};
         return true;
     }
 };
 
 struct KF32 {
-    static constexpr uint32_t CH = stk::kChunkF32, IN = 32, STEPS = stk::kStepsF32, SRC_SHIFT = 2;
-    __device__ static __forceinline__ bool fast(const UnitCtx&, const u32x4* in, uint64_t, uint32_t, u32x4* o) {
-        const uint32_t w[8] = {in[0].x, in[0].y, in[0].z, in[0].w, in[1].x, in[1].y, in[1].z, in[1].w};
+    static constexpr uint32_t CE = 8, IB = 32, LG = 16, CH = stk::kWordsF32;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 4; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
         bool nan = false;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) nan |= (w[k] & 0x7FFFFFFFu) > 0x7F800000u;
+        for (int k = 0; k < 8; ++k) nan |= (in[k] & 0x7FFFFFFFu) > 0x7F800000u;
         if (nan) return false;
         uint32_t r[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = pack_bf16(as_f32(w[2 * k]), as_f32(w[2 * k + 1]));
+        for (int k = 0; k < 4; ++k) r[k] = cvt_bf16x2(as_f32(in[2 * k]), as_f32(in[2 * k + 1]));
         o[0] = u32x4{r[0], r[1], r[2], r[3]};
         return true;
     }
 };
 
-__device__ __forceinline__ void fp8_dword(uint32_t x, float s256, uint32_t& lo, uint32_t& hi) {
-    lo = pack_bf16(e4m3_x2m8(x & 0xFFu) * s256, e4m3_x2m8((x >> 8) & 0xFFu) * s256);
-    hi = pack_bf16(e4m3_x2m8((x >> 16) & 0xFFu) * s256, e4m3_x2m8(x >> 24) * s256);
+// 4 e4m3 codes times s -> two packed bf16 pairs
+__device__ __forceinline__ void fp8x4_scaled(uint32_t x, float s, uint32_t& lo, uint32_t& hi) {
+    const f32x2 a = fp8x2<false>(x), b = fp8x2<true>(x);
+    lo = cvt_bf16x2(a.x * s, a.y * s);
+    hi = cvt_bf16x2(b.x * s, b.y * s);
 }
-
-__device__ __forceinline__ bool fp8_chunk(const u32x4& x, float s256, u32x4* o) {
-    if (has_nan_code(x.x | 0) || has_nan_code(x.y) || has_nan_code(x.z) || has_nan_code(x.w)) return false;
+// 16 e4m3 codes -> two output words; exact path if any code is NaN or s is not finite (so no
+// product is NaN)
+__device__ __forceinline__ bool fp8_chunk(const uint32_t* in, float s, u32x4* o) {
+    const uint32_t t = ((in[0] & 0x7F7F7F7Fu) + 0x01010101u) | ((in[1] & 0x7F7F7F7Fu) + 0x01010101u) |
+                       ((in[2] & 0x7F7F7F7Fu) + 0x01010101u) | ((in[3] & 0x7F7F7F7Fu) + 0x01010101u);
+    if ((t & 0x80808080u) != 0 || !finite(s)) return false;
     uint32_t r[8];
-    fp8_dword(x.x, s256, r[0], r[1]);
-    fp8_dword(x.y, s256, r[2], r[3]);
-    fp8_dword(x.z, s256, r[4], r[5]);
-    fp8_dword(x.w, s256, r[6], r[7]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fp8x4_scaled(in[k], s, r[2 * k], r[2 * k + 1]);
     o[0] = u32x4{r[0], r[1], r[2], r[3]};
     o[1] = u32x4{r[4], r[5], r[6], r[7]};
     return true;
 }
 
 struct KFp8Tensor {
-    static constexpr uint32_t CH = stk::kChunkFp8, IN = 16, STEPS = stk::kStepsFp8, SRC_SHIFT = 0;
-    __device__ static __forceinline__ bool fast(const UnitCtx& c, const u32x4* in, uint64_t, uint32_t, u32x4* o) {
-        return fp8_chunk(in[0], c.s, o);
+    static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, u32x4* o) {
+        return fp8_chunk(in, c.s, o);
     }
 };
 
 struct KFp8Block {
-    static constexpr uint32_t CH = stk::kChunkFp8, IN = 16, STEPS = stk::kStepsFp8, SRC_SHIFT = 0;
-    // e: first element of the chunk (multiple of 16); the caller guarantees cols % 16 == 0, so
-    // the chunk lies in one row and one 128-column block.
-    __device__ static __forceinline__ bool fast(const UnitCtx& c, const u32x4* in, uint64_t e, uint32_t, u32x4* o) {
+    static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
+    // e: first element of the chunk (a multiple of 16); with cols % 16 == 0 the chunk lies in
+    // one row and one 128-column block, otherwise it takes the exact path.
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, u32x4* o) {
+        if ((c.D.cols & 15u) != 0) return false;
         const uint32_t e32 = uint32_t(e);
         const uint32_t row = stk::div_apply(e32, c.D.div_magic, c.D.div_shift);
         const uint32_t col = e32 - row * c.D.cols;
-        const uint8_t* sp = c.blob + c.D.scale + 4ull * ((row >> 7) * c.D.grid_cols + (col >> 7));
-        const float S = (c.D.scale & 3) == 0 ? *reinterpret_cast<const float*>(sp) : as_f32(ld_u32_any(sp));
-        if (!foldable(S)) return false;
-        return fp8_chunk(in[0], S * 256.0f, o);
+        const float S = ld_f32(c.blob + c.D.scale + 4ull * ((row >> 7) * c.D.grid_cols + (col >> 7)), c.scale_al);
+        return fp8_chunk(in, S, o);
     }
 };
 
 struct KFp4 {
-    static constexpr uint32_t CH = stk::kChunkFp4, IN = 16, STEPS = stk::kStepsFp4, SRC_SHIFT = 0;  // src = e / 2
-    __device__ static __forceinline__ bool fast(const UnitCtx& c, const u32x4* in, uint64_t e, uint32_t, u32x4* o) {
-        // two block scales for elements [e, e + 16) and [e + 16, e + 32)
-        const uint8_t* sp = c.blob + c.D.scale + (e >> 4);
-        const uint32_t b2 = (c.D.scale & 1) == 0 ? uint32_t(*reinterpret_cast<const uint16_t*>(sp)) : ld_u16_any(sp);
-        const uint32_t c0 = b2 & 0xFFu, c1 = b2 >> 8;
-        if ((c0 & 0x7Fu) == 0x7Fu || (c1 & 0x7Fu) == 0x7Fu) return false;
-        // e4m3 * 2^14 so that (e2m1 * 2^-14) * it is the exact e2m1 * block-scale product
-        const float bs0 = e4m3_x2m8(c0) * 0x1p22f, bs1 = e4m3_x2m8(c1) * 0x1p22f;
+    static constexpr uint32_t CE = 8, IB = 4, LG = 4, CH = stk::kWordsFp4;
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
+    // 8 elements: (e2m1 * block scale) is exact in fp32, then one RNE multiply by g
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, u32x4* o) {
+        const uint32_t code = ld_u8(c.blob + c.D.scale + (e >> 4));  // block scale of these 8 elements
+        if (!finite(c.s) || (code & 0x7Fu) == 0x7Fu) return false;
+        const float bs = fp8x2<false>(code).x;
         const float g = c.s;
-        const uint32_t w[4] = {in[0].x, in[0].y, in[0].z, in[0].w};
-        uint32_t r[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float bs = k < 2 ? bs0 : bs1;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t byte = (w[k] >> (8 * p)) & 0xFFu;
-                const float t0 = e2m1_x2m14(byte & 15u) * bs, t1 = e2m1_x2m14(byte >> 4) * bs;
-                r[4 * k + p] = pack_bf16(t0 * g, t1 * g);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = u32x4{r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]};
+        const uint32_t x = in[0];
+        const f32x2 p0 = fp4x2<0>(x), p1 = fp4x2<1>(x), p2 = fp4x2<2>(x), p3 = fp4x2<3>(x);
+        o[0] = u32x4{cvt_bf16x2((p0.x * bs) * g, (p0.y * bs) * g), cvt_bf16x2((p1.x * bs) * g, (p1.y * bs) * g),
+                     cvt_bf16x2((p2.x * bs) * g, (p2.y * bs) * g), cvt_bf16x2((p3.x * bs) * g, (p3.y * bs) * g)};
         return true;
     }
 };
 
-// Output u32x4 words one chunk writes.
-template <class K>
-constexpr uint32_t out_words() { return K::CH * 2 / 16; }
+// ------------------------------------------------------------------------- aligned loads
 
-// Source byte offset of element e (relative to the tensor start).
-template <class K>
-__device__ __forceinline__ uint64_t src_off(uint64_t e) {
-    return std::is_same<K, KFp4>::value ? (e >> 1) : (e << K::SRC_SHIFT);
+template <uint32_t LG>
+__device__ __forceinline__ void ld_word(const uint8_t* p, uint32_t* d) {
+    if constexpr (LG == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else if constexpr (LG == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        d[0] = v.x; d[1] = v.y;
+    } else {
+        d[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
 }
 
-// One unit [e0, e0 + cnt) of kind K with source misalignment r = 4 * Q + sh (ALIGNED: r == 0).
-template <class K, int Q, bool ALIGNED>
-__device__ void run_unit(const UnitCtx& c, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
-    constexpr uint32_t NW = K::IN / 16;                // aligned source words a chunk needs
-    constexpr uint32_t LW = NW + (ALIGNED ? 0 : 1);    // words loaded per chunk
-    constexpr uint32_t OW = out_words<K>();
-    constexpr uint32_t STEP = stk::kWave * K::STEPS;   // chunks per wave step
-    const uint8_t* src = c.blob + c.D.src + src_off<K>(e0);
+// One step of a unit: chunks c = cbase + j*64 + lane (j < CH) of the unit whose first element is
+// e0; nch = whole chunks in the unit.  Source misalignment r = 4*Q + sh within an LG-byte word
+// (ALIGNED: r == 0).  Every load is issued before any decode.  Returns a mask of this lane's
+// chunks (bit j) that must take the exact path.
+template <class K, uint32_t Q, bool ALIGNED>
+__device__ __forceinline__ uint32_t step(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cbase,
+                                         uint32_t nch, uint32_t sh, uint32_t lane) {
+    constexpr uint32_t NW = K::IB / K::LG;           // aligned words one chunk needs
+    constexpr uint32_t LWN = NW + (ALIGNED ? 0 : 1);  // words loaded per chunk
+    constexpr uint32_t DW = K::LG / 4;               // dwords per loaded word
+    constexpr uint32_t OW = K::CE / stk::kWordElems; // output words per chunk
+    const uint8_t* src = c.blob + c.D.src + K::src_off(e0);
     const uint8_t* base = src - (ALIGNED ? 0 : (Q * 4 + sh));
-    uint16_t* out = c.out + e0;
-    const uint32_t nch = cnt / K::CH;
-    for (uint32_t j0 = 0; j0 < nch; j0 += STEP) {
-        u32x4 raw[K::STEPS][LW];
-        bool live[K::STEPS];
+    uint32_t raw[K::CH][LWN * DW];
+    bool live[K::CH];
 #pragma unroll
-        for (uint32_t s = 0; s < K::STEPS; ++s) {
-            const uint32_t j = j0 + s * stk::kWave + lane;
-            live[s] = j < nch;
-            if (live[s]) {
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        const uint32_t ci = cbase + j * stk::kWave + lane;
+        live[j] = ci < nch;
+        if (live[j]) {
 #pragma unroll
-                for (uint32_t w = 0; w < LW; ++w) raw[s][w] = ld16(base + size_t(j) * K::IN + 16 * w);
-            }
-        }
-#pragma unroll
-        for (uint32_t s = 0; s < K::STEPS; ++s) {
-            const uint32_t j = j0 + s * stk::kWave + lane;
-            if (!live[s]) continue;
-            u32x4 in[NW];
-#pragma unroll
-            for (uint32_t w = 0; w < NW; ++w) in[w] = ALIGNED ? raw[s][w] : funnel<Q>(raw[s][w], raw[s][w + 1], sh);
-            u32x4 o[OW];
-            const uint64_t e = e0 + uint64_t(j) * K::CH;
-            if (!c.exact_all && K::fast(c, in, e, j, o)) {
-#pragma unroll
-                for (uint32_t w = 0; w < OW; ++w) st16(out + size_t(j) * K::CH + 8 * w, o[w]);
-            } else {
-                chunk_exact(c.blob, c.D, c.out, e, K::CH);
-            }
+            for (uint32_t k = 0; k < LWN; ++k) ld_word<K::LG>(base + size_t(ci) * K::IB + k * K::LG, &raw[j][k * DW]);
         }
     }
-    // elements past the last whole chunk (only in a tensor's final unit)
-    for (uint32_t t = nch * K::CH + lane; t < cnt; t += stk::kWave)
-        c.out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
+    if (!out_ok(c)) return 0;
+    const bool vec = out_fast(c);
+    uint32_t fail = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        if (!live[j]) continue;
+        const uint32_t ci = cbase + j * stk::kWave + lane;
+        uint32_t in[K::IB / 4];
+#pragma unroll
+        for (uint32_t k = 0; k < K::IB / 4; ++k)
+            in[k] = ALIGNED ? raw[j][k] : __builtin_amdgcn_alignbyte(raw[j][Q + k + 1], raw[j][Q + k], sh);
+        const uint64_t e = e0 + uint64_t(ci) * K::CE;
+        u32x4 v[OW];
+        if (vec && K::fast(c, in, e, v)) {
+#pragma unroll
+            for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
+        } else {
+            fail |= 1u << j;
+        }
+    }
+    return fail;
 }
 
 template <class K>
-__device__ __forceinline__ void dispatch_align(const UnitCtx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
-    const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + src_off<K>(e0)) & 15u);
+__device__ __forceinline__ uint32_t step_any(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cbase,
+                                             uint32_t nch, uint32_t lane) {
+    const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)) & (K::LG - 1));
     const uint32_t sh = r & 3u;
-    switch (r == 0 ? 4 : int(r >> 2)) {
-        case 4: run_unit<K, 0, true>(c, e0, cnt, sh, lane); break;
-        case 0: run_unit<K, 0, false>(c, e0, cnt, sh, lane); break;
-        case 1: run_unit<K, 1, false>(c, e0, cnt, sh, lane); break;
-        case 2: run_unit<K, 2, false>(c, e0, cnt, sh, lane); break;
-        default: run_unit<K, 3, false>(c, e0, cnt, sh, lane); break;
+    if (r == 0) return step<K, 0, true>(c, out, e0, cbase, nch, sh, lane);
+    switch (r >> 2) {
+        case 0: return step<K, 0, false>(c, out, e0, cbase, nch, sh, lane);
+        case 1: if constexpr (K::LG > 4) return step<K, 1, false>(c, out, e0, cbase, nch, sh, lane);
+                [[fallthrough]];
+        case 2: if constexpr (K::LG > 8) return step<K, 2, false>(c, out, e0, cbase, nch, sh, lane);
+                [[fallthrough]];
+        default: if constexpr (K::LG > 8) return step<K, 3, false>(c, out, e0, cbase, nch, sh, lane);
+                 return 0;
     }
 }
 
-__device__ __forceinline__ uint64_t units_of(const Desc& D) {
-    return (D.numel + (uint64_t(1) << D.unit_shift) - 1) >> D.unit_shift;
+template <class K>
+__device__ __forceinline__ void run_unit(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
+                                         uint32_t lane) {
+    const uint32_t nch = cnt / K::CE;  // whole chunks in this unit
+    for (uint32_t cbase = 0; cbase < nch; cbase += K::CH * stk::kWave) {
+        uint32_t fail = step_any<K>(c, out, e0, cbase, nch, lane);
+        while (fail) {  // rare: NaN inputs, special scales, misaligned outputs
+            const uint32_t j = __builtin_ctz(fail);
+            fail &= fail - 1;
+            const uint64_t e = e0 + uint64_t(cbase + j * stk::kWave + lane) * K::CE;
+            for (uint32_t k = 0; k < K::CE; ++k) out[e + k] = uint16_t(elem_exact(c.blob, c.D, e + k));
+        }
+    }
+    // elements past the last whole chunk (only in an output's final unit)
+    if (!out_ok(c)) return;
+    for (uint32_t t = nch * K::CE + lane; t < cnt; t += stk::kWave)
+        out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
 }
+
+// ------------------------------------------------------------------------- the kernel
 
 __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __restrict__ blob,
-                                                             const st_desc* __restrict__ descs, uint32_t n,
-                                                             uint16_t* const* __restrict__ outs) {
+                                                             const uint8_t* __restrict__ table, uint64_t units,
+                                                             uint32_t groups, uint16_t* const* __restrict__ outs) {
+    // XCD-contiguous renumbering: workgroup b runs on XCD b % 8; XCD x gets the contiguous range
+    // of groups [start_x, start_x + count_x), a bijection of [0, groups).
+    const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
+    if (b >= groups) return;
+    const uint32_t q = groups / 8, rem = groups % 8, x = b % 8;
+    const uint32_t grp = x * q + (x < rem ? x : rem) + b / 8;
     const uint32_t lane = threadIdx.x & (stk::kWave - 1);
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-    const Desc last = load_desc(descs, n - 1);
-    const uint64_t total = last.unit_begin + units_of(last);
+    const uint64_t unit = uint64_t(grp) * ST_UNITS_PER_GROUP + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= units) return;
 
-    uint32_t d = 0;
-    Desc D = load_desc(descs, 0);
-    uint64_t next_begin = n > 1 ? descs[1].unit_begin : total;
-    for (uint64_t u = wave; u < total; u += nwaves) {
-        if (u >= next_begin) {
-            // last descriptor in (d, n) whose unit_begin <= u (empty outputs share a unit_begin
-            // with their successor and are skipped by taking the last match)
-            uint32_t lo = d + 1, hi = n - 1;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi + 1) >> 1;
-                if (descs[mid].unit_begin <= u) lo = mid;
-                else hi = mid - 1;
-            }
-            d = lo;
-            D = load_desc(descs, d);
-            next_begin = d + 1 < n ? descs[d + 1].unit_begin : total;
-        }
-        const uint64_t e0 = (u - D.unit_begin) << D.unit_shift;
-        const uint64_t left = D.numel - e0;
-        const uint32_t cnt = uint32_t(left < (uint64_t(1) << D.unit_shift) ? left : (uint64_t(1) << D.unit_shift));
-        UnitCtx c;
-        c.blob = blob;
-        c.D = D;
-        c.out = outs[D.out];
-        c.s = 0.0f;
-        c.exact_all = (reinterpret_cast<uintptr_t>(c.out) & 15u) != 0;
-        if ((reinterpret_cast<uintptr_t>(c.out) & 1u) != 0) continue;  // not a bf16 address: nothing is written
-        switch (D.kind) {
-            case ST_KIND_PASS_BF16: dispatch_align<KPass>(c, e0, cnt, lane); break;
-            case ST_KIND_CAST_F16: dispatch_align<KF16>(c, e0, cnt, lane); break;
-            case ST_KIND_CAST_F32: dispatch_align<KF32>(c, e0, cnt, lane); break;
-            case ST_KIND_FP8_TENSOR: {
-                const float s = as_f32(ld_u32_any(blob + D.scale));
-                c.exact_all |= !foldable(s);
-                c.s = s * 256.0f;
-                dispatch_align<KFp8Tensor>(c, e0, cnt, lane);
-                break;
-            }
-            case ST_KIND_FP8_BLOCK128:
-                c.exact_all |= (D.cols & 15u) != 0;
-                dispatch_align<KFp8Block>(c, e0, cnt, lane);
-                break;
-            default: {
-                const float g = as_f32(ld_u32_any(blob + D.scale2));
-                c.exact_all |= !(__builtin_fabsf(g) <= 3.4028234663852886e38f);  // NaN or infinite
-                c.s = g;
-                dispatch_align<KFp4>(c, e0, cnt, lane);
-                break;
-            }
-        }
+    // The map sits at a fixed offset and the descriptors right after it, so the header (magic
+    // and unit count, one scalar load), the map entry and the descriptor are the only loads ahead
+    // of the data.  A table that does not match n is left alone before anything indexes it.
+    const u32x4 hw = ld_uniform<u32x4>(table);
+    if ((hw.x != ST_TABLE_MAGIC) | (((uint64_t(hw.w) << 32) | hw.z) != units)) return;
+    const uint32_t* map = reinterpret_cast<const uint32_t*>(table + sizeof(st_table_header));
+    const st_desc* descs = reinterpret_cast<const st_desc*>(table + stk::table_desc_offset(groups));
+    uint32_t d = ld_uniform<uint32_t>(map + grp);
+    Desc D = load_desc(descs + d);
+    while (unit >= D.unit_begin + units_of(D)) D = load_desc(descs + (++d));
+
+    const uint64_t e0 = (unit - D.unit_begin) << D.unit_shift;
+    const uint64_t left = D.numel - e0;
+    const uint32_t cnt = uint32_t(left < (uint64_t(1) << D.unit_shift) ? left : (uint64_t(1) << D.unit_shift));
+    uint16_t* out = ld_uniform<uint16_t*>(outs + D.out);
+
+    Ctx c;
+    c.blob = blob;
+    c.D = D;
+    c.scale_al = (D.scale & 3u) == 0;
+    c.out = reinterpret_cast<uintptr_t>(out);
+    c.s = D.kind == ST_KIND_FP8_TENSOR ? ld_scalar_f32(blob + D.scale)
+        : D.kind == ST_KIND_NVFP4      ? ld_scalar_f32(blob + D.scale2)
+                                       : 0.0f;
+    switch (D.kind) {
+        case ST_KIND_PASS_BF16: run_unit<KPass>(c, out, e0, cnt, lane); break;
+        case ST_KIND_CAST_F16: run_unit<KF16>(c, out, e0, cnt, lane); break;
+        case ST_KIND_CAST_F32: run_unit<KF32>(c, out, e0, cnt, lane); break;
+        case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor>(c, out, e0, cnt, lane); break;
+        case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block>(c, out, e0, cnt, lane); break;
+        default: run_unit<KFp4>(c, out, e0, cnt, lane); break;
     }
 }
-
-uint32_t g_default_grid[64];
 
 }  // namespace
 
-extern "C" uint32_t st_default_grid(void) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (g_default_grid[dev]) return g_default_grid[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, materialize_kernel, kBlock, 0) != hipSuccess || per_cu <= 0)
-        per_cu = 1;
-    g_default_grid[dev] = uint32_t(cus) * uint32_t(per_cu);
-    return g_default_grid[dev];
-}
-
-extern "C" st_status st_materialize_grid(const void* blob, const void* descs, size_t n, void* const* outs, uint32_t grid,
-                                         void* stream) {
+extern "C" st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {
     if (n == 0) return ST_OK;
     if (!blob || !descs || !outs) return st_fail(ST_E_ARG, "st_materialize: null pointer");
-    if (n >= (size_t(1) << 32)) return st_fail(ST_E_ARG, "st_materialize: %zu descriptors (at most 2^32 - 1)", n);
     if (reinterpret_cast<uintptr_t>(blob) % ST_BLOB_ALIGN)
         return st_fail(ST_E_ARG, "st_materialize: blob is not %d-byte aligned", ST_BLOB_ALIGN);
-    if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "st_materialize: descriptor table is not 64-byte aligned");
-    if (grid == 0) grid = st_default_grid();
-    if (grid == 0) return st_fail(ST_E_HIP, "st_materialize: no usable HIP device");
-    hipLaunchKernelGGL(materialize_kernel, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint8_t*>(blob), static_cast<const st_desc*>(descs), uint32_t(n),
-                       reinterpret_cast<uint16_t* const*>(outs));
+    if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "st_materialize: work table is not 64-byte aligned");
+    const uint64_t groups = (uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
+    if (groups >= (uint64_t(1) << 31)) return st_fail(ST_E_ARG, "st_materialize: %zu work units is too many", n);
+    const uint32_t gx = uint32_t(groups < kMaxGridX ? groups : kMaxGridX);
+    const uint32_t gy = uint32_t((groups + gx - 1) / gx);
+    hipLaunchKernelGGL(materialize_kernel, dim3(gx, gy), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t*>(blob), static_cast<const uint8_t*>(descs), uint64_t(n),
+                       uint32_t(groups), reinterpret_cast<uint16_t* const*>(outs));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return st_fail(ST_E_HIP, "st_materialize: launch failed: %s", hipGetErrorString(e));
     return ST_OK;
-}
-
-extern "C" st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {
-    return st_materialize_grid(blob, descs, n, outs, 0, stream);
 }

@@ -10,28 +10,32 @@ static_assert(sizeof(st_desc) == 64, "st_desc must stay 64 bytes");
 // Records a printf-style message for st_last_error() on this thread and returns `code`.
 st_status st_fail(st_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// Elements one lane handles per chunk, and chunks per lane in one wave step.  A wave step is
-// the smallest work unit; its size is chosen so every unit moves roughly 10-16 KB of HBM traffic
-// whatever its kind, which keeps the static, interleaved unit schedule balanced.
-//   bf16/fp16 : 8 elements = 16 B in, 16 B out per chunk, 8 chunks -> 4096 elements (16 KB)
-//   fp32      : 8 elements = 32 B in, 16 B out per chunk, 4 chunks -> 2048 elements (12 KB)
-//   fp8       : 16 elements = 16 B in, 32 B out per chunk, 4 chunks -> 4096 elements (12 KB)
-//   nvfp4     : 32 elements = 16 B + 2 B in, 64 B out per chunk, 2 chunks -> 4096 (10.25 KB)
+// Work-unit geometry.  Every lane of a wavefront writes whole 16-byte output words (8 bf16
+// elements); output word o*64 + lane of a unit belongs to lane `lane`, so each store instruction
+// of the wavefront covers 1 KB of contiguous output.  kWords = output words per lane per unit:
+//   bf16/fp16 : 2 words -> 1024 elements (2 KB in, 2 KB out)
+//   fp32      : 1 word  ->  512 elements (2 KB in, 1 KB out)
+//   fp8       : 2 words -> 1024 elements (1 KB in, 2 KB out)
+//   nvfp4     : 4 words -> 2048 elements (1 KB + 128 B in, 4 KB out)
+// so every unit reads about 1-2 KB and writes 1-4 KB: one short, fully coalesced burst per wave.
 namespace stk {
 constexpr uint32_t kWave = 64;
-constexpr uint32_t kChunkPass = 8, kStepsPass = 8;
-constexpr uint32_t kChunkF32 = 8, kStepsF32 = 4;
-constexpr uint32_t kChunkFp8 = 16, kStepsFp8 = 4;
-constexpr uint32_t kChunkFp4 = 32, kStepsFp4 = 2;
+constexpr uint32_t kWordElems = 8;
+constexpr uint32_t kWordsPass = 2, kWordsF32 = 1, kWordsFp8 = 2, kWordsFp4 = 4;
 
 constexpr uint32_t ilog2(uint32_t x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 
-constexpr uint32_t step_shift(uint32_t kind) {
-    return kind == ST_KIND_PASS_BF16 || kind == ST_KIND_CAST_F16 ? ilog2(kWave * kChunkPass * kStepsPass)
-         : kind == ST_KIND_CAST_F32                              ? ilog2(kWave * kChunkF32 * kStepsF32)
-         : kind == ST_KIND_NVFP4                                 ? ilog2(kWave * kChunkFp4 * kStepsFp4)
-                                                                 : ilog2(kWave * kChunkFp8 * kStepsFp8);
+constexpr uint32_t words_per_lane(uint32_t kind) {
+    return kind == ST_KIND_PASS_BF16 || kind == ST_KIND_CAST_F16 ? kWordsPass
+         : kind == ST_KIND_CAST_F32                              ? kWordsF32
+         : kind == ST_KIND_NVFP4                                 ? kWordsFp4
+                                                                 : kWordsFp8;
 }
+// Where the descriptors start in a work table of `groups` map entries.
+constexpr uint64_t table_desc_offset(uint64_t groups) { return 64 + (groups * 4 + 63) / 64 * 64; }
+
+// log2 of the default unit size (elements) of a kind
+constexpr uint32_t step_shift(uint32_t kind) { return ilog2(kWave * kWordElems * words_per_lane(kind)); }
 
 // Exact unsigned 32-bit division by an invariant divisor d >= 1 (Granlund & Montgomery,
 // "Division by Invariant Integers using Multiplication", 1994, the round-up method with an

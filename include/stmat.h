@@ -15,7 +15,7 @@
  *
  *   st_index_build / st_index_open   header bytes -> index (host, metadata only)
  *   st_stage_file                    file byte ranges -> pinned ring -> device blob (side stream)
- *   st_materialize                   device blob + descriptor table -> bf16 outputs (one launch)
+ *   st_materialize                   device blob + work table -> bf16 outputs (one launch)
  *
  * Output element values (bit-exact definition; rounding is IEEE binary32 round-to-nearest-even
  * for every multiply, then round-to-nearest-even to bfloat16; any NaN result is 0x7FC0;
@@ -97,8 +97,33 @@ typedef struct st_output_info {
     int64_t scale2;          /* header-entry index of the NVFP4 global scale, or -1 */
 } st_output_info;
 
-/* Device descriptor: one per output, 64 bytes, built on the host, uploaded by the caller.
- * Offsets are bytes from the start of the blob (= the file's data section). */
+/* The device work table, built on the host by the library and uploaded by the caller as one
+ * block of device memory (64-byte aligned):
+ *
+ *   st_table_header                      64 bytes
+ *   uint32_t map[groups]                 at offset 64: for every group of 4 consecutive work units
+ *                                        (groups = ceil(units / 4)), the descriptor that holds the
+ *                                        group's first unit; padded to a multiple of 64 bytes
+ *   st_desc[n_desc]                      one 64-byte descriptor per output, at desc_offset =
+ *                                        64 + round_up(4 * groups, 64)
+ *
+ * A work unit is 2^unit_shift consecutive output elements of one output; an output of numel
+ * elements has ceil(numel / 2^unit_shift) units, numbered in output order from unit_begin.
+ * The kernel runs one 64-lane wavefront per unit and one 4-wave workgroup per map entry.
+ * Offsets in descriptors are bytes from the start of the blob (= the file's data section). */
+#define ST_TABLE_MAGIC 0x324D5453u   /* "STM2" */
+#define ST_UNITS_PER_GROUP 4
+
+typedef struct st_table_header {
+    uint32_t magic;          /* ST_TABLE_MAGIC */
+    uint32_t n_desc;         /* descriptors */
+    uint64_t units;          /* work units */
+    uint64_t desc_offset;    /* bytes from the table start to st_desc[0] */
+    uint64_t map_offset;     /* bytes from the table start to map[0] (always 64) */
+    uint64_t bytes;          /* size of the whole table */
+    uint64_t reserved[3];
+} st_table_header;           /* 64 bytes */
+
 typedef struct st_desc {
     uint64_t src;            /* weight bytes */
     uint64_t scale;          /* FP8_TENSOR fp32 scale / FP8_BLOCK128 fp32 grid / NVFP4 e4m3 block scales */
@@ -109,16 +134,14 @@ typedef struct st_desc {
     uint32_t cols;           /* FP8_BLOCK128: N, NVFP4: K, otherwise 0 */
     uint32_t grid_cols;      /* FP8_BLOCK128: ceil(N / 128) */
     uint32_t div_magic;      /* FP8_BLOCK128: multiplier of the exact division by N */
-    uint8_t kind;            /* st_kind */
-    uint8_t unit_shift;      /* a work unit is 2^unit_shift output elements */
-    uint8_t div_shift;       /* FP8_BLOCK128: shift of the exact division by N */
-    uint8_t reserved0;
-    uint32_t reserved1;
+    uint32_t meta;           /* st_kind | unit_shift << 8 | div_shift << 16 (a unit is
+                                2^unit_shift elements; div_shift goes with div_magic) */
+    uint32_t reserved;
 } st_desc;                   /* 64 bytes */
 
 /* Planning options; pass NULL for the defaults. */
 typedef struct st_plan_opts {
-    uint32_t unit_log2_scale;  /* work unit = (kind's wave step) << this; 0..6, default 0 */
+    uint32_t unit_log2_scale;  /* work unit = (kind's default unit) << this; 0..6, default 0 */
     uint32_t flags;            /* reserved, must be 0 */
 } st_plan_opts;
 
@@ -166,20 +189,21 @@ uint64_t st_index_output_arena_bytes(const st_index* idx);
 /* Bytes read + bytes written by materialising every output (the data section plus 2 bytes
  * per output element). */
 uint64_t st_index_traffic_bytes(const st_index* idx);
-/* Device memory the whole load needs: blob + descriptor table + pointer array + arena.
+/* Device memory the whole load needs: blob + work table + pointer array + arena.
  * Compare with the free device memory before allocating; the requirement is arithmetic. */
 uint64_t st_index_device_bytes(const st_index* idx);
 
-/* The full descriptor table (one st_desc per output, in output order, out = k), host memory
- * owned by the index.  *n = descriptors, *bytes = n * sizeof(st_desc), *total_units = work
- * units in the table (any of the three pointers may be NULL). */
-const st_desc* st_index_descs(const st_index* idx, size_t* n, size_t* bytes, uint64_t* total_units);
+/* The work table for every output (descriptor k writes outs[k]), host memory owned by the
+ * index.  *bytes = table size, *units = work units (the `n` st_materialize takes); either
+ * pointer may be NULL. */
+const void* st_index_table(const st_index* idx, size_t* bytes, uint64_t* units);
 
-/* A self-contained table for a subset of outputs: sel[0..k) are output indices (any order,
- * no repeats needed); descriptor j gets out = j, so outs[j] must point to output sel[j].
- * dst must hold k * sizeof(st_desc) bytes.  Used for on-demand loads of single tensors. */
-st_status st_index_descs_subset(const st_index* idx, const uint32_t* sel, size_t k,
-                                st_desc* dst, size_t dst_bytes, uint64_t* total_units);
+/* A self-contained work table for a subset of outputs: sel[0..k) are output indices (any
+ * order; repeats allowed); descriptor j writes outs[j], so outs[j] must point to output sel[j].
+ * With dst == NULL only *bytes and *units are set (a size query); otherwise dst_bytes must be
+ * at least that size.  Used for on-demand loads of single tensors. */
+st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t k, void* dst,
+                                size_t dst_bytes, size_t* bytes, uint64_t* units);
 
 /* Stage the data section of the file at `path` into `blob_dev` (device memory of at least
  * st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned).  Reads the file in chunks into the
@@ -195,22 +219,18 @@ st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, v
 
 /* Enqueue the grouped materialise kernel on `stream` (hipStream_t; NULL = default stream).
  *   blob   device copy of the data section (st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned)
- *   descs  device copy of n st_desc (from st_index_descs or st_index_descs_subset)
+ *   descs  device copy of a work table (st_index_table / st_index_table_subset), 64-byte aligned
+ *   n      the table's work-unit count (returned with the table); the launch is one 64-lane
+ *          wavefront per unit, so n decides the grid.  A value that disagrees with the table's
+ *          header makes every wavefront return without writing.
  *   outs   device array of bf16 output pointers, each ST_OUT_ALIGN-aligned and large enough
- *          for its output's numel elements; descriptor d writes outs[descs[d].out]
- * One persistent launch covers every descriptor.  Only enqueues: it never allocates, copies or
+ *          for its output's numel elements; descriptor d writes outs[desc[d].out]
+ * One launch covers every descriptor.  Only enqueues: it never allocates, copies or
  * synchronises; kernel faults surface at the caller's next synchronisation.  Returns ST_E_ARG
- * for null pointers (n > 0) and ST_E_HIP if the launch fails.  n == 0 is a no-op. */
+ * for null pointers or misaligned blob/table (n > 0) and ST_E_HIP if the launch fails.
+ * n == 0 is a no-op. */
 st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs,
                          void* stream);
-
-/* st_materialize with an explicit number of workgroups (0 = the library's persistent default,
- * a multiple of the device's compute units).  Workgroups beyond the table's work exit at once. */
-st_status st_materialize_grid(const void* blob, const void* descs, size_t n, void* const* outs,
-                              uint32_t grid, void* stream);
-
-/* The library's default persistent grid (workgroups of 256 threads) on the current device. */
-uint32_t st_default_grid(void);
 
 #ifdef __cplusplus
 }

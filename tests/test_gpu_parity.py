@@ -15,12 +15,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _gpu_outputs(buf: bytes, unit_log2_scale=0, grid=0):
+def _gpu_outputs(buf: bytes, unit_log2_scale=0):
     ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=unit_log2_scale)
     ck = st.DeviceCheckpoint(ix, None, DEV)
     ck.load_bytes(buf[ix.data_offset:])
     ck.arena.view(torch.int16).fill_(0x5A5A)     # poison: every element must be written
-    ck.materialize(grid=grid)
+    ck.materialize()
     torch.cuda.synchronize()
     return {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in ck.tensors.items()}, ck
 
@@ -45,9 +45,10 @@ def test_configs_small(k):
     assert_parity(synth.config_bytes(k, small=k != 1))
 
 
-@pytest.mark.parametrize("scale,grid", [(1, 0), (3, 0), (0, 1), (0, 7), (2, 3)])
-def test_unit_sizes_and_grids(scale, grid):
-    assert_parity(synth.config_bytes(3, small=True), unit_log2_scale=scale, grid=grid)
+@pytest.mark.parametrize("k", [1, 3, 4, 5])
+@pytest.mark.parametrize("scale", [1, 3, 6])
+def test_larger_work_units(k, scale):
+    assert_parity(synth.config_bytes(k, small=k != 1), unit_log2_scale=scale)
 
 
 def _pad(k):
@@ -127,7 +128,7 @@ def test_misaligned_output_pointers_take_the_exact_path():
     # a second arena, every output shifted by 2 bytes (bf16-aligned, not 16-byte aligned)
     arena = torch.empty(ix.arena_bytes // 2 + 8, dtype=torch.bfloat16, device=DEV)
     ptrs = torch.tensor([arena.data_ptr() + o.offset + 2 for o in outs], dtype=torch.int64).to(DEV)
-    st.materialize(ck.blob, ck.descs, ck.n, ptrs)
+    st.materialize(ck.blob, ck.table, ck.units, ptrs)
     torch.cuda.synchronize()
     want = oracle.materialize(buf)
     for o in outs:
@@ -143,15 +144,26 @@ def test_subset_table_writes_only_selected_outputs():
     ck.load_bytes(buf[ix.data_offset:])
     outs = ix.outputs()
     sel = [len(outs) - 1, 2, 0]
-    table, k, _ = ix.descs_subset(sel)
-    descs = torch.frombuffer(bytearray(table), dtype=torch.uint8).to(DEV)
+    raw, units = ix.table_subset(sel)
+    table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
     bufs = [torch.full((outs[s].numel,), -1, dtype=torch.int16, device=DEV) for s in sel]
     ptrs = torch.tensor([b.data_ptr() for b in bufs], dtype=torch.int64).to(DEV)
-    st.materialize(ck.blob, descs, k, ptrs)
+    st.materialize(ck.blob, table, units, ptrs)
     torch.cuda.synchronize()
     want = oracle.materialize(buf)
     for s, b in zip(sel, bufs):
         assert np.array_equal(b.cpu().numpy().view(np.uint16), want[outs[s].name].reshape(-1))
+
+
+def test_wrong_unit_count_writes_nothing():
+    buf = synth.config_bytes(1)
+    ix = st.SafeTensorIndex.from_bytes(buf)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    ck.load_bytes(buf[ix.data_offset:])
+    ck.arena.view(torch.int16).fill_(0x1234)
+    st.materialize(ck.blob, ck.table, ck.units - 1, ck.outs)
+    torch.cuda.synchronize()
+    assert bool((ck.arena.view(torch.int16) == 0x1234).all())
 
 
 def test_empty_outputs_and_empty_table():

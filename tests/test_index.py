@@ -59,25 +59,43 @@ def test_tiny_traffic_is_the_documented_figure():
     assert ix.data_size == 718_856 and ix.traffic_bytes == 718_856 + 913_408
 
 
-STEP_SHIFT = {"PASS_BF16": 12, "CAST_F16": 12, "CAST_F32": 11, "FP8_TENSOR": 12, "FP8_BLOCK128": 12, "NVFP4": 12}
+STEP_SHIFT = {"PASS_BF16": 10, "CAST_F16": 10, "CAST_F32": 9, "FP8_TENSOR": 10, "FP8_BLOCK128": 10, "NVFP4": 11}
+
+DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u8"),
+                 ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"), ("div_magic", "<u4"), ("kind", "u1"),
+                 ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1"), ("r1", "<u4")])  # meta, little-endian
+HEADER = np.dtype([("magic", "<u4"), ("n_desc", "<u4"), ("units", "<u8"), ("desc_offset", "<u8"),
+                   ("map_offset", "<u8"), ("bytes", "<u8"), ("reserved", "<u8", 3)])
 
 
-def _descs(table: bytes):
-    return np.frombuffer(table, dtype=np.dtype([(n, t) for n, t in [
-        ("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u8"),
-        ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"), ("div_magic", "<u4"), ("kind", "u1"),
-        ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1"), ("r1", "<u4")]]))
+def _table(raw: bytes):
+    h = np.frombuffer(raw, HEADER, count=1)[0]
+    assert h["magic"] == _lib.TABLE_MAGIC and h["bytes"] == len(raw) and len(raw) % 64 == 0
+    groups = -(-int(h["units"]) // _lib.UNITS_PER_GROUP)
+    assert h["map_offset"] == 64 and h["desc_offset"] == 64 + -(-groups * 4 // 64) * 64
+    d = np.frombuffer(raw, DESC, count=int(h["n_desc"]), offset=int(h["desc_offset"]))
+    m = np.frombuffer(raw, "<u4", count=groups, offset=int(h["map_offset"]))
+    return h, d, m
+
+
+def _check_map(d, m, units):
+    # every group of 4 units maps to the descriptor holding its first unit
+    ends = d["unit_begin"].astype(np.int64) + (-(-d["numel"].astype(np.int64) // (1 << d["unit_shift"].astype(np.int64))))
+    for g, di in enumerate(m):
+        u = g * _lib.UNITS_PER_GROUP
+        assert d[di]["unit_begin"] <= u < ends[di], (g, di)
+    assert ends.max(initial=0) == units
 
 
 @pytest.mark.parametrize("scale", [0, 2])
-def test_descriptor_table_invariants(scale):
+def test_table_invariants(scale):
     buf = synth.config_bytes(3, small=True)
     ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=scale)
-    table, n, units = ix.descs()
-    d = _descs(table)
+    raw, units = ix.table()
+    h, d, m = _table(raw)
     outs = ix.outputs()
     ents = ix.tensors()
-    assert n == len(outs) == len(d)
+    assert h["units"] == units and h["n_desc"] == len(outs) == len(d)
     pos = 0
     for k, (row, o) in enumerate(zip(d, outs)):
         assert row["out"] == k and row["numel"] == o.numel and _lib.KINDS[row["kind"]] == o.kind
@@ -92,13 +110,26 @@ def test_descriptor_table_invariants(scale):
         if o.kind == "FP8_BLOCK128":
             assert row["cols"] == o.shape[1] and row["grid_cols"] == -(-o.shape[1] // 128)
     assert pos == units
+    _check_map(d, m, units)
     # arena: 256-byte aligned, disjoint, in order
     offs = [o.offset for o in outs]
     assert all(x % 256 == 0 for x in offs)
     assert all(offs[i] + 2 * outs[i].numel <= offs[i + 1] for i in range(len(offs) - 1))
     assert ix.arena_bytes >= offs[-1] + 2 * outs[-1].numel
     assert ix.blob_bytes % 256 == 0 and ix.blob_bytes >= ix.data_size
-    assert ix.device_bytes >= ix.blob_bytes + ix.arena_bytes + 64 * n
+    assert ix.device_bytes >= ix.blob_bytes + ix.arena_bytes + len(raw)
+
+
+def test_map_with_empty_and_tiny_outputs():
+    f = make_file([("e", "BF16", (0,), b""), ("a", "F32", (3,), f32_bytes(1, 2, 3)), ("z", "F16", (0, 7), b""),
+                   ("b", "BF16", (2000,), b"\0" * 4000), ("c", "BF16", (1,), b"\0\0"), ("y", "BF16", (0,), b"")])
+    raw, units = st.SafeTensorIndex.from_bytes(f).table()
+    h, d, m = _table(raw)
+    assert units == 1 + 2 + 1
+    _check_map(d, m, units)
+    raw, units = st.SafeTensorIndex.from_bytes(make_file([])).table()
+    h, d, m = _table(raw)
+    assert units == 0 and len(d) == 0 and len(m) == 0
 
 
 @pytest.mark.parametrize("cols", [1, 2, 3, 7, 100, 127, 128, 129, 200, 300, 4096, 12288, 65535, 999983, 2 ** 31 - 1,
@@ -110,7 +141,7 @@ def test_block_division_constants_give_exact_quotients(cols):
            '"w.weight_scale_inv":{"dtype":"F32","shape":[%d,%d],"data_offsets":[0,0]}}')
     # a zero-row weight keeps the file empty while the planner still derives the constants
     f = raw_header_file(hdr % (0, cols, 0, -(-cols // 128)))
-    d = _descs(_index(f).descs()[0])[0]
+    d = _table(_index(f).table()[0])[1][0]
     m, l = int(d["div_magic"]), int(d["div_shift"])
     rng = np.random.default_rng(cols)
     ns = [0, 1, cols - 1, cols, cols + 1, 2 ** 32 - 1, 2 ** 32 - 2, (2 ** 32 - 1) // cols * cols,
@@ -125,19 +156,20 @@ def test_block_division_constants_give_exact_quotients(cols):
 def test_subset_table_is_self_contained():
     buf = synth.config_bytes(5, small=True)
     ix = _index(buf)
-    full = _descs(ix.descs()[0])
+    full = _table(ix.table()[0])[1]
     sel = [7, 3, 100, 3]
-    table, k, units = ix.descs_subset(sel)
-    d = _descs(table)
-    assert k == 4
+    raw, units = ix.table_subset(sel)
+    h, d, m = _table(raw)
+    assert h["n_desc"] == 4
     pos = 0
     for j, s in enumerate(sel):
         assert d[j]["out"] == j and d[j]["src"] == full[s]["src"] and d[j]["numel"] == full[s]["numel"]
         assert d[j]["unit_begin"] == pos
         pos += -(-int(d[j]["numel"]) // (1 << int(d[j]["unit_shift"])))
     assert units == pos
+    _check_map(d, m, units)
     with pytest.raises(st.StError):
-        ix.descs_subset([10 ** 6])
+        ix.table_subset([10 ** 6])
 
 
 @pytest.mark.parametrize("case", sorted(BAD))
