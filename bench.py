@@ -51,12 +51,17 @@ def parse():
     ap.add_argument("--unit-scale", type=int, default=0)
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (a known-size kernel that scales profiler byte counters)")
+    ap.add_argument("--aligned-variant", action="store_true",
+                    help="also time the scaled-FP8 checkpoint with every scale moved to the end (all weights 16-byte aligned)")
     return ap.parse_args()
 
 
-def gen(k, d):
+def gen(k, d, overrides=None):
     import synth
-    path = os.path.join(d, f"synthetic_c{k}.safetensors")
+    overrides = overrides or {}
+    path = os.path.join(d, f"synthetic_c{k}{'_' + '_'.join(overrides) if overrides else ''}.safetensors")
     t0 = time.perf_counter()
     last = [t0]
 
@@ -66,7 +71,7 @@ def gen(k, d):
             last[0] = now
             log(f"[bench] generating config {k}: {done}/{total} tensor groups, {now - t0:.0f}s")
 
-    synth.write_config(k, path, progress=progress)
+    synth.write_config(k, path, progress=progress, **overrides)
     dt = time.perf_counter() - t0
     log(f"[bench] generated config {k}: {os.path.getsize(path) / 1e9:.3f} GB in {dt:.1f}s")
     return path, dt
@@ -118,10 +123,10 @@ def cpu_baseline(path, budget_s):
                       f"decoded by the single-threaded NumPy oracle in {dt:.1f}s"}
 
 
-def measure(k, d, args, rng):
+def measure(k, d, args, rng, overrides=None):
     import torch
     import device_checkpoint_dequantisation_amd as st
-    path, gen_s = gen(k, d)
+    path, gen_s = gen(k, d, overrides)
     t0 = time.perf_counter()
     ix = st.SafeTensorIndex.open(path, args.unit_scale)
     index_ms = (time.perf_counter() - t0) * 1e3
@@ -188,6 +193,20 @@ def main():
             log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
         if not args.keep:
             os.remove(results[k]["path"])
+    aligned = None
+    if args.aligned_variant:
+        aligned = measure(2, d, args, rng, {"scales_last": True})
+        if not args.keep:
+            os.remove(aligned["path"])
+    if args.copy_calibration:
+        import torch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)   # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del a, b
     r = results[args.config]
     line = {
         "metric": METRIC, "value": round(r["GBps"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -202,6 +221,10 @@ def main():
                       "min": round(r["kernel_ms_min"], 4)},
         "staging": r["stage"], "index_build_ms": round(r["index_ms"], 2), "parity": r["parity"],
     }
+    if aligned is not None:
+        line["scaled_fp8_all_weights_16B_aligned"] = {"GBps": round(aligned["GBps"], 2),
+                                                      "kernel_ms_mean": round(aligned["kernel_ms_mean"], 4),
+                                                      "parity": aligned["parity"]}
     if args.all:
         line["formats"] = {
             f"c{k}": {"GBps": round(v["GBps"], 2), "hbm_peak_frac": round(v["GBps"] / HBM_PEAK_GBPS, 4),

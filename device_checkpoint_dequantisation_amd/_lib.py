@@ -28,8 +28,8 @@ class OutputInfo(C.Structure):
 
 class Desc(C.Structure):
     _fields_ = [("src", C.c_uint64), ("scale", C.c_uint64), ("scale2", C.c_uint64), ("numel", C.c_uint64),
-                ("unit_begin", C.c_uint64), ("out", C.c_uint32), ("cols", C.c_uint32), ("grid_cols", C.c_uint32),
-                ("div_magic", C.c_uint32), ("meta", C.c_uint32), ("reserved", C.c_uint32)]
+                ("unit_begin", C.c_uint32), ("unit_end", C.c_uint32), ("tail", C.c_uint32), ("out", C.c_uint32),
+                ("cols", C.c_uint32), ("grid_cols", C.c_uint32), ("div_magic", C.c_uint32), ("meta", C.c_uint32)]
 
 
 assert C.sizeof(Desc) == 64
@@ -41,7 +41,7 @@ class TableHeader(C.Structure):
 
 
 assert C.sizeof(TableHeader) == 64
-TABLE_MAGIC = 0x324D5453
+TABLE_MAGIC = 0x334D5453
 UNITS_PER_GROUP = 4
 
 

@@ -33,20 +33,22 @@ def _run(cmd, verbose):
     return r.stdout
 
 
-def build(verbose: bool = False, extra_device_flags=(), out: str = LIB) -> str:
-    """Compile every source and link libstmat.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_device_flags=(), out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile every source and link libstmat.so; returns its path.  ``defines`` (e.g.
+    "STK_WORDS_FP8=4") override the compile-time work-unit geometry in every source."""
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     objs = []
     # host-only sources
     for src in ("index.cpp",):
-        o = os.path.join(BUILD, src + ".o")
-        _run(["g++", "-O2", *COMMON, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        o = os.path.join(build_dir, src + ".o")
+        _run(["g++", "-O2", *COMMON, *dflags, "-c", os.path.join(CSRC, src), "-o", o], verbose)
         objs.append(o)
     # sources that call the HIP runtime or hold kernels
     for src in ("stage.cpp", "materialize.hip"):
-        o = os.path.join(BUILD, src + ".o")
+        o = os.path.join(build_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([HIPCC, *lang, *COMMON, *DEVICE, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        _run([HIPCC, *lang, *COMMON, *DEVICE, *dflags, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", o], verbose)
         objs.append(o)
     tmp = out + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)

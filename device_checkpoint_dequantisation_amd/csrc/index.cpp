@@ -17,6 +17,7 @@
 #include <map>
 #include <memory>
 #include <new>
+#include <stdexcept>
 #include <string>
 #include <unordered_map>
 #include <utility>
@@ -565,6 +566,7 @@ st_status classify(st_index& ix) {
 }
 
 st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64_t unit_begin, uint64_t* units) {
+    // unit_begin + units stays below 2^32: build_table rejects larger tables before use
     st_desc d;
     memset(&d, 0, sizeof d);
     const Tensor& t = ix.tensors[o.tensor];
@@ -572,7 +574,6 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     d.scale = o.scale >= 0 ? ix.tensors[size_t(o.scale)].begin : 0;
     d.scale2 = o.scale2 >= 0 ? ix.tensors[size_t(o.scale2)].begin : 0;
     d.numel = o.numel;
-    d.unit_begin = unit_begin;
     d.out = out_slot;
     const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
     uint32_t div_shift = 0;
@@ -589,6 +590,9 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     }
     d.meta = uint32_t(o.kind) | unit_shift << 8 | div_shift << 16;
     *units = (o.numel + (uint64_t(1) << unit_shift) - 1) >> unit_shift;
+    d.unit_begin = uint32_t(unit_begin);
+    d.unit_end = uint32_t(unit_begin + *units);
+    d.tail = uint32_t(o.numel - ((*units ? *units - 1 : 0) << unit_shift));
     return d;
 }
 
@@ -601,6 +605,7 @@ std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, 
     for (size_t j = 0; j < k; ++j) {
         descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units[j]);
         pos += units[j];
+        if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
     }
     const uint64_t groups = (pos + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
     st_table_header h;
@@ -618,7 +623,7 @@ std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, 
     size_t d = 0;
     for (uint64_t g = 0; g < groups; ++g) {
         const uint64_t u = g * ST_UNITS_PER_GROUP;
-        while (descs[d].unit_begin + units[d] <= u) ++d;  // skips outputs with no units
+        while (descs[d].unit_end <= u) ++d;  // skips outputs with no units
         map[g] = uint32_t(d);
     }
     *units_out = pos;
@@ -636,10 +641,11 @@ st_status plan(st_index& ix) {
     ix.arena_bytes = pos;
     std::vector<uint32_t> all(ix.outputs.size());
     for (size_t k = 0; k < all.size(); ++k) all[k] = uint32_t(k);
-    ix.table = build_table(ix, all.data(), all.size(), &ix.total_units);
-    if (ix.total_units / ST_UNITS_PER_GROUP >= (uint64_t(1) << 31))
-        return st_fail(ST_E_SHAPE, "checkpoint needs %llu work units; at most 2^33 are supported",
-                       (unsigned long long)ix.total_units);
+    try {
+        ix.table = build_table(ix, all.data(), all.size(), &ix.total_units);
+    } catch (const std::length_error&) {
+        return st_fail(ST_E_SHAPE, "checkpoint needs 2^32 or more work units");
+    }
     return ST_OK;
 }
 
@@ -739,9 +745,7 @@ extern "C" void st_index_free(st_index* idx) { delete idx; }
 
 extern "C" uint64_t st_index_data_offset(const st_index* idx) { return idx ? 8 + idx->header_len : 0; }
 extern "C" uint64_t st_index_data_size(const st_index* idx) { return idx ? idx->data_size : 0; }
-extern "C" uint64_t st_index_blob_bytes(const st_index* idx) {
-    return idx ? std::max<uint64_t>(256, round_up(idx->data_size, 256)) : 0;
-}
+extern "C" uint64_t st_index_blob_bytes(const st_index* idx) { return idx ? round_up(idx->data_size + 64, 256) : 0; }
 extern "C" size_t st_index_count(const st_index* idx) { return idx ? idx->tensors.size() : 0; }
 
 extern "C" st_status st_index_tensor(const st_index* idx, size_t i, st_tensor_meta* out) {
@@ -825,6 +829,8 @@ extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* 
         t = build_table(*idx, sel, k, &u);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
+    } catch (const std::length_error&) {
+        return st_fail(ST_E_SHAPE, "st_index_table_subset: 2^32 or more work units");
     }
     if (bytes) *bytes = t.size();
     if (units) *units = u;

@@ -66,15 +66,14 @@ __device__ __forceinline__ float ld_f32(const uint8_t* p, bool aligned) {
     return aligned ? *reinterpret_cast<const float*>(p) : __builtin_bit_cast(float, ld_u32_any(p));
 }
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
-// A wave-uniform fp32 at any byte address: the aligned dword(s) around it, by scalar loads.
+// A wave-uniform fp32 at any byte address: the two aligned dwords around it (the blob is padded
+// past its data), one scalar load, then a funnel shift.
 __device__ __forceinline__ float ld_scalar_f32(const uint8_t* p) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const uint32_t r = a & 3u;
-    const uint32_t lo = ld_uniform<uint32_t>(reinterpret_cast<const void*>(a - r));
-    if (r == 0) return __builtin_bit_cast(float, lo);
-    const uint32_t hi = ld_uniform<uint32_t>(reinterpret_cast<const void*>(a - r + 4));
-    return __builtin_bit_cast(float, uint32_t((uint64_t(hi) << 32 | lo) >> (8 * r)));
+    const u32x2 w = ld_uniform<u32x2>(reinterpret_cast<const void*>(a & ~uintptr_t(3)));
+    return __builtin_bit_cast(float, uint32_t((uint64_t(w.y) << 32 | w.x) >> (8 * (a & 3u))));
 }
+
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // Upper 16 bits = bf16 of f rounded to nearest, ties to even (f not NaN).
@@ -124,8 +123,8 @@ __device__ __forceinline__ bool finite(float s) { return __builtin_fabsf(s) <= 3
 // ------------------------------------------------------------------------- descriptors
 
 struct Desc {
-    uint64_t src, scale, scale2, numel, unit_begin;
-    uint32_t out, cols, grid_cols, div_magic, kind, unit_shift, div_shift;
+    uint64_t src, scale, scale2, numel;
+    uint32_t unit_begin, unit_end, tail, out, cols, grid_cols, div_magic, kind, unit_shift, div_shift;
 };
 
 // The 64-byte descriptor in one scalar load.
@@ -136,20 +135,19 @@ __device__ __forceinline__ Desc load_desc(const st_desc* d) {
     r.scale = uint64_t(w[3]) << 32 | w[2];
     r.scale2 = uint64_t(w[5]) << 32 | w[4];
     r.numel = uint64_t(w[7]) << 32 | w[6];
-    r.unit_begin = uint64_t(w[9]) << 32 | w[8];
-    r.out = w[10];
-    r.cols = w[11];
-    r.grid_cols = w[12];
-    r.div_magic = w[13];
-    r.kind = w[14] & 0xFFu;
-    r.unit_shift = (w[14] >> 8) & 0xFFu;
-    r.div_shift = (w[14] >> 16) & 0xFFu;
+    r.unit_begin = w[8];
+    r.unit_end = w[9];
+    r.tail = w[10];
+    r.out = w[11];
+    r.cols = w[12];
+    r.grid_cols = w[13];
+    r.div_magic = w[14];
+    r.kind = w[15] & 0xFFu;
+    r.unit_shift = (w[15] >> 8) & 0xFFu;
+    r.div_shift = (w[15] >> 16) & 0xFFu;
     return r;
 }
-static_assert(offsetof(st_desc, meta) == 14 * 4, "descriptor layout");
-__device__ __forceinline__ uint64_t units_of(const Desc& D) {
-    return (D.numel + (uint64_t(1) << D.unit_shift) - 1) >> D.unit_shift;
-}
+static_assert(offsetof(st_desc, meta) == 15 * 4, "descriptor layout");
 
 // bf16 bits of element e of descriptor D, straight from the definition, byte by byte.
 __device__ __forceinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob, const Desc& D, uint64_t e) {
@@ -190,12 +188,8 @@ struct Ctx {
     Desc D;
     float s;         // FP8_TENSOR: the per-tensor scale; NVFP4: the global scale
     bool scale_al;   // the descriptor's scale data is 4-byte aligned
-    uintptr_t out;   // output address
+    bool vec;        // the output is 16-byte aligned (vector stores)
 };
-
-// A usable output is a bf16 address; a 16-byte aligned one takes the vector stores.
-__device__ __forceinline__ bool out_ok(const Ctx& c) { return (c.out & 1u) == 0; }
-__device__ __forceinline__ bool out_fast(const Ctx& c) { return (c.out & 15u) == 0; }
 
 struct KPass {
     static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
@@ -313,135 +307,156 @@ __device__ __forceinline__ void ld_word(const uint8_t* p, uint32_t* d) {
     }
 }
 
-// One step of a unit: chunks c = cbase + j*64 + lane (j < CH) of the unit whose first element is
-// e0; nch = whole chunks in the unit.  Source misalignment r = 4*Q + sh within an LG-byte word
-// (ALIGNED: r == 0).  Every load is issued before any decode.  Returns a mask of this lane's
-// chunks (bit j) that must take the exact path.
+// Load the IB source bytes of chunk ci (relative to the unit) into in[], as LG-byte aligned
+// words; the source misalignment within a word is r = 4*Q + sh (ALIGNED: r == 0).
 template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ uint32_t step(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cbase,
-                                         uint32_t nch, uint32_t sh, uint32_t lane) {
-    constexpr uint32_t NW = K::IB / K::LG;           // aligned words one chunk needs
-    constexpr uint32_t LWN = NW + (ALIGNED ? 0 : 1);  // words loaded per chunk
-    constexpr uint32_t DW = K::LG / 4;               // dwords per loaded word
-    constexpr uint32_t OW = K::CE / stk::kWordElems; // output words per chunk
-    const uint8_t* src = c.blob + c.D.src + K::src_off(e0);
-    const uint8_t* base = src - (ALIGNED ? 0 : (Q * 4 + sh));
-    uint32_t raw[K::CH][LWN * DW];
-    bool live[K::CH];
+__device__ __forceinline__ void fetch(const uint8_t* base, uint32_t ci, uint32_t* raw) {
+    constexpr uint32_t LWN = K::IB / K::LG + (ALIGNED ? 0 : 1);
+#pragma unroll
+    for (uint32_t k = 0; k < LWN; ++k) ld_word<K::LG>(base + size_t(ci) * K::IB + k * K::LG, &raw[k * (K::LG / 4)]);
+}
+template <class K, uint32_t Q, bool ALIGNED>
+__device__ __forceinline__ void align_in(const uint32_t* raw, uint32_t sh, uint32_t* in) {
+#pragma unroll
+    for (uint32_t k = 0; k < K::IB / 4; ++k)
+        in[k] = ALIGNED ? raw[k] : __builtin_amdgcn_alignbyte(raw[Q + k + 1], raw[Q + k], sh);
+}
+
+// Exact path for one chunk (or its first n elements).
+__device__ __forceinline__ void chunk_exact(const Ctx& c, uint16_t* __restrict__ out, uint64_t e, uint32_t n) {
+    for (uint32_t k = 0; k < n; ++k) out[e + k] = uint16_t(elem_exact(c.blob, c.D, e + k));
+}
+
+// A unit of exactly CH * 64 whole chunks (the default unit size): no per-chunk bounds checks.
+// Every load is issued before any decode; lanes whose chunk cannot take the fast path are
+// finished by the exact path after a wave-wide vote.
+template <class K, uint32_t Q, bool ALIGNED>
+__device__ __forceinline__ void unit_full(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t sh,
+                                          uint32_t lane) {
+    constexpr uint32_t RW = (K::IB / K::LG + (ALIGNED ? 0 : 1)) * (K::LG / 4);
+    constexpr uint32_t OW = K::CE / stk::kWordElems;
+    const uint8_t* base = c.blob + c.D.src + K::src_off(e0) - (ALIGNED ? 0 : (Q * 4 + sh));
+    uint32_t raw[K::CH][RW];
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) fetch<K, Q, ALIGNED>(base, j * stk::kWave + lane, raw[j]);
+    bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
-        const uint32_t ci = cbase + j * stk::kWave + lane;
-        live[j] = ci < nch;
-        if (live[j]) {
+        uint32_t in[K::IB / 4];
+        align_in<K, Q, ALIGNED>(raw[j], sh, in);
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        u32x4 v[OW];
+        ok[j] = c.vec && K::fast(c, in, e, v);
+        if (ok[j]) {
 #pragma unroll
-            for (uint32_t k = 0; k < LWN; ++k) ld_word<K::LG>(base + size_t(ci) * K::IB + k * K::LG, &raw[j][k * DW]);
+            for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
         }
     }
-    if (!out_ok(c)) return 0;
-    const bool vec = out_fast(c);
-    uint32_t fail = 0;
+    bool all = true;
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) {
-        if (!live[j]) continue;
-        const uint32_t ci = cbase + j * stk::kWave + lane;
-        uint32_t in[K::IB / 4];
+    for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+    if (__builtin_amdgcn_ballot_w64(!all) == 0) return;  // the common case
 #pragma unroll
-        for (uint32_t k = 0; k < K::IB / 4; ++k)
-            in[k] = ALIGNED ? raw[j][k] : __builtin_amdgcn_alignbyte(raw[j][Q + k + 1], raw[j][Q + k], sh);
+    for (uint32_t j = 0; j < K::CH; ++j)
+        if (!ok[j]) chunk_exact(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
+}
+
+// Any unit: cnt elements (a larger unit size, or an output's final unit).
+template <class K, uint32_t Q, bool ALIGNED>
+__device__ __forceinline__ void unit_any(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
+                                      uint32_t sh, uint32_t lane) {
+    constexpr uint32_t RW = (K::IB / K::LG + (ALIGNED ? 0 : 1)) * (K::LG / 4);
+    constexpr uint32_t OW = K::CE / stk::kWordElems;
+    const uint8_t* base = c.blob + c.D.src + K::src_off(e0) - (ALIGNED ? 0 : (Q * 4 + sh));
+    const uint32_t nch = cnt / K::CE;  // whole chunks
+    for (uint32_t ci = lane; ci < nch; ci += stk::kWave) {
+        uint32_t raw[RW], in[K::IB / 4];
+        fetch<K, Q, ALIGNED>(base, ci, raw);
+        align_in<K, Q, ALIGNED>(raw, sh, in);
         const uint64_t e = e0 + uint64_t(ci) * K::CE;
         u32x4 v[OW];
-        if (vec && K::fast(c, in, e, v)) {
+        if (c.vec && K::fast(c, in, e, v)) {
 #pragma unroll
             for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
         } else {
-            fail |= 1u << j;
+            chunk_exact(c, out, e, K::CE);
         }
     }
-    return fail;
+    for (uint32_t t = nch * K::CE + lane; t < cnt; t += stk::kWave)  // past the last whole chunk
+        out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
 }
 
-template <class K>
-__device__ __forceinline__ uint32_t step_any(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cbase,
-                                             uint32_t nch, uint32_t lane) {
-    const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)) & (K::LG - 1));
-    const uint32_t sh = r & 3u;
-    if (r == 0) return step<K, 0, true>(c, out, e0, cbase, nch, sh, lane);
-    switch (r >> 2) {
-        case 0: return step<K, 0, false>(c, out, e0, cbase, nch, sh, lane);
-        case 1: if constexpr (K::LG > 4) return step<K, 1, false>(c, out, e0, cbase, nch, sh, lane);
-                [[fallthrough]];
-        case 2: if constexpr (K::LG > 8) return step<K, 2, false>(c, out, e0, cbase, nch, sh, lane);
-                [[fallthrough]];
-        default: if constexpr (K::LG > 8) return step<K, 3, false>(c, out, e0, cbase, nch, sh, lane);
-                 return 0;
-    }
+template <class K, uint32_t Q, bool ALIGNED>
+__device__ __forceinline__ void unit_dispatch(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
+                                              uint32_t sh, uint32_t lane) {
+    if (cnt == K::CE * K::CH * stk::kWave) unit_full<K, Q, ALIGNED>(c, out, e0, sh, lane);
+    else unit_any<K, Q, ALIGNED>(c, out, e0, cnt, sh, lane);
 }
 
 template <class K>
 __device__ __forceinline__ void run_unit(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
                                          uint32_t lane) {
-    const uint32_t nch = cnt / K::CE;  // whole chunks in this unit
-    for (uint32_t cbase = 0; cbase < nch; cbase += K::CH * stk::kWave) {
-        uint32_t fail = step_any<K>(c, out, e0, cbase, nch, lane);
-        while (fail) {  // rare: NaN inputs, special scales, misaligned outputs
-            const uint32_t j = __builtin_ctz(fail);
-            fail &= fail - 1;
-            const uint64_t e = e0 + uint64_t(cbase + j * stk::kWave + lane) * K::CE;
-            for (uint32_t k = 0; k < K::CE; ++k) out[e + k] = uint16_t(elem_exact(c.blob, c.D, e + k));
+    const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)) & (K::LG - 1));
+    const uint32_t sh = r & 3u;
+    if (r == 0) return unit_dispatch<K, 0, true>(c, out, e0, cnt, sh, lane);
+    if constexpr (K::LG == 4) {
+        unit_dispatch<K, 0, false>(c, out, e0, cnt, sh, lane);
+    } else {
+        switch (r >> 2) {
+            case 0: unit_dispatch<K, 0, false>(c, out, e0, cnt, sh, lane); break;
+            case 1: unit_dispatch<K, 1, false>(c, out, e0, cnt, sh, lane); break;
+            case 2: unit_dispatch<K, 2, false>(c, out, e0, cnt, sh, lane); break;
+            default: unit_dispatch<K, 3, false>(c, out, e0, cnt, sh, lane); break;
         }
     }
-    // elements past the last whole chunk (only in an output's final unit)
-    if (!out_ok(c)) return;
-    for (uint32_t t = nch * K::CE + lane; t < cnt; t += stk::kWave)
-        out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
 }
 
 // ------------------------------------------------------------------------- the kernel
 
 __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __restrict__ blob,
-                                                             const uint8_t* __restrict__ table, uint64_t units,
-                                                             uint32_t groups, uint16_t* const* __restrict__ outs) {
+                                                             const uint8_t* __restrict__ table, uint32_t units,
+                                                             uint32_t groups, uint32_t desc_off,
+                                                             uint16_t* const* __restrict__ outs) {
     // XCD-contiguous renumbering: workgroup b runs on XCD b % 8; XCD x gets the contiguous range
     // of groups [start_x, start_x + count_x), a bijection of [0, groups).
     const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
     if (b >= groups) return;
-    const uint32_t q = groups / 8, rem = groups % 8, x = b % 8;
-    const uint32_t grp = x * q + (x < rem ? x : rem) + b / 8;
-    const uint32_t lane = threadIdx.x & (stk::kWave - 1);
-    const uint64_t unit = uint64_t(grp) * ST_UNITS_PER_GROUP + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t x = b & 7u, q = groups >> 3, rem = groups & 7u;
+    const uint32_t grp = x * q + (x < rem ? x : rem) + (b >> 3);
+    const uint32_t unit = grp * ST_UNITS_PER_GROUP + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= units) return;
+    const uint32_t lane = threadIdx.x & (stk::kWave - 1);
 
-    // The map sits at a fixed offset and the descriptors right after it, so the header (magic
-    // and unit count, one scalar load), the map entry and the descriptor are the only loads ahead
-    // of the data.  A table that does not match n is left alone before anything indexes it.
+    // Header (magic, unit count) and this group's map entry, then the descriptor: the only loads
+    // ahead of the data.  A table that does not match n is left alone before anything indexes it.
     const u32x4 hw = ld_uniform<u32x4>(table);
-    if ((hw.x != ST_TABLE_MAGIC) | (((uint64_t(hw.w) << 32) | hw.z) != units)) return;
-    const uint32_t* map = reinterpret_cast<const uint32_t*>(table + sizeof(st_table_header));
-    const st_desc* descs = reinterpret_cast<const st_desc*>(table + stk::table_desc_offset(groups));
-    uint32_t d = ld_uniform<uint32_t>(map + grp);
+    if ((hw.x != ST_TABLE_MAGIC) | (hw.z != units) | (hw.w != 0)) return;
+    uint32_t d = ld_uniform<uint32_t>(table + sizeof(st_table_header) + 4 * size_t(grp));
+    const st_desc* descs = reinterpret_cast<const st_desc*>(table + desc_off);
     Desc D = load_desc(descs + d);
-    while (unit >= D.unit_begin + units_of(D)) D = load_desc(descs + (++d));
+    while (unit >= D.unit_end) D = load_desc(descs + (++d));  // at most 3 steps, past empty outputs
 
-    const uint64_t e0 = (unit - D.unit_begin) << D.unit_shift;
-    const uint64_t left = D.numel - e0;
-    const uint32_t cnt = uint32_t(left < (uint64_t(1) << D.unit_shift) ? left : (uint64_t(1) << D.unit_shift));
+    const uint64_t e0 = uint64_t(unit - D.unit_begin) << D.unit_shift;
+    const uint32_t cnt = unit + 1 == D.unit_end ? D.tail : 1u << D.unit_shift;
     uint16_t* out = ld_uniform<uint16_t*>(outs + D.out);
+    const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
+    if (oa & 1u) return;  // not a bf16 address: nothing is written
 
     Ctx c;
     c.blob = blob;
     c.D = D;
     c.scale_al = (D.scale & 3u) == 0;
-    c.out = reinterpret_cast<uintptr_t>(out);
+    c.vec = (oa & 15u) == 0;  // otherwise every chunk takes the exact path
     c.s = D.kind == ST_KIND_FP8_TENSOR ? ld_scalar_f32(blob + D.scale)
         : D.kind == ST_KIND_NVFP4      ? ld_scalar_f32(blob + D.scale2)
                                        : 0.0f;
     switch (D.kind) {
-        case ST_KIND_PASS_BF16: run_unit<KPass>(c, out, e0, cnt, lane); break;
-        case ST_KIND_CAST_F16: run_unit<KF16>(c, out, e0, cnt, lane); break;
-        case ST_KIND_CAST_F32: run_unit<KF32>(c, out, e0, cnt, lane); break;
         case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor>(c, out, e0, cnt, lane); break;
         case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block>(c, out, e0, cnt, lane); break;
-        default: run_unit<KFp4>(c, out, e0, cnt, lane); break;
+        case ST_KIND_NVFP4: run_unit<KFp4>(c, out, e0, cnt, lane); break;
+        case ST_KIND_PASS_BF16: run_unit<KPass>(c, out, e0, cnt, lane); break;
+        case ST_KIND_CAST_F16: run_unit<KF16>(c, out, e0, cnt, lane); break;
+        default: run_unit<KF32>(c, out, e0, cnt, lane); break;
     }
 }
 
@@ -453,13 +468,13 @@ extern "C" st_status st_materialize(const void* blob, const void* descs, size_t 
     if (reinterpret_cast<uintptr_t>(blob) % ST_BLOB_ALIGN)
         return st_fail(ST_E_ARG, "st_materialize: blob is not %d-byte aligned", ST_BLOB_ALIGN);
     if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "st_materialize: work table is not 64-byte aligned");
-    const uint64_t groups = (uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
-    if (groups >= (uint64_t(1) << 31)) return st_fail(ST_E_ARG, "st_materialize: %zu work units is too many", n);
-    const uint32_t gx = uint32_t(groups < kMaxGridX ? groups : kMaxGridX);
-    const uint32_t gy = uint32_t((groups + gx - 1) / gx);
+    if (uint64_t(n) >= (uint64_t(1) << 32)) return st_fail(ST_E_ARG, "st_materialize: %zu work units (at most 2^32 - 1)", n);
+    const uint32_t groups = uint32_t((uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP);
+    const uint32_t gx = groups < kMaxGridX ? groups : kMaxGridX;
+    const uint32_t gy = (groups + gx - 1) / gx;
     hipLaunchKernelGGL(materialize_kernel, dim3(gx, gy), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint8_t*>(blob), static_cast<const uint8_t*>(descs), uint64_t(n),
-                       uint32_t(groups), reinterpret_cast<uint16_t* const*>(outs));
+                       static_cast<const uint8_t*>(blob), static_cast<const uint8_t*>(descs), uint32_t(n), groups,
+                       uint32_t(stk::table_desc_offset(groups)), reinterpret_cast<uint16_t* const*>(outs));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return st_fail(ST_E_HIP, "st_materialize: launch failed: %s", hipGetErrorString(e));
     return ST_OK;

@@ -21,7 +21,20 @@ st_status st_fail(st_status code, const char* fmt, ...) __attribute__((format(pr
 namespace stk {
 constexpr uint32_t kWave = 64;
 constexpr uint32_t kWordElems = 8;
-constexpr uint32_t kWordsPass = 2, kWordsF32 = 1, kWordsFp8 = 2, kWordsFp4 = 4;
+#ifndef STK_WORDS_PASS
+#define STK_WORDS_PASS 2
+#endif
+#ifndef STK_WORDS_F32
+#define STK_WORDS_F32 1
+#endif
+#ifndef STK_WORDS_FP8
+#define STK_WORDS_FP8 2
+#endif
+#ifndef STK_WORDS_FP4
+#define STK_WORDS_FP4 4
+#endif
+constexpr uint32_t kWordsPass = STK_WORDS_PASS, kWordsF32 = STK_WORDS_F32, kWordsFp8 = STK_WORDS_FP8,
+                   kWordsFp4 = STK_WORDS_FP4;
 
 constexpr uint32_t ilog2(uint32_t x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 

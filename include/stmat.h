@@ -111,13 +111,13 @@ typedef struct st_output_info {
  * elements has ceil(numel / 2^unit_shift) units, numbered in output order from unit_begin.
  * The kernel runs one 64-lane wavefront per unit and one 4-wave workgroup per map entry.
  * Offsets in descriptors are bytes from the start of the blob (= the file's data section). */
-#define ST_TABLE_MAGIC 0x324D5453u   /* "STM2" */
+#define ST_TABLE_MAGIC 0x334D5453u   /* "STM3" */
 #define ST_UNITS_PER_GROUP 4
 
 typedef struct st_table_header {
     uint32_t magic;          /* ST_TABLE_MAGIC */
     uint32_t n_desc;         /* descriptors */
-    uint64_t units;          /* work units */
+    uint64_t units;          /* work units (below 2^32) */
     uint64_t desc_offset;    /* bytes from the table start to st_desc[0] */
     uint64_t map_offset;     /* bytes from the table start to map[0] (always 64) */
     uint64_t bytes;          /* size of the whole table */
@@ -129,14 +129,15 @@ typedef struct st_desc {
     uint64_t scale;          /* FP8_TENSOR fp32 scale / FP8_BLOCK128 fp32 grid / NVFP4 e4m3 block scales */
     uint64_t scale2;         /* NVFP4 fp32 global scale */
     uint64_t numel;          /* output elements */
-    uint64_t unit_begin;     /* index of this output's first work unit in the table */
+    uint32_t unit_begin;     /* this output's first work unit in the table */
+    uint32_t unit_end;       /* one past its last work unit */
+    uint32_t tail;           /* elements in its last unit (1 .. 2^unit_shift) */
     uint32_t out;            /* index into the outs[] pointer array */
     uint32_t cols;           /* FP8_BLOCK128: N, NVFP4: K, otherwise 0 */
     uint32_t grid_cols;      /* FP8_BLOCK128: ceil(N / 128) */
     uint32_t div_magic;      /* FP8_BLOCK128: multiplier of the exact division by N */
     uint32_t meta;           /* st_kind | unit_shift << 8 | div_shift << 16 (a unit is
                                 2^unit_shift elements; div_shift goes with div_magic) */
-    uint32_t reserved;
 } st_desc;                   /* 64 bytes */
 
 /* Planning options; pass NULL for the defaults. */
@@ -170,8 +171,9 @@ void st_index_free(st_index* idx);
 
 uint64_t st_index_data_offset(const st_index* idx);   /* 8 + N: file offset of the data section */
 uint64_t st_index_data_size(const st_index* idx);     /* bytes of the data section */
-/* Bytes to allocate for the device blob: data size rounded up to a multiple of 256.  The
- * kernel reads whole aligned 16-byte words, so the padding must be present. */
+/* Bytes to allocate for the device blob: data size plus 64, rounded up to a multiple of 256.
+ * The kernel reads whole aligned words, which may reach a few bytes past the data, so the
+ * padding must be present. */
 uint64_t st_index_blob_bytes(const st_index* idx);
 size_t st_index_count(const st_index* idx);           /* header entries (tensors) */
 st_status st_index_tensor(const st_index* idx, size_t i, st_tensor_meta* out);

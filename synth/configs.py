@@ -91,6 +91,25 @@ def g_scaled_fp8(prefix, shape, seed, scale_lo=0.001, scale_hi=0.01):
                   TensorSpec(prefix + ".scale_weight", "F32", ())], make, seed, cost=n)
 
 
+def g_scaled_fp8_split(prefix, shape, seed, scale_lo=0.001, scale_hi=0.01):
+    """The same pair as two groups (weight, scale) so the scale can sit elsewhere in the file;
+    the scale comes from its own stream, default_rng([*seed, 1]), which both groups draw."""
+    n = _numel(shape)
+
+    def scale():
+        return np.float32(np.random.default_rng([*seed, 1]).uniform(scale_lo, scale_hi))
+
+    def make_w(rng):
+        w = _normal(rng, n)
+        w /= scale()
+        np.clip(w, -E4M3_MAX, E4M3_MAX, out=w)
+        return [_e4m3(w)]
+
+    return (Group([TensorSpec(prefix + ".weight", "F8_E4M3", tuple(shape))], make_w, seed, cost=n),
+            Group([TensorSpec(prefix + ".scale_weight", "F32", ())], lambda rng: [np.array(scale(), np.float32)],
+                  (*seed, 2), cost=1))
+
+
 def g_block_fp8(prefix, shape, seed, block=128):
     """``prefix.weight`` e4m3fn [M, N] + ``prefix.weight_scale_inv`` fp32 [ceil(M/128), ceil(N/128)]
     drawn log-uniform in [1e-4, 1e-2]; each weight is divided by its own block's value."""
@@ -147,8 +166,12 @@ def tiny(seed=1):
     return gs, {"synthetic": "tiny", "seed": seed}, False
 
 
-def scaled_fp8(seed=2, blocks=57, hidden=3072, mlp=12288):
+def scaled_fp8(seed=2, blocks=57, hidden=3072, mlp=12288, scales_last=False):
+    """Scales follow their weights (most weights then start 4, 8 or 12 bytes off a 16-byte line);
+    with scales_last=True every scale moves to the end of the file and every weight is 16-byte
+    aligned (same shapes and distributions, different draws)."""
     gs = []
+    tail = []
     k = 0
 
     def sd():
@@ -156,17 +179,25 @@ def scaled_fp8(seed=2, blocks=57, hidden=3072, mlp=12288):
         k += 1
         return (seed, k)
 
+    def fp8(prefix, shape):
+        if scales_last:
+            w, sc = g_scaled_fp8_split(prefix, shape, sd())
+            gs.append(w)
+            tail.append(sc)
+        else:
+            gs.append(g_scaled_fp8(prefix, shape, sd()))
+
     for b in range(blocks):
         p = f"blocks.{b}."
         gs.append(g_plain(p + "norm1.weight", "BF16", (hidden,), sd()))
         for proj in ("q", "k", "v", "o"):
-            gs.append(g_scaled_fp8(p + f"attn.{proj}", (hidden, hidden), sd()))
+            fp8(p + f"attn.{proj}", (hidden, hidden))
             gs.append(g_plain(p + f"attn.{proj}.bias", "BF16", (hidden,), sd()))
         gs.append(g_plain(p + "norm2.weight", "BF16", (hidden,), sd()))
-        gs.append(g_scaled_fp8(p + "mlp.up", (mlp, hidden), sd()))
-        gs.append(g_scaled_fp8(p + "mlp.down", (hidden, mlp), sd()))
+        fp8(p + "mlp.up", (mlp, hidden))
+        fp8(p + "mlp.down", (hidden, mlp))
         gs.append(g_plain(p + "mlp.down.bias", "BF16", (hidden,), sd()))
-    return gs, {"synthetic": "scaled_fp8", "seed": seed}, True
+    return gs + tail, {"synthetic": "scaled_fp8" + ("_aligned" if scales_last else ""), "seed": seed}, True
 
 
 def block_fp8(seed=3, layers=28, hidden=4096, inter=12288, vocab=151936):

@@ -61,9 +61,9 @@ def test_tiny_traffic_is_the_documented_figure():
 
 STEP_SHIFT = {"PASS_BF16": 10, "CAST_F16": 10, "CAST_F32": 9, "FP8_TENSOR": 10, "FP8_BLOCK128": 10, "NVFP4": 11}
 
-DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u8"),
-                 ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"), ("div_magic", "<u4"), ("kind", "u1"),
-                 ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1"), ("r1", "<u4")])  # meta, little-endian
+DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u4"),
+                 ("unit_end", "<u4"), ("tail", "<u4"), ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"),
+                 ("div_magic", "<u4"), ("kind", "u1"), ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1")])
 HEADER = np.dtype([("magic", "<u4"), ("n_desc", "<u4"), ("units", "<u8"), ("desc_offset", "<u8"),
                    ("map_offset", "<u8"), ("bytes", "<u8"), ("reserved", "<u8", 3)])
 
@@ -81,6 +81,11 @@ def _table(raw: bytes):
 def _check_map(d, m, units):
     # every group of 4 units maps to the descriptor holding its first unit
     ends = d["unit_begin"].astype(np.int64) + (-(-d["numel"].astype(np.int64) // (1 << d["unit_shift"].astype(np.int64))))
+    assert np.array_equal(ends, d["unit_end"].astype(np.int64))
+    for row in d:   # the last unit's length
+        n, sh = int(row["numel"]), int(row["unit_shift"])
+        if n:
+            assert row["tail"] == n - ((-(-n // (1 << sh)) - 1) << sh) and 1 <= row["tail"] <= 1 << sh
     for g, di in enumerate(m):
         u = g * _lib.UNITS_PER_GROUP
         assert d[di]["unit_begin"] <= u < ends[di], (g, di)
