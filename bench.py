@@ -35,8 +35,35 @@ WORKLOADS = {
 }
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("device_checkpoint_dequantisation_amd/csrc/materialize.hip",
+                  "device_checkpoint_dequantisation_amd/csrc/st_internal.h")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def profiled_traffic(k):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (profiles/materialize_hbm_counters.md), or None when that summary does not cover config k or
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "materialize_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha, traffic = None, None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "kernel_sources_sha256":
+            sha = parts[1]
+        if len(parts) == 3 and parts[0] == "traffic_bytes" and parts[1] == f"c{k}":
+            traffic = int(parts[2])
+    return traffic if sha == h.hexdigest() else None
 
 
 def parse():
@@ -215,7 +242,7 @@ def main():
         "config": {"workload": WORKLOADS[args.config], "read_bytes": r["read"], "written_bytes": r["written"],
                    "outputs": r["outputs"], "hbm_peak_frac": round(r["GBps"] / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(r["kernel_GBps"], 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(r["kernel_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(r["kernel_GBps"] / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config)},
         "cpu_baseline": cpu,
         "kernel_ms": {"mean": round(r["kernel_ms_mean"], 4), "median": round(r["kernel_ms_median"], 4),
                       "min": round(r["kernel_ms_min"], 4)},
