@@ -24,9 +24,15 @@
 //    wavefronts take four consecutive units, whatever output they belong to, so small tensors are
 //    packed at wavefront granularity.  A per-workgroup map gives the descriptor of the group's
 //    first unit; a wavefront walks forward at most three descriptors.
-//  * Unaligned sources.  A tensor may start at any byte.  Loads are always naturally aligned
-//    words; the offset r of the source within a word (the same for every lane of a unit) is
-//    removed in registers with v_alignbyte over the two words the bytes straddle.
+//  * Unaligned sources.  A tensor may start at any byte.  A unit whose source is 16-byte aligned
+//    loads whole 16-byte words (4-byte words for NVFP4).  Otherwise each lane loads from the
+//    4-byte boundary at or below its bytes (16-byte words at 4-byte alignment plus one trailing
+//    dword), and the byte offset sh (the same for every lane of a unit) is removed in registers
+//    with v_alignbyte.  Measured on MI355X, this beats loading the two enclosing aligned 16-byte
+//    words and selecting among them.
+//  * Short dependency chain.  Ahead of a wavefront's data loads sit only the table header check,
+//    its map entry and its descriptor; the output pointer and the scalar scale are loaded once the
+//    data loads are in flight (a wait for one scalar load waits for all of them).
 //  * Decoding uses gfx950's conversion instructions (fp8 and fp4 to fp32, fp32 to bf16), each
 //    checked exhaustively against the exact decoding on the device; one fp32 multiply per scale.
 //  * Tails, NaN inputs, non-finite scales, block-FP8 widths not a multiple of 16 and misaligned
@@ -181,17 +187,19 @@ __device__ __forceinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob,
 // must take the exact path.  CH = chunks per lane per step; chunk c of a step belongs to lane
 // c % 64.
 
-// Per-unit context.  The scale is only loaded here; deciding whether it folds, and whether the
-// output pointer is usable, happens in the decode, after the data loads have been issued.
+// Per-unit context.  `s` and `vec` are filled in by finish_ctx, after the data loads are issued;
+// whether the scale folds into the fast path is decided in the decode.
 struct Ctx {
     const uint8_t* blob;
     Desc D;
+    uint16_t* const* outs;  // output pointers, indexed by the descriptor's `out`
     float s;         // FP8_TENSOR: the per-tensor scale; NVFP4: the global scale
     bool scale_al;   // the descriptor's scale data is 4-byte aligned
     bool vec;        // the output is 16-byte aligned (vector stores)
 };
 
 struct KPass {
+    static constexpr int SCALE = 0;  // no scalar scale
     static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
@@ -201,6 +209,7 @@ struct KPass {
 };
 
 struct KF16 {
+    static constexpr int SCALE = 0;  // no scalar scale
     static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
@@ -217,6 +226,7 @@ struct KF16 {
 };
 
 struct KF32 {
+    static constexpr int SCALE = 0;  // no scalar scale
     static constexpr uint32_t CE = 8, IB = 32, LG = 16, CH = stk::kWordsF32;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 4; }
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
@@ -253,6 +263,7 @@ __device__ __forceinline__ bool fp8_chunk(const uint32_t* in, float s, u32x4* o)
 }
 
 struct KFp8Tensor {
+    static constexpr int SCALE = 1;  // D.scale
     static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, u32x4* o) {
@@ -261,6 +272,7 @@ struct KFp8Tensor {
 };
 
 struct KFp8Block {
+    static constexpr int SCALE = 0;  // no scalar scale
     static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
     // e: first element of the chunk (a multiple of 16); with cols % 16 == 0 the chunk lies in
@@ -276,6 +288,7 @@ struct KFp8Block {
 };
 
 struct KFp4 {
+    static constexpr int SCALE = 2;  // D.scale2
     static constexpr uint32_t CE = 8, IB = 4, LG = 4, CH = stk::kWordsFp4;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
     // 8 elements: (e2m1 * block scale) is exact in fp32, then one RNE multiply by g
@@ -292,34 +305,54 @@ struct KFp4 {
     }
 };
 
-// ------------------------------------------------------------------------- aligned loads
+// ------------------------------------------------------------------------- loads
 
-template <uint32_t LG>
-__device__ __forceinline__ void ld_word(const uint8_t* p, uint32_t* d) {
-    if constexpr (LG == 16) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    } else if constexpr (LG == 8) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-        d[0] = v.x; d[1] = v.y;
-    } else {
-        d[0] = *reinterpret_cast<const uint32_t*>(p);
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// The IB source bytes of chunk ci (relative to the unit base) as IB/4 dwords in `in`.
+//  ALIGNED: base is LG-aligned; IB/LG naturally aligned LG-byte loads.
+//  otherwise: base is the 4-byte boundary sh bytes below the source; IB/16 16-byte loads at
+//  4-byte alignment (one 4-byte load for NVFP4) plus one trailing dword, then a funnel shift.
+template <class K, bool ALIGNED>
+struct Fetch {
+    static constexpr uint32_t N = K::IB / 4;            // dwords of input per chunk
+    static constexpr uint32_t RW = ALIGNED ? N : N + 1;  // dwords loaded per chunk
+    static __device__ __forceinline__ void load(const uint8_t* base, uint32_t ci, uint32_t* raw) {
+        const uint8_t* p = base + size_t(ci) * K::IB;
+        if constexpr (ALIGNED && K::LG == 16) {
+#pragma unroll
+            for (uint32_t k = 0; k < N / 4; ++k) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * k);
+                raw[4 * k] = v.x; raw[4 * k + 1] = v.y; raw[4 * k + 2] = v.z; raw[4 * k + 3] = v.w;
+            }
+        } else {
+            constexpr uint32_t W4 = N / 4;  // 16-byte loads
+#pragma unroll
+            for (uint32_t k = 0; k < W4; ++k) {
+                const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p + 16 * k);
+                raw[4 * k] = v.x; raw[4 * k + 1] = v.y; raw[4 * k + 2] = v.z; raw[4 * k + 3] = v.w;
+            }
+#pragma unroll
+            for (uint32_t k = 4 * W4; k < RW; ++k) raw[k] = reinterpret_cast<const uint32_t*>(p)[k];
+        }
     }
-}
+    static __device__ __forceinline__ void align(const uint32_t* raw, uint32_t sh, uint32_t* in) {
+#pragma unroll
+        for (uint32_t k = 0; k < N; ++k) in[k] = ALIGNED ? raw[k] : __builtin_amdgcn_alignbyte(raw[k + 1], raw[k], sh);
+    }
+};
 
-// Load the IB source bytes of chunk ci (relative to the unit) into in[], as LG-byte aligned
-// words; the source misalignment within a word is r = 4*Q + sh (ALIGNED: r == 0).
-template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ void fetch(const uint8_t* base, uint32_t ci, uint32_t* raw) {
-    constexpr uint32_t LWN = K::IB / K::LG + (ALIGNED ? 0 : 1);
-#pragma unroll
-    for (uint32_t k = 0; k < LWN; ++k) ld_word<K::LG>(base + size_t(ci) * K::IB + k * K::LG, &raw[k * (K::LG / 4)]);
-}
-template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ void align_in(const uint32_t* raw, uint32_t sh, uint32_t* in) {
-#pragma unroll
-    for (uint32_t k = 0; k < K::IB / 4; ++k)
-        in[k] = ALIGNED ? raw[k] : __builtin_amdgcn_alignbyte(raw[Q + k + 1], raw[Q + k], sh);
+// The output pointer and the kind's scalar scale, loaded after the unit's data loads are issued.
+// False: the output address is not a bf16 address, and nothing is written.
+template <class K>
+__device__ __forceinline__ bool finish_ctx(Ctx& c, uint16_t*& out) {
+    out = ld_uniform<uint16_t*>(c.outs + c.D.out);
+    if constexpr (K::SCALE == 1) c.s = ld_scalar_f32(c.blob + c.D.scale);
+    else if constexpr (K::SCALE == 2) c.s = ld_scalar_f32(c.blob + c.D.scale2);
+    else c.s = 0.0f;
+    const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
+    c.vec = (oa & 15u) == 0;
+    return (oa & 1u) == 0;
 }
 
 // Exact path for one chunk (or its first n elements).
@@ -328,22 +361,22 @@ __device__ __forceinline__ void chunk_exact(const Ctx& c, uint16_t* __restrict__
 }
 
 // A unit of exactly CH * 64 whole chunks (the default unit size): no per-chunk bounds checks.
-// Every load is issued before any decode; lanes whose chunk cannot take the fast path are
-// finished by the exact path after a wave-wide vote.
-template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ void unit_full(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t sh,
-                                          uint32_t lane) {
-    constexpr uint32_t RW = (K::IB / K::LG + (ALIGNED ? 0 : 1)) * (K::LG / 4);
+template <class K, bool ALIGNED>
+__device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, ALIGNED>;
     constexpr uint32_t OW = K::CE / stk::kWordElems;
-    const uint8_t* base = c.blob + c.D.src + K::src_off(e0) - (ALIGNED ? 0 : (Q * 4 + sh));
-    uint32_t raw[K::CH][RW];
+    const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
+    uint32_t raw[K::CH][F::RW];
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) fetch<K, Q, ALIGNED>(base, j * stk::kWave + lane, raw[j]);
+    for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
+    Ctx c = c0;
+    uint16_t* out;
+    if (!finish_ctx<K>(c, out)) return;
     bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
-        uint32_t in[K::IB / 4];
-        align_in<K, Q, ALIGNED>(raw[j], sh, in);
+        uint32_t in[F::N];
+        F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
         u32x4 v[OW];
         ok[j] = c.vec && K::fast(c, in, e, v);
@@ -362,17 +395,19 @@ __device__ __forceinline__ void unit_full(const Ctx& c, uint16_t* __restrict__ o
 }
 
 // Any unit: cnt elements (a larger unit size, or an output's final unit).
-template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ void unit_any(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
-                                      uint32_t sh, uint32_t lane) {
-    constexpr uint32_t RW = (K::IB / K::LG + (ALIGNED ? 0 : 1)) * (K::LG / 4);
+template <class K, bool ALIGNED>
+__device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, ALIGNED>;
     constexpr uint32_t OW = K::CE / stk::kWordElems;
-    const uint8_t* base = c.blob + c.D.src + K::src_off(e0) - (ALIGNED ? 0 : (Q * 4 + sh));
+    Ctx c = c0;
+    uint16_t* out;
+    if (!finish_ctx<K>(c, out)) return;
+    const uint8_t* base = c.blob + c.D.src + K::src_off(e0) - sh;
     const uint32_t nch = cnt / K::CE;  // whole chunks
     for (uint32_t ci = lane; ci < nch; ci += stk::kWave) {
-        uint32_t raw[RW], in[K::IB / 4];
-        fetch<K, Q, ALIGNED>(base, ci, raw);
-        align_in<K, Q, ALIGNED>(raw, sh, in);
+        uint32_t raw[F::RW], in[F::N];
+        F::load(base, ci, raw);
+        F::align(raw, sh, in);
         const uint64_t e = e0 + uint64_t(ci) * K::CE;
         u32x4 v[OW];
         if (c.vec && K::fast(c, in, e, v)) {
@@ -386,29 +421,19 @@ __device__ __forceinline__ void unit_any(const Ctx& c, uint16_t* __restrict__ ou
         out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
 }
 
-template <class K, uint32_t Q, bool ALIGNED>
-__device__ __forceinline__ void unit_dispatch(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
-                                              uint32_t sh, uint32_t lane) {
-    if (cnt == K::CE * K::CH * stk::kWave) unit_full<K, Q, ALIGNED>(c, out, e0, sh, lane);
-    else unit_any<K, Q, ALIGNED>(c, out, e0, cnt, sh, lane);
+template <class K, bool ALIGNED>
+__device__ __forceinline__ void unit_dispatch(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+    if (cnt == K::CE * K::CH * stk::kWave) unit_full<K, ALIGNED>(c, e0, sh, lane);
+    else unit_any<K, ALIGNED>(c, e0, cnt, sh, lane);
 }
 
+// Aligned: the unit's source starts on an LG-byte boundary; otherwise sh = its offset within a
+// 4-byte word (0 for a 4-byte-aligned source that is not 16-byte aligned).
 template <class K>
-__device__ __forceinline__ void run_unit(const Ctx& c, uint16_t* __restrict__ out, uint64_t e0, uint32_t cnt,
-                                         uint32_t lane) {
-    const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)) & (K::LG - 1));
-    const uint32_t sh = r & 3u;
-    if (r == 0) return unit_dispatch<K, 0, true>(c, out, e0, cnt, sh, lane);
-    if constexpr (K::LG == 4) {
-        unit_dispatch<K, 0, false>(c, out, e0, cnt, sh, lane);
-    } else {
-        switch (r >> 2) {
-            case 0: unit_dispatch<K, 0, false>(c, out, e0, cnt, sh, lane); break;
-            case 1: unit_dispatch<K, 1, false>(c, out, e0, cnt, sh, lane); break;
-            case 2: unit_dispatch<K, 2, false>(c, out, e0, cnt, sh, lane); break;
-            default: unit_dispatch<K, 3, false>(c, out, e0, cnt, sh, lane); break;
-        }
-    }
+__device__ __forceinline__ void run_unit(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
+    const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)));
+    if ((a & (K::LG - 1)) == 0) unit_dispatch<K, true>(c, e0, cnt, 0, lane);
+    else unit_dispatch<K, false>(c, e0, cnt, a & 3u, lane);
 }
 
 // ------------------------------------------------------------------------- the kernel
@@ -427,7 +452,7 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     if (unit >= units) return;
     const uint32_t lane = threadIdx.x & (stk::kWave - 1);
 
-    // Header (magic, unit count) and this group's map entry, then the descriptor: the only loads
+    // Header (magic, unit count), this group's map entry, then the descriptor: the only loads
     // ahead of the data.  A table that does not match n is left alone before anything indexes it.
     const u32x4 hw = ld_uniform<u32x4>(table);
     if ((hw.x != ST_TABLE_MAGIC) | (hw.z != units) | (hw.w != 0)) return;
@@ -438,25 +463,18 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
 
     const uint64_t e0 = uint64_t(unit - D.unit_begin) << D.unit_shift;
     const uint32_t cnt = unit + 1 == D.unit_end ? D.tail : 1u << D.unit_shift;
-    uint16_t* out = ld_uniform<uint16_t*>(outs + D.out);
-    const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
-    if (oa & 1u) return;  // not a bf16 address: nothing is written
-
     Ctx c;
     c.blob = blob;
     c.D = D;
+    c.outs = outs;
     c.scale_al = (D.scale & 3u) == 0;
-    c.vec = (oa & 15u) == 0;  // otherwise every chunk takes the exact path
-    c.s = D.kind == ST_KIND_FP8_TENSOR ? ld_scalar_f32(blob + D.scale)
-        : D.kind == ST_KIND_NVFP4      ? ld_scalar_f32(blob + D.scale2)
-                                       : 0.0f;
     switch (D.kind) {
-        case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor>(c, out, e0, cnt, lane); break;
-        case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block>(c, out, e0, cnt, lane); break;
-        case ST_KIND_NVFP4: run_unit<KFp4>(c, out, e0, cnt, lane); break;
-        case ST_KIND_PASS_BF16: run_unit<KPass>(c, out, e0, cnt, lane); break;
-        case ST_KIND_CAST_F16: run_unit<KF16>(c, out, e0, cnt, lane); break;
-        default: run_unit<KF32>(c, out, e0, cnt, lane); break;
+        case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor>(c, e0, cnt, lane); break;
+        case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block>(c, e0, cnt, lane); break;
+        case ST_KIND_NVFP4: run_unit<KFp4>(c, e0, cnt, lane); break;
+        case ST_KIND_PASS_BF16: run_unit<KPass>(c, e0, cnt, lane); break;
+        case ST_KIND_CAST_F16: run_unit<KF16>(c, e0, cnt, lane); break;
+        default: run_unit<KF32>(c, e0, cnt, lane); break;
     }
 }
 
