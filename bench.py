@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--unit-scale", type=int, default=0)
+    ap.add_argument("--stream-chunk-mb", type=int, default=128, help="staging step of the overlapped load")
+    ap.add_argument("--load-reps", type=int, default=2, help="repetitions of the end-to-end load comparison")
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -187,12 +189,41 @@ def measure(k, d, args, rng, overrides=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = np.array([a.elapsed_time(b) for a, b in evs])
+    # end-to-end load, warm page cache: serial (stage everything, then one launch) against the
+    # overlapped pipeline (each staging step decoded while later steps are read and copied)
+    pinned = torch.empty(512 << 20, dtype=torch.uint8, pin_memory=True)
+    plan = st.StreamPlan(ix, args.stream_chunk_mb << 20)
+    ck.stream(path, stream=stream, plan=plan)  # allocates the pinned ring once
+    ck.synchronize()
+    serial_s, stream_s, sstats = [], [], None
+    for _ in range(args.load_reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st.stage_file(path, ix, ck.blob, pinned, side)
+        side.synchronize()
+        ck.materialize(stream)
+        torch.cuda.synchronize()
+        serial_s.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        sstats = ck.stream(path, stream=stream, plan=plan)
+        ck.synchronize()
+        stream_s.append(time.perf_counter() - t0)
+    del pinned
+    sok, schecked, sbad = sampled_parity(path, ix, ck, rng)
+    log(f"[bench] load: serial {min(serial_s):.3f}s, streamed {min(stream_s):.3f}s in {len(plan.steps)} steps "
+        f"({sstats['launches']} launches); streamed parity {'ok' if sok else 'MISMATCH in ' + str(sbad)}")
     res = {
         "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
         "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
         "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min()), "index_ms": index_ms,
         "stage": {"file_to_pinned_GBps": ix.data_size / read_s / 1e9 if read_s > 0 else None,
-                  "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)"},
+                  "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)",
+                  "serial_load_GBps": round(ix.data_size / min(serial_s) / 1e9, 2),
+                  "streamed_load_GBps": round(ix.data_size / min(stream_s) / 1e9, 2),
+                  "streamed_load_s": round(min(stream_s), 4), "serial_load_s": round(min(serial_s), 4),
+                  "stream_chunk_MiB": args.stream_chunk_mb, "stream_steps": len(plan.steps),
+                  "stream_launches": sstats["launches"],
+                  "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}"},
         "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
     }
     res["GBps"] = traffic / (res["ms_per_step"] * 1e-3) / 1e9

@@ -18,9 +18,11 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import DTYPES, KINDS, Desc, OutputInfo, PlanOpts, StError, TensorMeta, check, lib  # noqa: F401
+from ._lib import (DTYPES, KINDS, Desc, OutputInfo, PlanOpts, StError, StreamStats, StreamStep, TensorMeta,  # noqa: F401
+                   check, lib)
 
-__all__ = ["SafeTensorIndex", "DeviceCheckpoint", "load", "materialize", "stage_file", "StError", "KINDS"]
+__all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "load", "materialize", "stage_file", "stream_file",
+           "StError", "KINDS"]
 
 
 @dataclass(frozen=True)
@@ -159,6 +161,57 @@ class SafeTensorIndex:
         return dst.raw[: nb.value], units.value
 
 
+@dataclass(frozen=True)
+class StagingStep:
+    bytes: int
+    ranges: tuple       # ((begin, end), ...) of the data section
+    outputs: tuple      # output indices this step completes
+    table_offset: int   # byte offset of its work table in StreamPlan.tables
+    units: int          # work units of that table (0: nothing to decode)
+
+
+class StreamPlan:
+    """Staging steps of at most ``chunk_bytes`` over a checkpoint's data section, each with the
+    outputs it completes and their work table (st_stream_plan_build)."""
+
+    def __init__(self, index: SafeTensorIndex, chunk_bytes: int = 128 << 20):
+        h = C.c_void_p()
+        check(lib().st_stream_plan_build(index._h, chunk_bytes, C.byref(h)), "st_stream_plan_build")
+        self._h = h.value
+        self.index = index
+        L = lib()
+        self.chunk_bytes = L.st_stream_plan_chunk_bytes(self._h)
+        n = C.c_size_t()
+        p = L.st_stream_plan_order(self._h, C.byref(n))
+        self.order = [p[i] for i in range(n.value)]
+        p = L.st_stream_plan_ranges(self._h, C.byref(n))
+        ranges = [(p[i].begin, p[i].end, p[i].step) for i in range(n.value)]
+        self.ranges = [(b, e) for b, e, _ in ranges]
+        self.range_steps = [s for _, _, s in ranges]
+        nb = C.c_size_t()
+        tp = L.st_stream_plan_tables(self._h, C.byref(nb))
+        self.tables = C.string_at(tp, nb.value) if nb.value else b""
+        steps = []
+        for k in range(L.st_stream_plan_num_steps(self._h)):
+            st = StreamStep()
+            check(L.st_stream_plan_step(self._h, k, C.byref(st)), "st_stream_plan_step")
+            steps.append(StagingStep(st.bytes, tuple(self.ranges[st.first_range: st.first_range + st.n_ranges]),
+                                     tuple(self.order[st.first_out: st.first_out + st.n_out]), st.table_offset,
+                                     st.units))
+        self.steps = steps
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().st_stream_plan_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def _torch():
     import torch
     return torch
@@ -181,6 +234,21 @@ def materialize(blob, table, units: int, outs, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
     check(lib().st_materialize(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
                                C.c_void_p(outs.data_ptr()), C.c_void_p(s.cuda_stream)), "st_materialize")
+
+
+def stream_file(path: str, index: SafeTensorIndex, plan: StreamPlan, blob, tables, outs_plan, pinned, side_stream,
+                stream) -> dict:
+    """Read, copy and decode ``path`` step by step (st_stream_file).  ``tables``: device copy of
+    plan.tables; ``outs_plan``: device int64 pointers in plan order; ``pinned``: pinned uint8 host
+    tensor of at least 4 * plan.chunk_bytes.  Returns once everything is enqueued."""
+    st = StreamStats()
+    check(lib().st_stream_file(os.fsencode(path), index._h, plan._h, C.c_void_p(blob.data_ptr()),
+                               C.c_void_p(tables.data_ptr() if tables is not None else 0),
+                               C.c_void_p(outs_plan.data_ptr()), C.c_void_p(pinned.data_ptr()), pinned.numel(),
+                               C.c_void_p(side_stream.cuda_stream), C.c_void_p(stream.cuda_stream), None,
+                               C.byref(st)), "st_stream_file")
+    return {"seconds_read": st.seconds_read, "seconds_wait": st.seconds_wait, "bytes_read": st.bytes_read,
+            "steps": st.steps, "launches": st.launches}
 
 
 class DeviceCheckpoint:
@@ -223,6 +291,39 @@ class DeviceCheckpoint:
         side.synchronize()
         del pinned
 
+    def stream(self, path: str, chunk_mb: int = 128, stream=None, plan: StreamPlan | None = None) -> dict:
+        """Stage and decode ``path`` with the overlapped pipeline: each staging step's outputs are
+        decoded on ``stream`` (default: the current stream) while later steps are read and copied.
+        Returns the pipeline's statistics once everything is enqueued; the outputs are ready when
+        ``stream`` reaches this point (the pinned ring is held until then, see ``synchronize``)."""
+        torch = _torch()
+        plan = plan or StreamPlan(self.index, chunk_mb << 20)
+        compute = stream if stream is not None else torch.cuda.current_stream(self.device)
+        need = 4 * plan.chunk_bytes
+        if getattr(self, "_pinned", None) is None or self._pinned.numel() < need:
+            self._pinned = torch.empty(need, dtype=torch.uint8, pin_memory=True)
+        tables = (torch.frombuffer(bytearray(plan.tables), dtype=torch.uint8).to(self.device, non_blocking=False)
+                  if plan.tables else None)
+        order = torch.tensor(plan.order or [0], dtype=torch.int64, device=self.device)
+        outs_plan = self.outs[order] if plan.order else self.outs
+        side = torch.cuda.Stream(self.device)
+        compute.wait_stream(torch.cuda.current_stream(self.device))  # tables and outs_plan are ready
+        side.wait_stream(compute)  # earlier decodes of this blob are done before it is overwritten
+        for t in (tables, outs_plan):
+            if t is not None:
+                t.record_stream(compute)
+        stats = stream_file(path, self.index, plan, self.blob, tables, outs_plan, self._pinned, side, compute)
+        self._inflight = (plan, tables, outs_plan, side, compute)
+        return stats
+
+    def synchronize(self):
+        """Wait for a streamed load and release its transient buffers (the pinned ring is kept)."""
+        inflight = getattr(self, "_inflight", None)
+        if inflight:
+            inflight[4].synchronize()
+            inflight[3].synchronize()
+            self._inflight = None
+
     def load_bytes(self, data_section: bytes):
         """Stage from bytes already in host memory (tests): the data section only."""
         torch = _torch()
@@ -237,10 +338,18 @@ class DeviceCheckpoint:
         return self.tensors
 
 
-def load(path: str, device="cuda", unit_log2_scale: int = 0) -> dict:
-    """Every output of the checkpoint at ``path`` as a bf16 tensor on ``device``."""
+def load(path: str, device="cuda", unit_log2_scale: int = 0, streamed: bool = True, chunk_mb: int = 128) -> dict:
+    """Every output of the checkpoint at ``path`` as a bf16 tensor on ``device``.  By default the
+    overlapped pipeline decodes each staging step while later steps are read and copied;
+    ``streamed=False`` stages the whole data section first and then decodes it in one launch."""
     idx = SafeTensorIndex.open(path, unit_log2_scale)
-    ck = DeviceCheckpoint(idx, path, device)
+    ck = DeviceCheckpoint(idx, None, device)
+    if streamed:
+        ck.stream(path, chunk_mb=chunk_mb)
+        ck.synchronize()
+        ck._pinned = None
+        return ck.tensors
+    ck.stage(path)
     out = ck.materialize()
     _torch().cuda.current_stream(ck.device).synchronize()
     return out

@@ -49,6 +49,23 @@ class PlanOpts(C.Structure):
     _fields_ = [("unit_log2_scale", C.c_uint32), ("flags", C.c_uint32)]
 
 
+class StreamRange(C.Structure):
+    _fields_ = [("begin", C.c_uint64), ("end", C.c_uint64), ("step", C.c_uint32), ("reserved", C.c_uint32)]
+
+
+class StreamStep(C.Structure):
+    _fields_ = [("bytes", C.c_uint64), ("first_range", C.c_uint32), ("n_ranges", C.c_uint32),
+                ("first_out", C.c_uint32), ("n_out", C.c_uint32), ("table_offset", C.c_uint64), ("units", C.c_uint64)]
+
+
+class StreamStats(C.Structure):
+    _fields_ = [("seconds_read", C.c_double), ("seconds_wait", C.c_double), ("bytes_read", C.c_uint64),
+                ("steps", C.c_uint32), ("launches", C.c_uint32)]
+
+
+assert C.sizeof(StreamRange) == 24 and C.sizeof(StreamStep) == 40 and C.sizeof(StreamStats) == 32
+
+
 # name -> (restype, argtypes); the full list of exported symbols the header declares.
 SIGNATURES = {
     "st_last_error": (C.c_char_p, []),
@@ -75,6 +92,16 @@ SIGNATURES = {
     "st_stage_file": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                                 C.POINTER(C.c_double)]),
     "st_materialize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "st_stream_plan_build": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p)]),
+    "st_stream_plan_free": (None, [C.c_void_p]),
+    "st_stream_plan_chunk_bytes": (C.c_uint64, [C.c_void_p]),
+    "st_stream_plan_num_steps": (C.c_size_t, [C.c_void_p]),
+    "st_stream_plan_step": (C.c_int, [C.c_void_p, C.c_size_t, C.POINTER(StreamStep)]),
+    "st_stream_plan_ranges": (C.POINTER(StreamRange), [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "st_stream_plan_order": (C.POINTER(C.c_uint32), [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "st_stream_plan_tables": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "st_stream_file": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(StreamStats)]),
 }
 
 _lib = None

@@ -40,7 +40,7 @@ def build(verbose: bool = False, extra_device_flags=(), out: str = LIB, defines=
     dflags = [f"-D{d}" for d in defines]
     objs = []
     # host-only sources
-    for src in ("index.cpp",):
+    for src in ("index.cpp", "stream_plan.cpp"):
         o = os.path.join(build_dir, src + ".o")
         _run(["g++", "-O2", *COMMON, *dflags, "-c", os.path.join(CSRC, src), "-o", o], verbose)
         objs.append(o)

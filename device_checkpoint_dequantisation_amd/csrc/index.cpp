@@ -23,6 +23,7 @@
 #include <utility>
 #include <vector>
 
+#include "index_impl.h"
 #include "st_internal.h"
 
 // ---------------------------------------------------------------------------------- errors
@@ -42,8 +43,12 @@ st_status st_fail(st_status code, const char* fmt, ...) {
 }
 
 static void st_clear() { g_err.clear(); }
+void sti::clear_error() { st_clear(); }
 
 namespace {
+
+using sti::Output;
+using sti::Tensor;
 
 // ---------------------------------------------------------------------------------- dtypes
 
@@ -298,22 +303,6 @@ class JsonReader {
 
 // ---------------------------------------------------------------------------------- index
 
-struct Tensor {
-    std::string name;
-    int dtype;
-    std::vector<int64_t> shape;
-    uint64_t begin, end;
-    uint64_t numel;
-};
-
-struct Output {
-    uint32_t tensor;
-    int64_t scale = -1, scale2 = -1;
-    st_kind kind;
-    std::vector<int64_t> shape;
-    uint64_t numel;
-};
-
 bool ends_with(const std::string& s, const char* suf) {
     size_t n = strlen(suf);
     return s.size() >= n && memcmp(s.data() + s.size() - n, suf, n) == 0;
@@ -337,19 +326,6 @@ uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-struct st_index {
-    uint64_t header_len = 0;   // N
-    uint64_t data_size = 0;
-    std::string metadata_json = "{}";
-    std::vector<Tensor> tensors;
-    std::unordered_map<std::string, uint32_t> by_name;
-    std::vector<Output> outputs;
-    std::vector<uint64_t> out_offset;  // arena offsets
-    uint64_t arena_bytes = 0;
-    std::vector<unsigned char> table;  // header + descriptors + unit map
-    uint64_t total_units = 0;
-    uint32_t unit_log2_scale = 0;
-};
 
 namespace {
 
@@ -420,7 +396,7 @@ st_status parse_entries(st_index& ix, const JVal& root) {
         }
         if (of->t != JVal::Arr || of->a.size() != 2)
             return st_fail(ST_E_OFFSETS, "%s: data_offsets must be two non-negative integers", name.c_str());
-        int64_t b, e;
+        int64_t b = 0, e = 0;
         if (read_int(of->a[0], name, "data_offsets", b) || read_int(of->a[1], name, "data_offsets", e))
             return st_fail(ST_E_OFFSETS, "%s: data_offsets must be two non-negative integers", name.c_str());
         if (b > e) return st_fail(ST_E_OFFSETS, "%s: data_offsets begin %lld > end %lld", name.c_str(), (long long)b, (long long)e);
@@ -596,9 +572,11 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     return d;
 }
 
+}  // namespace
+
 // Work table for outputs sel[0..k): header, descriptors (descriptor j writes outs[j]) and the
 // map from each group of ST_UNITS_PER_GROUP units to the descriptor holding its first unit.
-std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out) {
+std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out) {
     std::vector<st_desc> descs(k);
     std::vector<uint64_t> units(k);
     uint64_t pos = 0;
@@ -630,6 +608,8 @@ std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, 
     return t;
 }
 
+namespace {
+
 st_status plan(st_index& ix) {
     if (ix.outputs.size() >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "more than 2^32 outputs");
     uint64_t pos = 0;
@@ -642,7 +622,7 @@ st_status plan(st_index& ix) {
     std::vector<uint32_t> all(ix.outputs.size());
     for (size_t k = 0; k < all.size(); ++k) all[k] = uint32_t(k);
     try {
-        ix.table = build_table(ix, all.data(), all.size(), &ix.total_units);
+        ix.table = sti::build_table(ix, all.data(), all.size(), &ix.total_units);
     } catch (const std::length_error&) {
         return st_fail(ST_E_SHAPE, "checkpoint needs 2^32 or more work units");
     }
@@ -826,7 +806,7 @@ extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* 
     uint64_t u = 0;
     std::vector<unsigned char> t;
     try {
-        t = build_table(*idx, sel, k, &u);
+        t = sti::build_table(*idx, sel, k, &u);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
     } catch (const std::length_error&) {

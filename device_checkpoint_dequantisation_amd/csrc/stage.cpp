@@ -2,10 +2,14 @@
 //
 // The pages ("Disk tier safetensors streaming design audit", "Strategy summary / Range reads
 // and tiering") read only a tensor's byte range into (optionally pinned) host memory, copy it
-// to the GPU and release the host buffer.  Here the whole data section is one range: it is read
-// in chunks by a few threads into a ring carved from the caller's pinned buffer, and each chunk
-// is copied with hipMemcpyAsync on a side stream while the next chunk is being read.  An event
-// per ring slot keeps a slot from being overwritten before its copy has finished.
+// to the GPU and release the host buffer.  Byte ranges are read by a few threads into a ring
+// carved from the caller's pinned buffer, and each slot is copied with hipMemcpyAsync on a side
+// stream while the next one is being read.  An event per ring slot keeps a slot from being
+// overwritten before its copy has finished.
+//  * st_stage_file: the whole data section, in slot-sized chunks.
+//  * st_stream_file: the steps of a stream plan; after each step's copies the compute stream waits
+//    for them and decodes the outputs the step completes, so decoding overlaps later reads and
+//    copies.
 #include <fcntl.h>
 #include <sys/stat.h>
 #include <unistd.h>
@@ -15,98 +19,287 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <condition_variable>
+#include <mutex>
 #include <thread>
 #include <vector>
 
+#include "index_impl.h"
 #include "st_internal.h"
 
 namespace {
 
 constexpr size_t kMinPinned = size_t(2) << 20;
 constexpr int kSlots = 4;
-constexpr int kReaders = 8;
+#ifndef ST_READERS
+#define ST_READERS 8
+#endif
+constexpr int kReaders = ST_READERS;  // pool threads; the calling thread reads too
 
-// Reads [off, off + len) of fd into dst with `kReaders` threads; false on a short read.
-bool read_range(int fd, char* dst, uint64_t off, size_t len) {
-    std::atomic<bool> ok{true};
-    auto piece = [&](size_t b, size_t e) {
-        while (b < e) {
-            ssize_t r = pread(fd, dst + b, e - b, off_t(off + b));
-            if (r <= 0) { ok = false; return; }
-            b += size_t(r);
-        }
-    };
-    const size_t min_piece = size_t(4) << 20;
-    int nt = int(std::min<size_t>(kReaders, std::max<size_t>(1, len / min_piece)));
-    if (nt == 1) {
-        piece(0, len);
-        return ok;
+struct Piece {
+    char* dst;
+    uint64_t off;  // file offset
+    size_t len;
+};
+
+// Reader threads for one staging call.  read() splits a batch of ranges into pieces and reads
+// them with pread on the pool's threads and the calling thread; every thread takes part in every
+// batch, so a batch is over once all of them have checked in.
+class ReaderPool {
+  public:
+    explicit ReaderPool(int fd) : fd_(fd) {
+        for (int i = 0; i < kReaders; ++i) threads_.emplace_back([this] { worker(); });
     }
-    std::vector<std::thread> th;
-    size_t step = (len + size_t(nt) - 1) / size_t(nt);
-    step = (step + 4095) & ~size_t(4095);
-    for (size_t b = 0; b < len; b += step) th.emplace_back(piece, b, std::min(len, b + step));
-    for (auto& t : th) t.join();
-    return ok;
+    ~ReaderPool() {
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& t : threads_) t.join();
+    }
+    // False if a read failed or hit the end of the file.
+    bool read(const std::vector<Piece>& ranges) {
+        size_t total = 0;
+        for (const Piece& r : ranges) total += r.len;
+        const size_t piece = std::max<size_t>(size_t(1) << 20, (total / (2 * (kReaders + 1)) + 4095) & ~size_t(4095));
+        std::vector<Piece> pieces;
+        for (const Piece& r : ranges)
+            for (size_t b = 0; b < r.len; b += piece)
+                pieces.push_back(Piece{r.dst + b, r.off + b, std::min(piece, r.len - b)});
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            pieces_.swap(pieces);
+            next_.store(0);
+            ok_.store(true);
+            checked_in_ = 0;
+            ++gen_;
+        }
+        cv_.notify_all();
+        drain();
+        std::unique_lock<std::mutex> lk(m_);
+        done_cv_.wait(lk, [this] { return checked_in_ == threads_.size(); });
+        return ok_.load();
+    }
+
+  private:
+    void drain() {
+        for (size_t i = next_.fetch_add(1); i < pieces_.size(); i = next_.fetch_add(1)) {
+            const Piece& p = pieces_[i];
+            size_t b = 0;
+            while (b < p.len) {
+                const ssize_t r = pread(fd_, p.dst + b, p.len - b, off_t(p.off + b));
+                if (r <= 0) {
+                    ok_.store(false);
+                    break;
+                }
+                b += size_t(r);
+            }
+        }
+    }
+    void worker() {
+        uint64_t seen = 0;
+        std::unique_lock<std::mutex> lk(m_);
+        for (;;) {
+            cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+            if (stop_) return;
+            seen = gen_;
+            lk.unlock();
+            drain();
+            lk.lock();
+            if (++checked_in_ == threads_.size()) done_cv_.notify_all();
+        }
+    }
+
+    int fd_;
+    std::vector<std::thread> threads_;
+    std::mutex m_;
+    std::condition_variable cv_, done_cv_;
+    std::vector<Piece> pieces_;   // written only while every thread is idle
+    std::atomic<size_t> next_{0};
+    std::atomic<bool> ok_{true};
+    size_t checked_in_ = 0;
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+};
+
+// An open file descriptor, closed on scope exit.
+struct FileFd {
+    int fd = -1;
+    ~FileFd() {
+        if (fd >= 0) close(fd);
+    }
+};
+
+// Opens `path` and checks that its size is what the index expects.
+st_status open_checked(const char* path, const st_index* idx, FileFd& f) {
+    const uint64_t want = st_index_data_offset(idx) + st_index_data_size(idx);
+    f.fd = open(path, O_RDONLY | O_CLOEXEC);
+    if (f.fd < 0) return st_fail(ST_E_IO, "cannot open %s", path);
+    struct stat sb;
+    if (fstat(f.fd, &sb) != 0 || uint64_t(sb.st_size) != want)
+        return st_fail(ST_E_IO, "%s is %lld bytes, the index expects %llu", path, (long long)sb.st_size,
+                       (unsigned long long)want);
+    return ST_OK;
+}
+
+struct RingEvents {
+    hipEvent_t ev[kSlots];
+    int n = 0;
+    st_status create() {
+        for (; n < kSlots; ++n)
+            if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) != hipSuccess)
+                return st_fail(ST_E_HIP, "hipEventCreate failed");
+        return ST_OK;
+    }
+    ~RingEvents() {
+        for (int k = 0; k < n; ++k) (void)hipEventDestroy(ev[k]);
+    }
+};
+
+double seconds_since(std::chrono::steady_clock::time_point t0) {
+    return std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
 }
 
 }  // namespace
 
 extern "C" st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, void* pinned,
                                    size_t pinned_bytes, void* side_stream, void* done_event, double* seconds_read) {
+    if (seconds_read) *seconds_read = 0;
     if (!path || !idx || !blob_dev || !pinned) return st_fail(ST_E_ARG, "st_stage_file: null pointer");
     if (pinned_bytes < kMinPinned)
         return st_fail(ST_E_ARG, "st_stage_file: pinned buffer of %zu bytes, at least %zu needed", pinned_bytes, kMinPinned);
     if (reinterpret_cast<uintptr_t>(blob_dev) % ST_BLOB_ALIGN)
         return st_fail(ST_E_ARG, "st_stage_file: blob is not %d-byte aligned", ST_BLOB_ALIGN);
     const uint64_t off0 = st_index_data_offset(idx), size = st_index_data_size(idx);
-    int fd = open(path, O_RDONLY | O_CLOEXEC);
-    if (fd < 0) return st_fail(ST_E_IO, "cannot open %s", path);
-    struct stat sb;
-    if (fstat(fd, &sb) != 0 || uint64_t(sb.st_size) != off0 + size) {
-        close(fd);
-        return st_fail(ST_E_IO, "%s is %lld bytes, the index expects %llu", path, (long long)sb.st_size,
-                       (unsigned long long)(off0 + size));
-    }
+    FileFd file;
+    st_status status = open_checked(path, idx, file);
+    if (status != ST_OK) return status;
+    RingEvents ring;
+    if ((status = ring.create()) != ST_OK) return status;
+    ReaderPool pool(file.fd);
     hipStream_t stream = static_cast<hipStream_t>(side_stream);
-    size_t chunk = (pinned_bytes / kSlots) & ~size_t(4095);
-    hipEvent_t ev[kSlots];
-    for (int s = 0; s < kSlots; ++s)
-        if (hipEventCreateWithFlags(&ev[s], hipEventDisableTiming) != hipSuccess) {
-            for (int k = 0; k < s; ++k) (void)hipEventDestroy(ev[k]);
-            close(fd);
-            return st_fail(ST_E_HIP, "st_stage_file: hipEventCreate failed");
-        }
-    st_status status = ST_OK;
+    const size_t chunk = (pinned_bytes / kSlots) & ~size_t(4095);
     double t_read = 0;
     uint64_t done = 0;
     for (uint64_t i = 0; done < size; ++i) {
-        int s = int(i % kSlots);
+        const int s = int(i % kSlots);
         char* slot = static_cast<char*>(pinned) + size_t(s) * chunk;
-        size_t len = size_t(std::min<uint64_t>(chunk, size - done));
-        if (i >= kSlots && hipEventSynchronize(ev[s]) != hipSuccess) {
+        const size_t len = size_t(std::min<uint64_t>(chunk, size - done));
+        if (i >= kSlots && hipEventSynchronize(ring.ev[s]) != hipSuccess) {
             status = st_fail(ST_E_HIP, "st_stage_file: waiting for a staging copy failed");
             break;
         }
         auto t0 = std::chrono::steady_clock::now();
-        bool ok = read_range(fd, slot, off0 + done, len);
-        t_read += std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+        const bool ok = pool.read({Piece{slot, off0 + done, len}});
+        t_read += seconds_since(t0);
         if (!ok) {
             status = st_fail(ST_E_IO, "read of %s failed at byte %llu", path, (unsigned long long)(off0 + done));
             break;
         }
         if (hipMemcpyAsync(static_cast<char*>(blob_dev) + done, slot, len, hipMemcpyHostToDevice, stream) != hipSuccess ||
-            hipEventRecord(ev[s], stream) != hipSuccess) {
+            hipEventRecord(ring.ev[s], stream) != hipSuccess) {
             status = st_fail(ST_E_HIP, "st_stage_file: hipMemcpyAsync of %zu bytes failed", len);
             break;
         }
         done += len;
     }
-    close(fd);
     if (status == ST_OK && done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), stream) != hipSuccess)
         status = st_fail(ST_E_HIP, "st_stage_file: hipEventRecord failed");
     if (status != ST_OK) (void)hipStreamSynchronize(stream);  // nothing may still read the ring
-    for (int s = 0; s < kSlots; ++s) (void)hipEventDestroy(ev[s]);
     if (seconds_read) *seconds_read = t_read;
+    return status;
+}
+
+extern "C" st_status st_stream_file(const char* path, const st_index* idx, const st_stream_plan* plan, void* blob_dev,
+                                    const void* tables_dev, void* const* outs_dev, void* pinned, size_t pinned_bytes,
+                                    void* side_stream, void* compute_stream, void* done_event, st_stream_stats* stats) {
+    if (stats) *stats = st_stream_stats{};
+    if (!path || !idx || !plan || !blob_dev || !pinned) return st_fail(ST_E_ARG, "st_stream_file: null pointer");
+    if (!st_stream_plan_of(plan, idx)) return st_fail(ST_E_ARG, "st_stream_file: the plan was built from another index");
+    const uint64_t chunk = st_stream_plan_chunk_bytes(plan);
+    if (pinned_bytes / kSlots < chunk)
+        return st_fail(ST_E_ARG, "st_stream_file: pinned buffer of %zu bytes, %d chunks of %llu bytes needed", pinned_bytes,
+                       kSlots, (unsigned long long)chunk);
+    if (reinterpret_cast<uintptr_t>(blob_dev) % ST_BLOB_ALIGN)
+        return st_fail(ST_E_ARG, "st_stream_file: blob is not %d-byte aligned", ST_BLOB_ALIGN);
+    size_t table_bytes = 0, n_order = 0, n_ranges = 0;
+    (void)st_stream_plan_tables(plan, &table_bytes);
+    (void)st_stream_plan_order(plan, &n_order);
+    const st_stream_range* ranges = st_stream_plan_ranges(plan, &n_ranges);
+    if (table_bytes && (!tables_dev || reinterpret_cast<uintptr_t>(tables_dev) % 64))
+        return st_fail(ST_E_ARG, "st_stream_file: tables_dev is null or not 64-byte aligned");
+    if (n_order && !outs_dev) return st_fail(ST_E_ARG, "st_stream_file: outs_dev is null");
+
+    const uint64_t off0 = st_index_data_offset(idx);
+    FileFd file;
+    st_status status = open_checked(path, idx, file);
+    if (status != ST_OK) return status;
+    RingEvents ring;
+    if ((status = ring.create()) != ST_OK) return status;
+    ReaderPool pool(file.fd);
+    std::vector<Piece> batch;
+    hipStream_t side = static_cast<hipStream_t>(side_stream), compute = static_cast<hipStream_t>(compute_stream);
+    st_stream_stats st{};
+    const size_t nsteps = st_stream_plan_num_steps(plan);
+    for (size_t s = 0; status == ST_OK && s < nsteps; ++s) {
+        st_stream_step step;
+        (void)st_stream_plan_step(plan, s, &step);
+        const int slot_id = int(s % kSlots);
+        char* slot = static_cast<char*>(pinned) + size_t(slot_id) * chunk;
+        if (step.bytes) {
+            if (s >= size_t(kSlots)) {
+                auto t0 = std::chrono::steady_clock::now();
+                if (hipEventSynchronize(ring.ev[slot_id]) != hipSuccess) {
+                    status = st_fail(ST_E_HIP, "st_stream_file: waiting for a staging copy failed");
+                    break;
+                }
+                st.seconds_wait += seconds_since(t0);
+            }
+            size_t pos = 0;
+            batch.clear();
+            for (uint32_t r = step.first_range; r < step.first_range + step.n_ranges && r < n_ranges; ++r) {
+                const size_t len = size_t(ranges[r].end - ranges[r].begin);
+                batch.push_back(Piece{slot + pos, off0 + ranges[r].begin, len});
+                pos += len;
+            }
+            auto t0 = std::chrono::steady_clock::now();
+            if (!pool.read(batch))
+                status = st_fail(ST_E_IO, "read of %s failed in step %zu", path, s);
+            st.seconds_read += seconds_since(t0);
+            if (status != ST_OK) break;
+            pos = 0;
+            for (uint32_t r = step.first_range; r < step.first_range + step.n_ranges && r < n_ranges; ++r) {
+                const size_t len = size_t(ranges[r].end - ranges[r].begin);
+                if (hipMemcpyAsync(static_cast<char*>(blob_dev) + ranges[r].begin, slot + pos, len, hipMemcpyHostToDevice,
+                                   side) != hipSuccess) {
+                    status = st_fail(ST_E_HIP, "st_stream_file: hipMemcpyAsync of %zu bytes failed", len);
+                    break;
+                }
+                pos += len;
+            }
+            if (status != ST_OK) break;
+            if (hipEventRecord(ring.ev[slot_id], side) != hipSuccess) {
+                status = st_fail(ST_E_HIP, "st_stream_file: hipEventRecord failed");
+                break;
+            }
+            st.bytes_read += pos;
+            ++st.steps;
+        }
+        if (step.units) {
+            if (step.bytes && hipStreamWaitEvent(compute, ring.ev[slot_id], 0) != hipSuccess) {
+                status = st_fail(ST_E_HIP, "st_stream_file: hipStreamWaitEvent failed");
+                break;
+            }
+            status = st_materialize(blob_dev, static_cast<const char*>(tables_dev) + step.table_offset, size_t(step.units),
+                                    outs_dev + step.first_out, compute_stream);
+            if (status != ST_OK) break;
+            ++st.launches;
+        }
+    }
+    if (status == ST_OK && done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), compute) != hipSuccess)
+        status = st_fail(ST_E_HIP, "st_stream_file: hipEventRecord failed");
+    if (status != ST_OK) (void)hipStreamSynchronize(side);  // nothing may still read the ring
+    if (stats) *stats = st;
     return status;
 }

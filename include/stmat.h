@@ -15,6 +15,7 @@
  *
  *   st_index_build / st_index_open   header bytes -> index (host, metadata only)
  *   st_stage_file                    file byte ranges -> pinned ring -> device blob (side stream)
+ *   st_stream_plan_build/st_stream_file  staging steps, each decoded as soon as its bytes land
  *   st_materialize                   device blob + work table -> bf16 outputs (one launch)
  *
  * Output element values (bit-exact definition; rounding is IEEE binary32 round-to-nearest-even
@@ -218,6 +219,76 @@ st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t
 st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, void* pinned,
                         size_t pinned_bytes, void* side_stream, void* done_event,
                         double* seconds_read);
+
+/* ---- Overlapped streaming: range reads, copies and decoding in flight together ----------------
+ * The pages' disk tier reads only the byte ranges a load needs into pinned host memory, copies
+ * them to the GPU and then releases the host buffer ("Disk tier safetensors streaming design
+ * audit", "Strategy summary / Range reads and tiering").  A stream plan cuts the data section
+ * into staging steps of at most chunk_bytes.  Each step carries a work table for the outputs
+ * whose weight and scale bytes have all been copied once the step's copies are done.
+ * st_stream_file reads, copies and decodes step by step, so decoding overlaps the reads and copies
+ * of later steps.  Bytes are staged in file order, except that a scale tensor lying more than one
+ * chunk past the end of its weight is staged first (checkpoints that keep all scales at the end). */
+
+typedef struct st_stream_plan st_stream_plan;  /* opaque, host memory, library-owned */
+
+typedef struct {
+    uint64_t begin, end;    /* bytes [begin, end) of the data section */
+    uint32_t step;          /* the staging step that copies them */
+    uint32_t reserved;
+} st_stream_range;
+
+typedef struct {
+    uint64_t bytes;         /* bytes this step copies */
+    uint32_t first_range;   /* its ranges: st_stream_plan_ranges()[first_range .. + n_ranges) */
+    uint32_t n_ranges;
+    uint32_t first_out;     /* outputs it completes: st_stream_plan_order()[first_out .. + n_out) */
+    uint32_t n_out;
+    uint64_t table_offset;  /* byte offset of its work table in st_stream_plan_tables (64-B aligned) */
+    uint64_t units;         /* that table's work-unit count; 0 = nothing to decode */
+} st_stream_step;
+
+/* Plan the streaming load of `idx` in steps of at most chunk_bytes (>= 64 KiB).  Every byte of
+ * the data section belongs to exactly one range; every output to exactly one step. */
+st_status st_stream_plan_build(const st_index* idx, uint64_t chunk_bytes, st_stream_plan** out);
+void      st_stream_plan_free(st_stream_plan* plan);
+uint64_t  st_stream_plan_chunk_bytes(const st_stream_plan* plan);
+size_t    st_stream_plan_num_steps(const st_stream_plan* plan);
+st_status st_stream_plan_step(const st_stream_plan* plan, size_t s, st_stream_step* out);
+/* All ranges, step-major; valid for the plan's lifetime. */
+const st_stream_range* st_stream_plan_ranges(const st_stream_plan* plan, size_t* n);
+/* Output indices in plan order (step-major); entry j of the `outs_dev` array passed to
+ * st_stream_file must point to output order[j]. */
+const uint32_t* st_stream_plan_order(const st_stream_plan* plan, size_t* n);
+/* Every step's work table, concatenated (host memory; upload once to a 64-byte aligned device
+ * buffer for st_stream_file). */
+const void* st_stream_plan_tables(const st_stream_plan* plan, size_t* bytes);
+
+typedef struct {
+    double seconds_read;    /* wall time in file reads */
+    double seconds_wait;    /* wall time waiting for a ring slot's previous copy */
+    uint64_t bytes_read;
+    uint32_t steps;         /* steps staged */
+    uint32_t launches;      /* st_materialize launches enqueued */
+} st_stream_stats;
+
+/* Stream the file at `path` through `plan`: for each step, read its ranges into a slot of the
+ * pinned ring (pinned_bytes >= 4 * chunk_bytes; four slots), copy them into `blob_dev` with
+ * hipMemcpyAsync on `side_stream`, make `compute_stream` wait for those copies and enqueue
+ * st_materialize over the step's table on `compute_stream`.
+ *   blob_dev    st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned (as for st_stage_file)
+ *   tables_dev  device copy of st_stream_plan_tables, 64-byte aligned
+ *   outs_dev    device array of output pointers in plan order (see st_stream_plan_order)
+ *   done_event  (may be NULL) recorded on compute_stream after the last launch: once it has
+ *               completed, every output is decoded and the pinned buffer is free.
+ * Returns once every read is done and every copy and launch is enqueued.  The library allocates no
+ * device memory and synchronises no stream (it waits on its own ring events before reusing a
+ * slot).  Errors: ST_E_ARG (null pointers, pinned buffer too small, plan of another index,
+ * misaligned buffers), ST_E_IO (open, size or read failure), ST_E_HIP (a copy, event or launch);
+ * after an error the side stream has been synchronised so the ring is no longer read. */
+st_status st_stream_file(const char* path, const st_index* idx, const st_stream_plan* plan, void* blob_dev,
+                         const void* tables_dev, void* const* outs_dev, void* pinned, size_t pinned_bytes,
+                         void* side_stream, void* compute_stream, void* done_event, st_stream_stats* stats);
 
 /* Enqueue the grouped materialise kernel on `stream` (hipStream_t; NULL = default stream).
  *   blob   device copy of the data section (st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned)

@@ -185,7 +185,8 @@ def test_staging_from_file_matches_bytes(tmp_path):
     ck = st.DeviceCheckpoint(ix, str(p), DEV, pinned_mb=2)
     host = ck.blob[: ix.data_size].cpu().numpy().tobytes()
     assert host == buf[ix.data_offset:]
-    out = st.load(str(p), DEV)
     want = oracle.materialize(buf)
-    for name, w in want.items():
-        assert np.array_equal(out[name].view(torch.int16).cpu().numpy().view(np.uint16), w), name
+    for streamed in (True, False):
+        out = st.load(str(p), DEV, streamed=streamed)
+        for name, w in want.items():
+            assert np.array_equal(out[name].view(torch.int16).cpu().numpy().view(np.uint16), w), (streamed, name)
