@@ -78,6 +78,7 @@ def parse():
     ap.add_argument("--unit-scale", type=int, default=0)
     ap.add_argument("--stream-chunk-mb", type=int, default=128, help="staging step of the overlapped load")
     ap.add_argument("--load-reps", type=int, default=2, help="repetitions of the end-to-end load comparison")
+    ap.add_argument("--no-lazy", action="store_true", help="skip the on-demand (per-layer) load measurement")
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -233,6 +234,36 @@ def measure(k, d, args, rng, overrides=None):
     return res
 
 
+def lazy_loads(path, dev):
+    """On-demand loads through StreamStateDict, one layer (keys sharing their first two name
+    components) per load: without a RAM tier, filling it, and served from it."""
+    import torch
+    import device_checkpoint_dequantisation_amd as st
+    probe = st.StreamStateDict(path, dev)
+    groups = {}
+    for k in probe:
+        groups.setdefault(".".join(k.split(".")[:2]), []).append(k)
+    src = sum(probe.meta(k).source_bytes for k in probe)
+    res = {"layers": len(groups), "source_bytes": src}
+    for label, ram in (("file", 0), ("file_into_ram", 1 << 40), ("ram", None)):
+        if ram is not None:
+            sd = st.StreamStateDict(path, dev, ram_cache_bytes=ram, index=probe.index)
+        before = dict(sd.stats)
+        torch.cuda.synchronize()
+        times = []
+        for keys in groups.values():
+            t0 = time.perf_counter()
+            got = sd.load(keys)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            del got
+        res[label] = {"GBps": round(src / sum(times) / 1e9, 2), "ms_per_layer_mean": round(1e3 * float(np.mean(times)), 3),
+                      "ms_per_layer_max": round(1e3 * float(np.max(times)), 3),
+                      "launches": int(sd.stats["launches"] - before.get("launches", 0)),
+                      "ram_hits": int(sd.stats["ram_hits"] - before.get("ram_hits", 0))}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +277,9 @@ def main():
     cpu = None
     for k in configs:
         results[k] = measure(k, d, args, rng)
+        if k == args.config and not args.no_lazy:
+            results[k]["lazy"] = lazy_loads(results[k]["path"], "cuda:0")
+            log(f"[bench] lazy per-layer loads: {results[k]['lazy']}")
         if k == args.config and not args.no_cpu:
             cpu = cpu_baseline(results[k]["path"], args.cpu_seconds)
             log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
@@ -279,6 +313,8 @@ def main():
                       "min": round(r["kernel_ms_min"], 4)},
         "staging": r["stage"], "index_build_ms": round(r["index_ms"], 2), "parity": r["parity"],
     }
+    if "lazy" in r:
+        line["lazy_loads"] = r["lazy"]
     if aligned is not None:
         line["scaled_fp8_all_weights_16B_aligned"] = {"GBps": round(aligned["GBps"], 2),
                                                       "kernel_ms_mean": round(aligned["kernel_ms_mean"], 4),

@@ -18,11 +18,11 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import (DTYPES, KINDS, Desc, OutputInfo, PlanOpts, StError, StreamStats, StreamStep, TensorMeta,  # noqa: F401
-                   check, lib)
+from ._lib import (DTYPES, KINDS, PLAN_PACK, Desc, OutputInfo, PlanOpts, StError, StreamStats, StreamStep,  # noqa: F401
+                   TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "load", "materialize", "stage_file", "stream_file",
-           "StError", "KINDS"]
+           "read_plans", "StError", "KINDS"]
 
 
 @dataclass(frozen=True)
@@ -171,23 +171,35 @@ class StagingStep:
 
 
 class StreamPlan:
-    """Staging steps of at most ``chunk_bytes`` over a checkpoint's data section, each with the
-    outputs it completes and their work table (st_stream_plan_build)."""
+    """Staging steps of at most ``chunk_bytes`` over a checkpoint's bytes, each with the outputs it
+    completes and their work table.  ``select=None`` plans every output, laid out like the data
+    section (st_stream_plan_build); a list of output indices plans those only
+    (st_stream_plan_select), in a compact blob if ``pack``."""
 
-    def __init__(self, index: SafeTensorIndex, chunk_bytes: int = 128 << 20):
+    def __init__(self, index: SafeTensorIndex, chunk_bytes: int = 128 << 20, select=None, pack: bool = False):
         h = C.c_void_p()
-        check(lib().st_stream_plan_build(index._h, chunk_bytes, C.byref(h)), "st_stream_plan_build")
+        if select is None:
+            if pack:
+                raise ValueError("pack needs a selection of outputs")
+            check(lib().st_stream_plan_build(index._h, chunk_bytes, C.byref(h)), "st_stream_plan_build")
+        else:
+            sel = list(select)
+            arr = (C.c_uint32 * max(1, len(sel)))(*sel)
+            check(lib().st_stream_plan_select(index._h, arr, len(sel), chunk_bytes, PLAN_PACK if pack else 0,
+                                              C.byref(h)), "st_stream_plan_select")
         self._h = h.value
         self.index = index
+        self.packed = bool(pack)
         L = lib()
         self.chunk_bytes = L.st_stream_plan_chunk_bytes(self._h)
+        self.blob_bytes = L.st_stream_plan_blob_bytes(self._h)
         n = C.c_size_t()
         p = L.st_stream_plan_order(self._h, C.byref(n))
         self.order = [p[i] for i in range(n.value)]
         p = L.st_stream_plan_ranges(self._h, C.byref(n))
-        ranges = [(p[i].begin, p[i].end, p[i].step) for i in range(n.value)]
-        self.ranges = [(b, e) for b, e, _ in ranges]
-        self.range_steps = [s for _, _, s in ranges]
+        self.ranges = [(p[i].begin, p[i].end) for i in range(n.value)]
+        self.range_dsts = [p[i].dst for i in range(n.value)]
+        self.range_steps = [p[i].step for i in range(n.value)]
         nb = C.c_size_t()
         tp = L.st_stream_plan_tables(self._h, C.byref(nb))
         self.tables = C.string_at(tp, nb.value) if nb.value else b""
@@ -199,6 +211,13 @@ class StreamPlan:
                                      tuple(self.order[st.first_out: st.first_out + st.n_out]), st.table_offset,
                                      st.units))
         self.steps = steps
+
+    def tensor_offset(self, begin: int) -> int:
+        """Blob offset of the data-section byte ``begin`` (which the plan reads)."""
+        for (b, e), d in zip(self.ranges, self.range_dsts):
+            if b <= begin < e:
+                return d + (begin - b)
+        raise KeyError(begin)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -234,6 +253,17 @@ def materialize(blob, table, units: int, outs, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
     check(lib().st_materialize(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
                                C.c_void_p(outs.data_ptr()), C.c_void_p(s.cuda_stream)), "st_materialize")
+
+
+def read_plans(path: str, index: SafeTensorIndex, plans, hosts) -> float:
+    """Read each plan's ranges into the matching host uint8 tensor (st_read_plans); returns seconds."""
+    n = len(plans)
+    ph = (C.c_void_p * max(1, n))(*[p._h for p in plans])
+    hb = (C.c_void_p * max(1, n))(*[h.data_ptr() for h in hosts])
+    nb = (C.c_size_t * max(1, n))(*[h.numel() for h in hosts])
+    secs = C.c_double()
+    check(lib().st_read_plans(os.fsencode(path), index._h, ph, hb, nb, n, C.byref(secs)), "st_read_plans")
+    return secs.value
 
 
 def stream_file(path: str, index: SafeTensorIndex, plan: StreamPlan, blob, tables, outs_plan, pinned, side_stream,
@@ -353,3 +383,10 @@ def load(path: str, device="cuda", unit_log2_scale: int = 0, streamed: bool = Tr
     out = ck.materialize()
     _torch().cuda.current_stream(ck.device).synchronize()
     return out
+
+
+from .lazy import (DiskRef, FilterViewStateDict, LazyModuleLoader, OutputMeta, PrefixViewStateDict,  # noqa: E402,F401
+                   RamCache, RenameViewStateDict, StreamStateDict)
+
+__all__ += ["StreamStateDict", "PrefixViewStateDict", "FilterViewStateDict", "RenameViewStateDict", "RamCache",
+            "LazyModuleLoader", "DiskRef", "OutputMeta"]

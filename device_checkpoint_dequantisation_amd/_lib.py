@@ -50,7 +50,11 @@ class PlanOpts(C.Structure):
 
 
 class StreamRange(C.Structure):
-    _fields_ = [("begin", C.c_uint64), ("end", C.c_uint64), ("step", C.c_uint32), ("reserved", C.c_uint32)]
+    _fields_ = [("begin", C.c_uint64), ("end", C.c_uint64), ("dst", C.c_uint64), ("step", C.c_uint32),
+                ("reserved", C.c_uint32)]
+
+
+PLAN_PACK = 1
 
 
 class StreamStep(C.Structure):
@@ -63,7 +67,7 @@ class StreamStats(C.Structure):
                 ("steps", C.c_uint32), ("launches", C.c_uint32)]
 
 
-assert C.sizeof(StreamRange) == 24 and C.sizeof(StreamStep) == 40 and C.sizeof(StreamStats) == 32
+assert C.sizeof(StreamRange) == 32 and C.sizeof(StreamStep) == 40 and C.sizeof(StreamStats) == 32
 
 
 # name -> (restype, argtypes); the full list of exported symbols the header declares.
@@ -93,7 +97,13 @@ SIGNATURES = {
                                 C.POINTER(C.c_double)]),
     "st_materialize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "st_stream_plan_build": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p)]),
+    "st_stream_plan_select": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_uint64, C.c_uint32,
+                                        C.POINTER(C.c_void_p)]),
     "st_stream_plan_free": (None, [C.c_void_p]),
+    "st_stream_plan_blob_bytes": (C.c_uint64, [C.c_void_p]),
+    "st_read_plan": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.POINTER(C.c_double)]),
+    "st_read_plans": (C.c_int, [C.c_char_p, C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
+                                C.POINTER(C.c_size_t), C.c_size_t, C.POINTER(C.c_double)]),
     "st_stream_plan_chunk_bytes": (C.c_uint64, [C.c_void_p]),
     "st_stream_plan_num_steps": (C.c_size_t, [C.c_void_p]),
     "st_stream_plan_step": (C.c_int, [C.c_void_p, C.c_size_t, C.POINTER(StreamStep)]),

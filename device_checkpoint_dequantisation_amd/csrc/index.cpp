@@ -541,14 +541,17 @@ st_status classify(st_index& ix) {
     return ST_OK;
 }
 
-st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64_t unit_begin, uint64_t* units) {
+// `at[t]` (if given) is where tensor t's bytes sit in the device blob; by default the blob is the
+// data section itself.
+st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64_t unit_begin, uint64_t* units,
+                  const uint64_t* at) {
     // unit_begin + units stays below 2^32: build_table rejects larger tables before use
     st_desc d;
     memset(&d, 0, sizeof d);
-    const Tensor& t = ix.tensors[o.tensor];
-    d.src = t.begin;
-    d.scale = o.scale >= 0 ? ix.tensors[size_t(o.scale)].begin : 0;
-    d.scale2 = o.scale2 >= 0 ? ix.tensors[size_t(o.scale2)].begin : 0;
+    auto where = [&](size_t t) { return at ? at[t] : ix.tensors[t].begin; };
+    d.src = where(o.tensor);
+    d.scale = o.scale >= 0 ? where(size_t(o.scale)) : 0;
+    d.scale2 = o.scale2 >= 0 ? where(size_t(o.scale2)) : 0;
     d.numel = o.numel;
     d.out = out_slot;
     const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
@@ -574,14 +577,13 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
 
 }  // namespace
 
-// Work table for outputs sel[0..k): header, descriptors (descriptor j writes outs[j]) and the
-// map from each group of ST_UNITS_PER_GROUP units to the descriptor holding its first unit.
-std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out) {
+std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out,
+                                            const uint64_t* at) {
     std::vector<st_desc> descs(k);
     std::vector<uint64_t> units(k);
     uint64_t pos = 0;
     for (size_t j = 0; j < k; ++j) {
-        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units[j]);
+        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units[j], at);
         pos += units[j];
         if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
     }

@@ -27,10 +27,12 @@ struct Output {
     uint64_t numel;
 };
 
-// Work table for outputs sel[0..k): header, group map and descriptors (descriptor j writes
-// outs[j]).  Throws std::length_error at 2^32 or more work units, std::bad_alloc when out of
-// memory.
-std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out);
+// Work table for outputs sel[0..k): header, the map from each group of ST_UNITS_PER_GROUP units to
+// the descriptor holding its first unit, and the descriptors (descriptor j writes outs[j]).
+// at[t], if given, is the device-blob offset of tensor t's bytes (default: its data-section
+// offset).  Throws std::length_error at 2^32 or more work units, std::bad_alloc when out of memory.
+std::vector<unsigned char> build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out,
+                                       const uint64_t* at = nullptr);
 
 // Clears this thread's st_last_error() message.
 void clear_error();

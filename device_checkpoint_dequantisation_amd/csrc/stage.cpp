@@ -10,6 +10,7 @@
 //  * st_stream_file: the steps of a stream plan; after each step's copies the compute stream waits
 //    for them and decodes the outputs the step completes, so decoding overlaps later reads and
 //    copies.
+//  * st_read_plan: a plan's ranges straight into host memory (the RAM tier), no GPU calls.
 #include <fcntl.h>
 #include <sys/stat.h>
 #include <unistd.h>
@@ -271,7 +272,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
             pos = 0;
             for (uint32_t r = step.first_range; r < step.first_range + step.n_ranges && r < n_ranges; ++r) {
                 const size_t len = size_t(ranges[r].end - ranges[r].begin);
-                if (hipMemcpyAsync(static_cast<char*>(blob_dev) + ranges[r].begin, slot + pos, len, hipMemcpyHostToDevice,
+                if (hipMemcpyAsync(static_cast<char*>(blob_dev) + ranges[r].dst, slot + pos, len, hipMemcpyHostToDevice,
                                    side) != hipSuccess) {
                     status = st_fail(ST_E_HIP, "st_stream_file: hipMemcpyAsync of %zu bytes failed", len);
                     break;
@@ -302,4 +303,41 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     if (status != ST_OK) (void)hipStreamSynchronize(side);  // nothing may still read the ring
     if (stats) *stats = st;
     return status;
+}
+
+extern "C" st_status st_read_plans(const char* path, const st_index* idx, const st_stream_plan* const* plans,
+                                   void* const* host_blobs, const size_t* host_bytes, size_t n, double* seconds_read) {
+    if (seconds_read) *seconds_read = 0;
+    if (!path || !idx || (n && (!plans || !host_blobs || !host_bytes))) return st_fail(ST_E_ARG, "st_read_plans: null pointer");
+    std::vector<Piece> batch;
+    const uint64_t off0 = st_index_data_offset(idx);
+    for (size_t j = 0; j < n; ++j) {
+        if (!plans[j] || !host_blobs[j]) return st_fail(ST_E_ARG, "st_read_plans: null plan or buffer %zu", j);
+        if (!st_stream_plan_of(plans[j], idx))
+            return st_fail(ST_E_ARG, "st_read_plans: plan %zu was built from another index", j);
+        if (host_bytes[j] < st_stream_plan_blob_bytes(plans[j]))
+            return st_fail(ST_E_ARG, "st_read_plans: host buffer %zu holds %zu bytes, %llu needed", j, host_bytes[j],
+                           (unsigned long long)st_stream_plan_blob_bytes(plans[j]));
+        size_t nr = 0;
+        const st_stream_range* ranges = st_stream_plan_ranges(plans[j], &nr);
+        for (size_t r = 0; r < nr; ++r)
+            batch.push_back(Piece{static_cast<char*>(host_blobs[j]) + ranges[r].dst, off0 + ranges[r].begin,
+                                  size_t(ranges[r].end - ranges[r].begin)});
+    }
+    FileFd file;
+    st_status status = open_checked(path, idx, file);
+    if (status != ST_OK) return status;
+    auto t0 = std::chrono::steady_clock::now();
+    {
+        ReaderPool pool(file.fd);
+        if (!pool.read(batch)) status = st_fail(ST_E_IO, "read of %s failed", path);
+    }
+    if (seconds_read) *seconds_read = seconds_since(t0);
+    return status;
+}
+
+extern "C" st_status st_read_plan(const char* path, const st_index* idx, const st_stream_plan* plan, void* host_blob,
+                                  size_t host_bytes, double* seconds_read) {
+    if (!plan || !host_blob) return st_fail(ST_E_ARG, "st_read_plan: null pointer");
+    return st_read_plans(path, idx, &plan, &host_blob, &host_bytes, 1, seconds_read);
 }

@@ -220,23 +220,32 @@ st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, v
                         size_t pinned_bytes, void* side_stream, void* done_event,
                         double* seconds_read);
 
-/* ---- Overlapped streaming: range reads, copies and decoding in flight together ----------------
+/* ---- Streaming plans: range reads, copies and decoding in flight together ----------------------
  * The pages' disk tier reads only the byte ranges a load needs into pinned host memory, copies
- * them to the GPU and then releases the host buffer ("Disk tier safetensors streaming design
- * audit", "Strategy summary / Range reads and tiering").  A stream plan cuts the data section
- * into staging steps of at most chunk_bytes.  Each step carries a work table for the outputs
- * whose weight and scale bytes have all been copied once the step's copies are done.
- * st_stream_file reads, copies and decodes step by step, so decoding overlaps the reads and copies
- * of later steps.  Bytes are staged in file order, except that a scale tensor lying more than one
- * chunk past the end of its weight is staged first (checkpoints that keep all scales at the end). */
+ * them to the GPU and then releases the host buffer; a state dict loads tensors on demand and a RAM
+ * tier keeps recently read weights ("Disk tier safetensors streaming design audit", "Strategy
+ * summary / Range reads and tiering", "Disk tier integration").  A stream plan covers every output
+ * of a checkpoint (st_stream_plan_build) or a chosen set (st_stream_plan_select).  It reads the
+ * outputs' weight and scale tensors, as runs of file-adjacent tensors, and cuts them into
+ * staging steps of at most chunk_bytes.  Bytes are staged in file order, except that a scale
+ * tensor lying more than one chunk past the end of its weight is staged first (checkpoints that
+ * keep all scales at the end).  Each step carries a work table for the outputs whose inputs have
+ * all been copied once the step's copies are done.  The device blob is either laid out like the
+ * data section (st_index_blob_bytes) or, with ST_PLAN_PACK, compact: only the plan's runs, each
+ * starting on a 256-byte boundary plus its data-section offset mod 256 (so the kernel sees the
+ * same alignment).  st_stream_file reads, copies and decodes step by step, so decoding overlaps
+ * the reads and copies of later steps; st_read_plan reads a plan's bytes into host memory. */
 
 typedef struct st_stream_plan st_stream_plan;  /* opaque, host memory, library-owned */
 
 typedef struct {
     uint64_t begin, end;    /* bytes [begin, end) of the data section */
+    uint64_t dst;           /* byte offset in the plan's device blob where they go */
     uint32_t step;          /* the staging step that copies them */
     uint32_t reserved;
 } st_stream_range;
+
+#define ST_PLAN_PACK 1u     /* st_stream_plan_select: compact blob of only the selected inputs */
 
 typedef struct {
     uint64_t bytes;         /* bytes this step copies */
@@ -248,11 +257,19 @@ typedef struct {
     uint64_t units;         /* that table's work-unit count; 0 = nothing to decode */
 } st_stream_step;
 
-/* Plan the streaming load of `idx` in steps of at most chunk_bytes (>= 64 KiB).  Every byte of
- * the data section belongs to exactly one range; every output to exactly one step. */
+/* Plan the streaming load of every output of `idx` in steps of at most chunk_bytes (>= 64 KiB).
+ * Every byte of the data section belongs to exactly one range; every output to exactly one step;
+ * the blob is laid out like the data section. */
 st_status st_stream_plan_build(const st_index* idx, uint64_t chunk_bytes, st_stream_plan** out);
+/* Plan the load of outputs sel[0..k) (distinct indices) only: the ranges cover their weight and
+ * scale tensors (plus gaps of at most 4 KiB between file-adjacent ones).  flags: 0 or
+ * ST_PLAN_PACK.  Output order within a step follows sel. */
+st_status st_stream_plan_select(const st_index* idx, const uint32_t* sel, size_t k, uint64_t chunk_bytes,
+                                uint32_t flags, st_stream_plan** out);
 void      st_stream_plan_free(st_stream_plan* plan);
 uint64_t  st_stream_plan_chunk_bytes(const st_stream_plan* plan);
+/* Bytes of the device blob the plan's tables address (ST_BLOB_ALIGN-aligned allocation). */
+uint64_t  st_stream_plan_blob_bytes(const st_stream_plan* plan);
 size_t    st_stream_plan_num_steps(const st_stream_plan* plan);
 st_status st_stream_plan_step(const st_stream_plan* plan, size_t s, st_stream_step* out);
 /* All ranges, step-major; valid for the plan's lifetime. */
@@ -273,10 +290,10 @@ typedef struct {
 } st_stream_stats;
 
 /* Stream the file at `path` through `plan`: for each step, read its ranges into a slot of the
- * pinned ring (pinned_bytes >= 4 * chunk_bytes; four slots), copy them into `blob_dev` with
+ * pinned ring (pinned_bytes >= 4 * chunk_bytes; four slots), copy each to blob_dev + dst with
  * hipMemcpyAsync on `side_stream`, make `compute_stream` wait for those copies and enqueue
  * st_materialize over the step's table on `compute_stream`.
- *   blob_dev    st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned (as for st_stage_file)
+ *   blob_dev    st_stream_plan_blob_bytes bytes, ST_BLOB_ALIGN-aligned
  *   tables_dev  device copy of st_stream_plan_tables, 64-byte aligned
  *   outs_dev    device array of output pointers in plan order (see st_stream_plan_order)
  *   done_event  (may be NULL) recorded on compute_stream after the last launch: once it has
@@ -289,6 +306,18 @@ typedef struct {
 st_status st_stream_file(const char* path, const st_index* idx, const st_stream_plan* plan, void* blob_dev,
                          const void* tables_dev, void* const* outs_dev, void* pinned, size_t pinned_bytes,
                          void* side_stream, void* compute_stream, void* done_event, st_stream_stats* stats);
+
+/* Read every range of `plan` from the file at `path` into host memory: range r lands at
+ * host_blob + dst.  host_bytes must be at least st_stream_plan_blob_bytes(plan); bytes no range
+ * covers are left as they are.  Uploading host_blob (one copy) and launching the plan's tables
+ * then decodes the plan's outputs without touching the file again (a RAM tier).  Synchronous;
+ * no GPU calls.  If `seconds_read` is not NULL it receives the wall time of the reads. */
+st_status st_read_plan(const char* path, const st_index* idx, const st_stream_plan* plan, void* host_blob,
+                       size_t host_bytes, double* seconds_read);
+/* st_read_plan for n plans of the same index at once (one pool of reader threads): plan j's
+ * ranges land in host_blobs[j], which holds host_bytes[j] bytes. */
+st_status st_read_plans(const char* path, const st_index* idx, const st_stream_plan* const* plans,
+                        void* const* host_blobs, const size_t* host_bytes, size_t n, double* seconds_read);
 
 /* Enqueue the grouped materialise kernel on `stream` (hipStream_t; NULL = default stream).
  *   blob   device copy of the data section (st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned)

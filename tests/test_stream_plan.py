@@ -169,3 +169,122 @@ def test_stream_file_rejects_a_plan_of_another_index_before_any_gpu_call(tmp_pat
     rc = lib().st_stream_file(str(path).encode(), a._h, plan._h, fake, fake, fake, fake, 1024, None, None, None,
                               C.byref(st_))
     assert rc == -1 and b"pinned buffer" in lib().st_last_error()
+
+
+# ---------------------------------------------------------------- selected and packed plans
+
+def _descs(table):
+    from device_checkpoint_dequantisation_amd._lib import Desc, TableHeader
+    h = TableHeader.from_buffer_copy(table[:64])
+    size = C.sizeof(Desc)
+    return [Desc.from_buffer_copy(table[h.desc_offset + j * size: h.desc_offset + (j + 1) * size])
+            for j in range(h.n_desc)]
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+@pytest.mark.parametrize("pack", [False, True])
+def test_selected_plan_reads_only_what_it_needs(k, pack, tmp_path):
+    buf = synth.config_bytes(k, small=True, **({"scales_last": True} if k == 2 and pack else {}))
+    path = tmp_path / "c.safetensors"
+    path.write_bytes(buf)
+    ix = st.SafeTensorIndex.open(str(path))
+    outs, ents = ix.outputs(), ix.tensors()
+    rng = np.random.default_rng(k)
+    sel = sorted(rng.choice(len(outs), size=max(1, len(outs) // 3), replace=False).tolist(), reverse=True)
+    plan = st.StreamPlan(ix, 64 << 10, select=sel, pack=pack)
+    assert sorted(plan.order) == sorted(sel)
+    # within a step, outputs keep the selection's order
+    for s in plan.steps:
+        assert list(s.outputs) == [o for o in sel if o in s.outputs]
+    needed = sorted({(ents[i].begin, ents[i].end) for o in sel for i in (outs[o].tensor, outs[o].scale, outs[o].scale2)
+                     if i >= 0 and ents[i].end > ents[i].begin})
+    # every needed byte is read exactly once; nothing else except small gaps between needed tensors
+    cover = sorted(plan.ranges)
+    for (b0, e0), (b1, e1) in zip(cover, cover[1:]):
+        assert e0 <= b1
+    read = sum(e - b for b, e in plan.ranges)
+    need = sum(e - b for b, e in needed)
+    assert need <= read <= need + 4096 * len(needed)
+    union = []
+    for b, e in cover:
+        if union and union[-1][1] == b:
+            union[-1][1] = e
+        else:
+            union.append([b, e])
+    for b, e in needed:
+        assert any(rb <= b and e <= re for rb, re in union)
+    # destinations: identity, or a compact blob keeping each byte's offset mod 256
+    for (b, e), d in zip(plan.ranges, plan.range_dsts):
+        if pack:
+            assert d % 256 == b % 256 and d + (e - b) + 64 <= plan.blob_bytes
+        else:
+            assert d == b
+    if pack:
+        spans = sorted((d, d + e - b) for (b, e), d in zip(plan.ranges, plan.range_dsts))
+        for (d0, e0), (d1, e1) in zip(spans, spans[1:]):
+            assert e0 <= d1
+        assert plan.blob_bytes <= need + 256 * (len(needed) + 1) + 4096 * len(needed)
+    else:
+        assert plan.blob_bytes == ix.blob_bytes
+    # the tables point at where the bytes land
+    for s in plan.steps:
+        if not s.outputs:
+            continue
+        hdr_bytes = int.from_bytes(plan.tables[s.table_offset + 32: s.table_offset + 40], "little")
+        descs = _descs(plan.tables[s.table_offset: s.table_offset + hdr_bytes])
+        for j, o in enumerate(s.outputs):
+            co = outs[o]
+            assert descs[j].src == plan.tensor_offset(ents[co.tensor].begin) or ents[co.tensor].end == ents[co.tensor].begin
+            if co.scale >= 0:
+                assert descs[j].scale == plan.tensor_offset(ents[co.scale].begin)
+            if co.scale2 >= 0:
+                assert descs[j].scale2 == plan.tensor_offset(ents[co.scale2].begin)
+    # st_read_plans lands every needed byte at its destination (host only, no GPU)
+    import torch
+    host = torch.full((plan.blob_bytes,), 0xEE, dtype=torch.uint8)
+    st.read_plans(str(path), ix, [plan], [host])
+    data = np.frombuffer(buf, np.uint8)[ix.data_offset:]
+    hb = host.numpy()
+    for b, e in needed:
+        d = plan.tensor_offset(b)
+        assert np.array_equal(hb[d: d + e - b], data[b:e])
+
+
+def test_select_errors():
+    ix = st.SafeTensorIndex.from_bytes(synth.config_bytes(2, small=True))
+    with pytest.raises(st.StError, match="out of range"):
+        st.StreamPlan(ix, 64 << 10, select=[ix.num_outputs])
+    with pytest.raises(st.StError, match="twice"):
+        st.StreamPlan(ix, 64 << 10, select=[1, 1])
+    with pytest.raises(ValueError):
+        st.StreamPlan(ix, 64 << 10, pack=True)
+    plan = st.StreamPlan(ix, 64 << 10, select=[], pack=True)
+    assert plan.order == [] and len(plan.steps) == 1 and plan.steps[0].units == 0
+
+
+def test_read_plans_several_and_errors(tmp_path):
+    buf = synth.config_bytes(4, small=True)
+    path = tmp_path / "c4.safetensors"
+    path.write_bytes(buf)
+    ix = st.SafeTensorIndex.open(str(path))
+    import torch
+    plans = [st.StreamPlan(ix, 64 << 10, select=[k], pack=True) for k in range(ix.num_outputs)]
+    hosts = [torch.zeros(p.blob_bytes, dtype=torch.uint8) for p in plans]
+    st.read_plans(str(path), ix, plans, hosts)
+    data = np.frombuffer(buf, np.uint8)[ix.data_offset:]
+    ents = ix.tensors()
+    for k, (p, h) in enumerate(zip(plans, hosts)):
+        co = ix.output(k)
+        for i in (co.tensor, co.scale, co.scale2):
+            if i >= 0:
+                e = ents[i]
+                d = p.tensor_offset(e.begin)
+                assert np.array_equal(h.numpy()[d: d + e.end - e.begin], data[e.begin:e.end])
+    with pytest.raises(st.StError, match="needed"):
+        st.read_plans(str(path), ix, plans[:1], [torch.zeros(8, dtype=torch.uint8)])
+    other = st.SafeTensorIndex.open(str(path))
+    with pytest.raises(st.StError, match="another index"):
+        st.read_plans(str(path), other, plans[:1], hosts[:1])
+    (tmp_path / "short.safetensors").write_bytes(buf[:-1])
+    with pytest.raises(st.StError, match="ST_E_IO"):
+        st.read_plans(str(tmp_path / "short.safetensors"), ix, plans[:1], hosts[:1])
