@@ -78,7 +78,10 @@ def parse():
     ap.add_argument("--unit-scale", type=int, default=0)
     ap.add_argument("--stream-chunk-mb", type=int, default=128, help="staging step of the overlapped load")
     ap.add_argument("--load-reps", type=int, default=2, help="repetitions of the end-to-end load comparison")
-    ap.add_argument("--no-lazy", action="store_true", help="skip the on-demand (per-layer) load measurement")
+    ap.add_argument("--extras", action="store_true",
+                    help="also measure, for the main config, the serial vs streamed end-to-end load, on-demand "
+                         "per-layer loads and tensor-parallel shard decodes (they launch the kernel on other tables, "
+                         "so a kernel-trace summary of the default command covers only the timed decode)")
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -179,6 +182,10 @@ def measure(k, d, args, rng, overrides=None):
     torch.cuda.synchronize()
     ok, checked, bad = sampled_parity(path, ix, ck, rng)
     log(f"[bench] sampled parity vs oracle: {'ok' if ok else 'MISMATCH in ' + str(bad)} ({checked} elements)")
+    shards = None
+    if k == args.config and args.extras:
+        shards = tp_shards(ix, ck, max(3, args.steps // 5))
+        log(f"[bench] tensor-parallel shards: {shards}")
     # timed region: K back-to-back launches, wall clock + per-launch HIP events on the same stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -190,8 +197,31 @@ def measure(k, d, args, rng, overrides=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = np.array([a.elapsed_time(b) for a, b in evs])
-    # end-to-end load, warm page cache: serial (stage everything, then one launch) against the
-    # overlapped pipeline (each staging step decoded while later steps are read and copied)
+    load = None
+    if k == args.config and args.extras:
+        load = end_to_end_loads(path, ix, ck, side, stream, args, rng)
+    res = {
+        "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
+        "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
+        "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min()), "index_ms": index_ms,
+        "stage": dict({"file_to_pinned_GBps": ix.data_size / read_s / 1e9 if read_s > 0 else None,
+                       "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)"},
+                      **(load or {})),
+        "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
+        "shards": shards,
+    }
+    res["GBps"] = traffic / (res["ms_per_step"] * 1e-3) / 1e9
+    res["kernel_GBps"] = traffic / (res["kernel_ms_mean"] * 1e-3) / 1e9
+    del ck
+    torch.cuda.empty_cache()
+    return res
+
+
+def end_to_end_loads(path, ix, ck, side, stream, args, rng):
+    """End-to-end load with a warm page cache: serial (stage everything, then one launch) against
+    the overlapped pipeline (each staging step decoded while later steps are read and copied)."""
+    import torch
+    import device_checkpoint_dequantisation_amd as st
     pinned = torch.empty(512 << 20, dtype=torch.uint8, pin_memory=True)
     plan = st.StreamPlan(ix, args.stream_chunk_mb << 20)
     ck.stream(path, stream=stream, plan=plan)  # allocates the pinned ring once
@@ -210,39 +240,84 @@ def measure(k, d, args, rng, overrides=None):
         ck.synchronize()
         stream_s.append(time.perf_counter() - t0)
     del pinned
-    sok, schecked, sbad = sampled_parity(path, ix, ck, rng)
+    sok, _, sbad = sampled_parity(path, ix, ck, rng)
     log(f"[bench] load: serial {min(serial_s):.3f}s, streamed {min(stream_s):.3f}s in {len(plan.steps)} steps "
         f"({sstats['launches']} launches); streamed parity {'ok' if sok else 'MISMATCH in ' + str(sbad)}")
-    res = {
-        "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
-        "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
-        "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min()), "index_ms": index_ms,
-        "stage": {"file_to_pinned_GBps": ix.data_size / read_s / 1e9 if read_s > 0 else None,
-                  "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)",
-                  "serial_load_GBps": round(ix.data_size / min(serial_s) / 1e9, 2),
-                  "streamed_load_GBps": round(ix.data_size / min(stream_s) / 1e9, 2),
-                  "streamed_load_s": round(min(stream_s), 4), "serial_load_s": round(min(serial_s), 4),
-                  "stream_chunk_MiB": args.stream_chunk_mb, "stream_steps": len(plan.steps),
-                  "stream_launches": sstats["launches"],
-                  "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}"},
-        "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
-    }
-    res["GBps"] = traffic / (res["ms_per_step"] * 1e-3) / 1e9
-    res["kernel_GBps"] = traffic / (res["kernel_ms_mean"] * 1e-3) / 1e9
-    del ck
-    torch.cuda.empty_cache()
+    return {"serial_load_GBps": round(ix.data_size / min(serial_s) / 1e9, 2),
+            "streamed_load_GBps": round(ix.data_size / min(stream_s) / 1e9, 2),
+            "streamed_load_s": round(min(stream_s), 4), "serial_load_s": round(min(serial_s), 4),
+            "stream_chunk_MiB": args.stream_chunk_mb, "stream_steps": len(plan.steps),
+            "stream_launches": sstats["launches"], "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}"}
+
+
+def tp_shards(ix, ck, steps, n=8):
+    """Decode the whole checkpoint as n-way tensor-parallel shards of every 2-d output (row shards,
+    then column shards; cuts on scale-block boundaries), one launch per layout, and check every
+    shard against the unsharded decode on the GPU."""
+    import torch
+    outs = ix.outputs()
+    res = {}
+    for label, axis in (("row_shards", 0), ("col_shards", 1)):
+        slices = []
+        for k, o in enumerate(outs):
+            if len(o.shape) != 2:
+                slices.append((k, None, None))
+                continue
+            dim = o.shape[axis]
+            q = 128 if o.kind == "FP8_BLOCK128" else 16 if (o.kind == "NVFP4" and axis == 1) else 1
+            step = max(q, -(-dim // n // q) * q)
+            for b in range(0, dim, step):
+                part = (b, min(dim, b + step))
+                slices.append((k, part, None) if axis == 0 else (k, None, part))
+        shapes = [ix.slice_shape(*sl) for sl in slices]
+        offs, total = [], 0
+        for r, c in shapes:
+            offs.append(total)
+            total += (2 * r * c + 255) // 256 * 256
+        arena = torch.empty(max(total, 256) // 2, dtype=torch.bfloat16, device=ck.device)
+        base = arena.data_ptr()
+        ptrs = torch.tensor([base + o for o in offs], dtype=torch.int64).to(ck.device)
+        raw, units = ix.table_slices(slices)
+        strided = axis == 1  # column shards need the strided kernel; row shards are contiguous
+        table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(ck.device)
+        stream = torch.cuda.current_stream(ck.device)
+        import device_checkpoint_dequantisation_amd as st
+        st.materialize(ck.blob, table, units, ptrs, stream, slices=strided)
+        torch.cuda.synchronize()
+        ok = True
+        for (k, rows, cols), (r, c), off in zip(slices, shapes, offs):
+            got = arena[off // 2: off // 2 + r * c].view(r, c)
+            whole = ck.tensors[outs[k].name]
+            whole = whole.reshape(whole.shape[0], -1) if whole.dim() >= 2 else whole.reshape(-1, 1)
+            r0, r1 = rows if rows else (0, whole.shape[0])
+            c0, c1 = cols if cols else (0, whole.shape[1])
+            ok &= torch.equal(got.view(torch.int16), whole[r0:r1, c0:c1].view(torch.int16))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            st.materialize(ck.blob, table, units, ptrs, stream, slices=strided)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[label] = {"shards_per_output": n, "slices": len(slices), "kernel_ms_mean": round(ms, 4),
+                      "kernel": "st_materialize_slices" if strided else "st_materialize",
+                      "GBps": round(ix.traffic_bytes / (ms * 1e-3) / 1e9, 2),
+                      "parity": "bit-exact vs whole decode" if ok else "MISMATCH"}
+        del arena
     return res
 
 
 def lazy_loads(path, dev):
-    """On-demand loads through StreamStateDict, one layer (keys sharing their first two name
-    components) per load: without a RAM tier, filling it, and served from it."""
+    """On-demand loads through StreamStateDict, one layer (keys sharing their name up to the first
+    numeric component) per load: without a RAM tier, filling it, and served from it."""
     import torch
     import device_checkpoint_dequantisation_amd as st
+    import re
     probe = st.StreamStateDict(path, dev)
     groups = {}
-    for k in probe:
-        groups.setdefault(".".join(k.split(".")[:2]), []).append(k)
+    for k in probe:  # a layer: the name up to its first numeric component ("blocks.3", "model.layers.12")
+        m = re.match(r"^(.*?\.\d+)\.", k)
+        groups.setdefault(m.group(1) if m else k.split(".")[0], []).append(k)
     src = sum(probe.meta(k).source_bytes for k in probe)
     res = {"layers": len(groups), "source_bytes": src}
     for label, ram in (("file", 0), ("file_into_ram", 1 << 40), ("ram", None)):
@@ -277,7 +352,7 @@ def main():
     cpu = None
     for k in configs:
         results[k] = measure(k, d, args, rng)
-        if k == args.config and not args.no_lazy:
+        if k == args.config and args.extras:
             results[k]["lazy"] = lazy_loads(results[k]["path"], "cuda:0")
             log(f"[bench] lazy per-layer loads: {results[k]['lazy']}")
         if k == args.config and not args.no_cpu:
@@ -315,6 +390,8 @@ def main():
     }
     if "lazy" in r:
         line["lazy_loads"] = r["lazy"]
+    if r.get("shards"):
+        line["tp_shards"] = r["shards"]
     if aligned is not None:
         line["scaled_fp8_all_weights_16B_aligned"] = {"GBps": round(aligned["GBps"], 2),
                                                       "kernel_ms_mean": round(aligned["kernel_ms_mean"], 4),

@@ -18,8 +18,8 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import (DTYPES, KINDS, PLAN_PACK, Desc, OutputInfo, PlanOpts, StError, StreamStats, StreamStep,  # noqa: F401
-                   TensorMeta, check, lib)
+from ._lib import (DTYPES, KINDS, PLAN_PACK, Desc, OutputInfo, PlanOpts, Slice, StError, StreamStats,  # noqa: F401
+                   StreamStep, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "load", "materialize", "stage_file", "stream_file",
            "read_plans", "StError", "KINDS"]
@@ -142,6 +142,44 @@ class SafeTensorIndex:
         """Output (weight) names, in output order; metadata only."""
         return [self.output(k).name for k in range(self.num_outputs)]
 
+    # ---- slices
+    @staticmethod
+    def _slices(slices):
+        arr = (Slice * max(1, len(slices)))()
+        for j, sl in enumerate(slices):
+            out, rows, cols = (sl + (None, None))[:3] if isinstance(sl, tuple) else (sl, None, None)
+            r0, r1 = rows if rows is not None else (0, -1)
+            c0, c1 = cols if cols is not None else (0, -1)
+            arr[j] = Slice(int(out), 0, int(r0), int(-1 if r1 is None else r1), int(c0), int(-1 if c1 is None else c1))
+        return arr
+
+    def slice_shape(self, output: int, rows=None, cols=None) -> tuple:
+        """(rows, cols) of a slice of the output's matrix view (st_index_slice_numel)."""
+        arr = self._slices([(output, rows, cols)])
+        r, c = C.c_uint64(), C.c_uint64()
+        check(lib().st_index_slice_numel(self._h, arr, C.byref(r), C.byref(c)), "st_index_slice_numel")
+        return r.value, c.value
+
+    def has_column_slices(self, slices) -> bool:
+        """True if any slice takes part of its output's columns (a strided source)."""
+        for sl in slices:
+            out, rows, cols = (sl + (None, None))[:3] if isinstance(sl, tuple) else (sl, None, None)
+            if cols is not None and self.slice_shape(out, None, cols)[1] != self.slice_shape(out)[1]:
+                return True
+        return False
+
+    def table_slices(self, slices):
+        """Work table for slices, each ``(output, (row_begin, row_end), (col_begin, col_end))`` with
+        None for a whole dimension and -1 for "to the end"; descriptor j writes outs[j]."""
+        arr = self._slices(list(slices))
+        k = len(slices)
+        nb, units = C.c_size_t(), C.c_uint64()
+        check(lib().st_index_table_slices(self._h, arr, k, None, 0, C.byref(nb), C.byref(units)), "st_index_table_slices")
+        dst = C.create_string_buffer(nb.value)
+        check(lib().st_index_table_slices(self._h, arr, k, dst, nb.value, C.byref(nb), C.byref(units)),
+              "st_index_table_slices")
+        return dst.raw[: nb.value], units.value
+
     # ---- work tables
     def table(self):
         """(bytes of the work table for every output, work units = the n st_materialize takes)."""
@@ -246,13 +284,15 @@ def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> 
     return secs.value
 
 
-def materialize(blob, table, units: int, outs, stream=None):
+def materialize(blob, table, units: int, outs, stream=None, slices: bool = False):
     """Enqueue the grouped kernel: ``blob`` (the staged data section), ``table`` (a work table) and
-    ``outs`` (device pointers, int64) are device tensors; ``units`` is the table's work-unit count."""
+    ``outs`` (device pointers, int64) are device tensors; ``units`` is the table's work-unit count.
+    ``slices`` selects the kernel with the strided path for column slices (st_materialize_slices)."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
-    check(lib().st_materialize(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
-                               C.c_void_p(outs.data_ptr()), C.c_void_p(s.cuda_stream)), "st_materialize")
+    fn, name = (lib().st_materialize_slices, "st_materialize_slices") if slices else (lib().st_materialize, "st_materialize")
+    check(fn(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units, C.c_void_p(outs.data_ptr()),
+             C.c_void_p(s.cuda_stream)), name)
 
 
 def read_plans(path: str, index: SafeTensorIndex, plans, hosts) -> float:
@@ -361,6 +401,24 @@ class DeviceCheckpoint:
         if data_section:
             host = torch.frombuffer(bytearray(data_section), dtype=torch.uint8)
             self.blob[: len(data_section)].copy_(host)
+
+    def materialize_slices(self, slices, stream=None, strided_kernel: bool | None = None) -> list:
+        """bf16 tensors [rows, cols] for slices of outputs (see SafeTensorIndex.table_slices),
+        decoded in one launch from the staged blob.  ``strided_kernel`` (default: whether any
+        slice cuts columns) picks st_materialize_slices; with False, the whole-output kernel's
+        exact path decodes column slices element by element."""
+        torch = _torch()
+        slices = list(slices)
+        shapes = [self.index.slice_shape(*((sl + (None, None))[:3] if isinstance(sl, tuple) else (sl,))) for sl in slices]
+        outs = [torch.empty(shp, dtype=torch.bfloat16, device=self.device) for shp in shapes]
+        raw, units = self.index.table_slices(slices)
+        if strided_kernel is None:
+            strided_kernel = self.index.has_column_slices(slices)
+        table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        ptrs = torch.tensor([o.data_ptr() for o in outs] or [0], dtype=torch.int64).to(self.device)
+        if units:
+            materialize(self.blob, table, units, ptrs, stream, slices=strided_kernel)
+        return outs
 
     def materialize(self, stream=None):
         if self.units:

@@ -27,7 +27,8 @@ class OutputInfo(C.Structure):
 
 
 class Desc(C.Structure):
-    _fields_ = [("src", C.c_uint64), ("scale", C.c_uint64), ("scale2", C.c_uint64), ("numel", C.c_uint64),
+    _fields_ = [("src", C.c_uint64), ("scale", C.c_uint64), ("scale2", C.c_uint64), ("pitch", C.c_uint32),
+                ("flags", C.c_uint32),
                 ("unit_begin", C.c_uint32), ("unit_end", C.c_uint32), ("tail", C.c_uint32), ("out", C.c_uint32),
                 ("cols", C.c_uint32), ("grid_cols", C.c_uint32), ("div_magic", C.c_uint32), ("meta", C.c_uint32)]
 
@@ -43,6 +44,17 @@ class TableHeader(C.Structure):
 assert C.sizeof(TableHeader) == 64
 TABLE_MAGIC = 0x334D5453
 UNITS_PER_GROUP = 4
+
+
+DESC_EXACT = 1
+
+
+class Slice(C.Structure):
+    _fields_ = [("output", C.c_uint32), ("reserved", C.c_uint32), ("row_begin", C.c_int64), ("row_end", C.c_int64),
+                ("col_begin", C.c_int64), ("col_end", C.c_int64)]
+
+
+assert C.sizeof(Slice) == 40
 
 
 class PlanOpts(C.Structure):
@@ -93,9 +105,13 @@ SIGNATURES = {
     "st_index_table": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
     "st_index_table_subset": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_void_p, C.c_size_t,
                                         C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
+    "st_index_table_slices": (C.c_int, [C.c_void_p, C.POINTER(Slice), C.c_size_t, C.c_void_p, C.c_size_t,
+                                        C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
+    "st_index_slice_numel": (C.c_int, [C.c_void_p, C.POINTER(Slice), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
     "st_stage_file": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                                 C.POINTER(C.c_double)]),
     "st_materialize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "st_materialize_slices": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "st_stream_plan_build": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p)]),
     "st_stream_plan_select": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_uint64, C.c_uint32,
                                         C.POINTER(C.c_void_p)]),

@@ -552,7 +552,6 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     d.src = where(o.tensor);
     d.scale = o.scale >= 0 ? where(size_t(o.scale)) : 0;
     d.scale2 = o.scale2 >= 0 ? where(size_t(o.scale2)) : 0;
-    d.numel = o.numel;
     d.out = out_slot;
     const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
     uint32_t div_shift = 0;
@@ -577,22 +576,18 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
 
 }  // namespace
 
-std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out,
-                                            const uint64_t* at) {
-    std::vector<st_desc> descs(k);
-    std::vector<uint64_t> units(k);
-    uint64_t pos = 0;
-    for (size_t j = 0; j < k; ++j) {
-        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units[j], at);
-        pos += units[j];
-        if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
-    }
-    const uint64_t groups = (pos + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
+namespace {
+
+// A work table from descriptors whose unit ranges are set, `units` in total: header, map,
+// descriptors.
+std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units) {
+    const size_t k = descs.size();
+    const uint64_t groups = (units + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
     st_table_header h;
     memset(&h, 0, sizeof h);
     h.magic = ST_TABLE_MAGIC;
     h.n_desc = uint32_t(k);
-    h.units = pos;
+    h.units = units;
     h.map_offset = sizeof(st_table_header);
     h.desc_offset = stk::table_desc_offset(groups);
     h.bytes = h.desc_offset + k * sizeof(st_desc);
@@ -606,9 +601,112 @@ std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* 
         while (descs[d].unit_end <= u) ++d;  // skips outputs with no units
         map[g] = uint32_t(d);
     }
-    *units_out = pos;
     return t;
 }
+
+}  // namespace
+
+std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out,
+                                            const uint64_t* at) {
+    std::vector<st_desc> descs(k);
+    uint64_t pos = 0;
+    for (size_t j = 0; j < k; ++j) {
+        uint64_t units = 0;
+        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units, at);
+        pos += units;
+        if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
+    }
+    *units_out = pos;
+    return assemble(descs, pos);
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------------- slices
+
+// A slice with its bounds resolved against the output's matrix view [R, C].
+struct Slice {
+    uint64_t R, C, r0, r1, c0, c1;
+    uint64_t rows() const { return r1 - r0; }
+    uint64_t cols() const { return c1 - c0; }
+    bool strided() const { return !(c0 == 0 && c1 == C); }
+};
+
+st_status resolve_slice(const st_index& ix, const st_slice& sl, Slice& g) {
+    if (sl.output >= ix.outputs.size())
+        return st_fail(ST_E_ARG, "slice of output %u, the index has %zu", sl.output, ix.outputs.size());
+    const Output& o = ix.outputs[sl.output];
+    const std::string& name = ix.tensors[o.tensor].name;
+    if (sl.reserved) return st_fail(ST_E_ARG, "%s: slice.reserved must be 0", name.c_str());
+    g.R = o.shape.empty() ? 1 : uint64_t(o.shape[0]);
+    g.C = o.shape.size() <= 1 ? 1 : (g.R ? o.numel / g.R : 0);
+    if (o.shape.size() > 1 && g.R == 0) {
+        g.C = 1;
+        for (size_t d = 1; d < o.shape.size(); ++d) g.C *= uint64_t(o.shape[d]);
+    }
+    const int64_t r1 = sl.row_end < 0 ? int64_t(g.R) : sl.row_end, c1 = sl.col_end < 0 ? int64_t(g.C) : sl.col_end;
+    if (sl.row_begin < 0 || sl.row_begin > r1 || uint64_t(r1) > g.R || sl.col_begin < 0 || sl.col_begin > c1 ||
+        uint64_t(c1) > g.C)
+        return st_fail(ST_E_ARG, "%s: slice rows [%lld, %lld) cols [%lld, %lld) outside [%llu, %llu]", name.c_str(),
+                       (long long)sl.row_begin, (long long)r1, (long long)sl.col_begin, (long long)c1,
+                       (unsigned long long)g.R, (unsigned long long)g.C);
+    g.r0 = uint64_t(sl.row_begin);
+    g.r1 = uint64_t(r1);
+    g.c0 = uint64_t(sl.col_begin);
+    g.c1 = uint64_t(c1);
+    if (o.kind == ST_KIND_FP8_BLOCK128 && (g.r0 % 128 || g.c0 % 128))
+        return st_fail(ST_E_SHAPE, "%s: block-FP8 slices start at multiples of 128 (rows %llu, cols %llu)",
+                       name.c_str(), (unsigned long long)g.r0, (unsigned long long)g.c0);
+    if (o.kind == ST_KIND_NVFP4 && (g.c0 % 16 || g.cols() % 16))
+        return st_fail(ST_E_SHAPE, "%s: NVFP4 column slices start at and span multiples of 16 (cols [%llu, %llu))",
+                       name.c_str(), (unsigned long long)g.c0, (unsigned long long)g.c1);
+    if (g.strided() && (g.rows() * g.cols() >= (uint64_t(1) << 32) || g.C >= (uint64_t(1) << 32)))
+        return st_fail(ST_E_SHAPE, "%s: a column slice needs fewer than 2^32 elements and rows shorter than 2^32",
+                       name.c_str());
+    return ST_OK;
+}
+
+st_desc make_slice_desc(const st_index& ix, const Output& o, const Slice& g, uint32_t out_slot, uint64_t unit_begin,
+                        uint64_t* units) {
+    st_desc d;
+    memset(&d, 0, sizeof d);
+    const Tensor& t = ix.tensors[o.tensor];
+    const uint32_t bits = stk::source_bits(o.kind);
+    const uint64_t first = g.r0 * g.C + g.c0;  // first source element
+    d.src = t.begin + first * bits / 8;
+    d.scale = o.scale >= 0 ? ix.tensors[size_t(o.scale)].begin : 0;
+    d.scale2 = o.scale2 >= 0 ? ix.tensors[size_t(o.scale2)].begin : 0;
+    d.out = out_slot;
+    const uint64_t width = g.strided() ? g.cols() : g.C;  // the row length the kernel indexes by
+    uint32_t div_shift = 0;
+    if (o.kind == ST_KIND_FP8_BLOCK128) {
+        d.grid_cols = uint32_t((g.C + 127) / 128);
+        d.scale += 4 * ((g.r0 / 128) * d.grid_cols + g.c0 / 128);
+    } else if (o.kind == ST_KIND_NVFP4) {
+        d.scale += first / 16;
+    }
+    if (o.kind == ST_KIND_FP8_BLOCK128 || o.kind == ST_KIND_NVFP4 || g.strided()) d.cols = uint32_t(width);
+    if ((o.kind == ST_KIND_FP8_BLOCK128 || g.strided()) && width) {
+        d.div_magic = stk::div_magic(uint32_t(width));
+        div_shift = stk::div_shift(uint32_t(width));
+    }
+    if (g.strided()) {
+        d.pitch = uint32_t(g.C);
+        const bool whole_chunks = g.cols() % stk::chunk_elems(o.kind) == 0;
+        const bool aligned_rows = (g.C * bits / 8) % stk::load_word_bytes(o.kind) == 0 && (g.C * bits) % 8 == 0;
+        if (!whole_chunks || !aligned_rows) d.flags = ST_DESC_EXACT;
+    }
+    const uint64_t numel = g.rows() * g.cols();
+    const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
+    d.meta = uint32_t(o.kind) | unit_shift << 8 | div_shift << 16;
+    *units = (numel + (uint64_t(1) << unit_shift) - 1) >> unit_shift;
+    d.unit_begin = uint32_t(unit_begin);
+    d.unit_end = uint32_t(unit_begin + *units);
+    d.tail = uint32_t(numel - ((*units ? *units - 1 : 0) << unit_shift));
+    return d;
+}
+
+}  // namespace
 
 namespace {
 
@@ -819,6 +917,47 @@ extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* 
     if (!dst) return ST_OK;
     if (dst_bytes < t.size())
         return st_fail(ST_E_ARG, "st_index_table_subset: dst holds %zu bytes, %zu needed", dst_bytes, t.size());
+    memcpy(dst, t.data(), t.size());
+    return ST_OK;
+}
+
+extern "C" st_status st_index_slice_numel(const st_index* idx, const st_slice* s, uint64_t* rows, uint64_t* cols) {
+    st_clear();
+    if (!idx || !s) return st_fail(ST_E_ARG, "st_index_slice_numel: null pointer");
+    Slice g;
+    st_status r = resolve_slice(*idx, *s, g);
+    if (r != ST_OK) return r;
+    if (rows) *rows = g.rows();
+    if (cols) *cols = g.cols();
+    return ST_OK;
+}
+
+extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* slices, size_t k, void* dst,
+                                           size_t dst_bytes, size_t* bytes, uint64_t* units) {
+    st_clear();
+    if (!idx || (k && !slices)) return st_fail(ST_E_ARG, "st_index_table_slices: null pointer");
+    std::vector<unsigned char> t;
+    uint64_t pos = 0;
+    try {
+        std::vector<st_desc> descs(k);
+        for (size_t j = 0; j < k; ++j) {
+            Slice g;
+            st_status r = resolve_slice(*idx, slices[j], g);
+            if (r != ST_OK) return r;
+            uint64_t u = 0;
+            descs[j] = make_slice_desc(*idx, idx->outputs[slices[j].output], g, uint32_t(j), pos, &u);
+            pos += u;
+            if (pos >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "st_index_table_slices: 2^32 or more work units");
+        }
+        t = assemble(descs, pos);
+    } catch (const std::bad_alloc&) {
+        return st_fail(ST_E_NOMEM, "out of host memory");
+    }
+    if (bytes) *bytes = t.size();
+    if (units) *units = pos;
+    if (!dst) return ST_OK;
+    if (dst_bytes < t.size())
+        return st_fail(ST_E_ARG, "st_index_table_slices: dst holds %zu bytes, %zu needed", dst_bytes, t.size());
     memcpy(dst, t.data(), t.size());
     return ST_OK;
 }

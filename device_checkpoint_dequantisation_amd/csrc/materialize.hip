@@ -129,7 +129,8 @@ __device__ __forceinline__ bool finite(float s) { return __builtin_fabsf(s) <= 3
 // ------------------------------------------------------------------------- descriptors
 
 struct Desc {
-    uint64_t src, scale, scale2, numel;
+    uint64_t src, scale, scale2;
+    uint32_t pitch, flags;
     uint32_t unit_begin, unit_end, tail, out, cols, grid_cols, div_magic, kind, unit_shift, div_shift;
 };
 
@@ -140,7 +141,8 @@ __device__ __forceinline__ Desc load_desc(const st_desc* d) {
     r.src = uint64_t(w[1]) << 32 | w[0];
     r.scale = uint64_t(w[3]) << 32 | w[2];
     r.scale2 = uint64_t(w[5]) << 32 | w[4];
-    r.numel = uint64_t(w[7]) << 32 | w[6];
+    r.pitch = w[6];
+    r.flags = w[7];
     r.unit_begin = w[8];
     r.unit_end = w[9];
     r.tail = w[10];
@@ -155,24 +157,33 @@ __device__ __forceinline__ Desc load_desc(const st_desc* d) {
 }
 static_assert(offsetof(st_desc, meta) == 15 * 4, "descriptor layout");
 
+// Source element of output element e: e itself, or for a column slice (pitch != 0) the element
+// row * pitch + col of the slice's source rows, with row = e / cols and col = e % cols.
+__device__ __forceinline__ uint64_t src_elem(const Desc& D, uint64_t e) {
+    if (D.pitch == 0) return e;
+    const uint32_t row = stk::div_apply(uint32_t(e), D.div_magic, D.div_shift);
+    return e + uint64_t(row) * (D.pitch - D.cols);
+}
+
 // bf16 bits of element e of descriptor D, straight from the definition, byte by byte.
 __device__ __forceinline__ uint32_t elem_exact(const uint8_t* __restrict__ blob, const Desc& D, uint64_t e) {
     const uint8_t* s = blob + D.src;
+    const uint64_t x = src_elem(D, e);
     switch (D.kind) {
-        case ST_KIND_PASS_BF16: return ld_u16_any(s + 2 * e);
-        case ST_KIND_CAST_F16: return bf16_canon(h2f(ld_u16_any(s + 2 * e)));
-        case ST_KIND_CAST_F32: return bf16_canon(as_f32(ld_u32_any(s + 4 * e)));
-        case ST_KIND_FP8_TENSOR: return bf16_canon(e4m3_exact(ld_u8(s + e)) * as_f32(ld_u32_any(blob + D.scale)));
-        case ST_KIND_FP8_BLOCK128: {
+        case ST_KIND_PASS_BF16: return ld_u16_any(s + 2 * x);
+        case ST_KIND_CAST_F16: return bf16_canon(h2f(ld_u16_any(s + 2 * x)));
+        case ST_KIND_CAST_F32: return bf16_canon(as_f32(ld_u32_any(s + 4 * x)));
+        case ST_KIND_FP8_TENSOR: return bf16_canon(e4m3_exact(ld_u8(s + x)) * as_f32(ld_u32_any(blob + D.scale)));
+        case ST_KIND_FP8_BLOCK128: {  // the scale grid position comes from the output's row and column
             const uint32_t e32 = uint32_t(e);
             const uint32_t row = stk::div_apply(e32, D.div_magic, D.div_shift);
             const uint32_t col = e32 - row * D.cols;
             const float S = as_f32(ld_u32_any(blob + D.scale + 4ull * ((row >> 7) * D.grid_cols + (col >> 7))));
-            return bf16_canon(e4m3_exact(ld_u8(s + e)) * S);
+            return bf16_canon(e4m3_exact(ld_u8(s + x)) * S);
         }
-        default: {  // NVFP4: K % 16 == 0, so block scale (i, j / 16) sits at flat index e / 16
-            const uint32_t nib = (ld_u8(s + (e >> 1)) >> ((e & 1) * 4)) & 15u;
-            const float bs = e4m3_exact(ld_u8(blob + D.scale + (e >> 4)));
+        default: {  // NVFP4: K % 16 == 0, so block scale (i, j / 16) sits at flat source index x / 16
+            const uint32_t nib = (ld_u8(s + (x >> 1)) >> ((x & 1) * 4)) & 15u;
+            const float bs = e4m3_exact(ld_u8(blob + D.scale + (x >> 4)));
             const float g = as_f32(ld_u32_any(blob + D.scale2));
             const float t = e2m1_exact(nib) * bs;
             return bf16_canon(t * g);
@@ -198,21 +209,28 @@ struct Ctx {
     bool vec;        // the output is 16-byte aligned (vector stores)
 };
 
-struct KPass {
+// CE, IB, LG from the kind's geometry (shared with the host planner); CH chunks per lane per unit.
+template <uint32_t KIND_>
+struct Geom {
+    static constexpr uint32_t KIND = KIND_, CE = stk::chunk_elems(KIND_), LG = stk::load_word_bytes(KIND_),
+                              IB = CE * stk::source_bits(KIND_) / 8;
+};
+
+struct KPass : Geom<ST_KIND_PASS_BF16> {
     static constexpr int SCALE = 0;  // no scalar scale
-    static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
+    static constexpr uint32_t CH = stk::kWordsPass;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, u32x4* o) {
         o[0] = u32x4{in[0], in[1], in[2], in[3]};
         return true;
     }
 };
 
-struct KF16 {
+struct KF16 : Geom<ST_KIND_CAST_F16> {
     static constexpr int SCALE = 0;  // no scalar scale
-    static constexpr uint32_t CE = 8, IB = 16, LG = 16, CH = stk::kWordsPass;
+    static constexpr uint32_t CH = stk::kWordsPass;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, u32x4* o) {
         bool nan = false;
 #pragma unroll
         for (int k = 0; k < 4; ++k) nan |= (in[k] & 0x7FFFu) > 0x7C00u || (in[k] & 0x7FFF0000u) > 0x7C000000u;
@@ -225,11 +243,11 @@ struct KF16 {
     }
 };
 
-struct KF32 {
+struct KF32 : Geom<ST_KIND_CAST_F32> {
     static constexpr int SCALE = 0;  // no scalar scale
-    static constexpr uint32_t CE = 8, IB = 32, LG = 16, CH = stk::kWordsF32;
+    static constexpr uint32_t CH = stk::kWordsF32;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 4; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, u32x4* o) {
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, u32x4* o) {
         bool nan = false;
 #pragma unroll
         for (int k = 0; k < 8; ++k) nan |= (in[k] & 0x7FFFFFFFu) > 0x7F800000u;
@@ -262,22 +280,22 @@ __device__ __forceinline__ bool fp8_chunk(const uint32_t* in, float s, u32x4* o)
     return true;
 }
 
-struct KFp8Tensor {
+struct KFp8Tensor : Geom<ST_KIND_FP8_TENSOR> {
     static constexpr int SCALE = 1;  // D.scale
-    static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
+    static constexpr uint32_t CH = stk::kWordsFp8 / 2;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, u32x4* o) {
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t, u32x4* o) {
         return fp8_chunk(in, c.s, o);
     }
 };
 
-struct KFp8Block {
+struct KFp8Block : Geom<ST_KIND_FP8_BLOCK128> {
     static constexpr int SCALE = 0;  // no scalar scale
-    static constexpr uint32_t CE = 16, IB = 16, LG = 16, CH = stk::kWordsFp8 / 2;
+    static constexpr uint32_t CH = stk::kWordsFp8 / 2;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    // e: first element of the chunk (a multiple of 16); with cols % 16 == 0 the chunk lies in
-    // one row and one 128-column block, otherwise it takes the exact path.
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, u32x4* o) {
+    // e: first output element of the chunk (a multiple of 16); with cols % 16 == 0 the chunk lies
+    // in one row and one 128-column block, otherwise it takes the exact path.
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, uint64_t, u32x4* o) {
         if ((c.D.cols & 15u) != 0) return false;
         const uint32_t e32 = uint32_t(e);
         const uint32_t row = stk::div_apply(e32, c.D.div_magic, c.D.div_shift);
@@ -287,13 +305,14 @@ struct KFp8Block {
     }
 };
 
-struct KFp4 {
+struct KFp4 : Geom<ST_KIND_NVFP4> {
     static constexpr int SCALE = 2;  // D.scale2
-    static constexpr uint32_t CE = 8, IB = 4, LG = 4, CH = stk::kWordsFp4;
+    static constexpr uint32_t CH = stk::kWordsFp4;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
-    // 8 elements: (e2m1 * block scale) is exact in fp32, then one RNE multiply by g
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, u32x4* o) {
-        const uint32_t code = ld_u8(c.blob + c.D.scale + (e >> 4));  // block scale of these 8 elements
+    // 8 elements from source element x: (e2m1 * block scale) is exact in fp32, then one RNE
+    // multiply by g
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, u32x4* o) {
+        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 4));  // block scale of these 8 elements
         if (!finite(c.s) || (code & 0x7Fu) == 0x7Fu) return false;
         const float bs = fp8x2<false>(code).x;
         const float g = c.s;
@@ -304,6 +323,8 @@ struct KFp4 {
         return true;
     }
 };
+
+static_assert(KPass::IB == 16 && KF32::IB == 32 && KFp8Tensor::IB == 16 && KFp4::IB == 4, "chunk geometry");
 
 // ------------------------------------------------------------------------- loads
 
@@ -379,7 +400,7 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
         F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
         u32x4 v[OW];
-        ok[j] = c.vec && K::fast(c, in, e, v);
+        ok[j] = c.vec && K::fast(c, in, e, e, v);
         if (ok[j]) {
 #pragma unroll
             for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
@@ -410,7 +431,7 @@ __device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cn
         F::align(raw, sh, in);
         const uint64_t e = e0 + uint64_t(ci) * K::CE;
         u32x4 v[OW];
-        if (c.vec && K::fast(c, in, e, v)) {
+        if (c.vec && K::fast(c, in, e, e, v)) {
 #pragma unroll
             for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
         } else {
@@ -419,6 +440,85 @@ __device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cn
     }
     for (uint32_t t = nch * K::CE + lane; t < cnt; t += stk::kWave)  // past the last whole chunk
         out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
+}
+
+// A unit of a column slice: chunk starts are mapped to their source elements one by one (the
+// host guarantees that a chunk never crosses a row and that every chunk has the alignment of the
+// slice's first source byte, or marks the descriptor exact-only).  A whole unit issues all of a
+// lane's loads before decoding, like unit_full; a partial one walks its chunks.
+template <class K, bool ALIGNED>
+__device__ __forceinline__ void unit_strided(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, ALIGNED>;
+    constexpr uint32_t OW = K::CE / stk::kWordElems;
+    const uint8_t* base = c0.blob + c0.D.src - sh;
+    if (cnt == K::CE * K::CH * stk::kWave) {
+        uint32_t raw[K::CH][F::RW];
+        uint64_t xs[K::CH];
+#pragma unroll
+        for (uint32_t j = 0; j < K::CH; ++j) {
+            xs[j] = src_elem(c0.D, e0 + uint64_t(j * stk::kWave + lane) * K::CE);
+            F::load(base + K::src_off(xs[j]), 0, raw[j]);
+        }
+        Ctx c = c0;
+        uint16_t* out;
+        if (!finish_ctx<K>(c, out)) return;
+        bool ok[K::CH];
+#pragma unroll
+        for (uint32_t j = 0; j < K::CH; ++j) {
+            uint32_t in[F::N];
+            F::align(raw[j], sh, in);
+            const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+            u32x4 v[OW];
+            ok[j] = c.vec && K::fast(c, in, e, xs[j], v);
+            if (ok[j]) {
+#pragma unroll
+                for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
+            }
+        }
+        bool all = true;
+#pragma unroll
+        for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+        if (__builtin_amdgcn_ballot_w64(!all) == 0) return;
+#pragma unroll
+        for (uint32_t j = 0; j < K::CH; ++j)
+            if (!ok[j]) chunk_exact(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
+        return;
+    }
+    Ctx c = c0;
+    uint16_t* out;
+    if (!finish_ctx<K>(c, out)) return;
+    const uint32_t nch = cnt / K::CE;
+    for (uint32_t ci = lane; ci < nch; ci += stk::kWave) {
+        const uint64_t e = e0 + uint64_t(ci) * K::CE;
+        const uint64_t x = src_elem(c.D, e);
+        uint32_t raw[F::RW], in[F::N];
+        F::load(base + K::src_off(x), 0, raw);
+        F::align(raw, sh, in);
+        u32x4 v[OW];
+        if (c.vec && K::fast(c, in, e, x, v)) {
+#pragma unroll
+            for (uint32_t w = 0; w < OW; ++w) *reinterpret_cast<u32x4*>(out + e + w * stk::kWordElems) = v[w];
+        } else {
+            chunk_exact(c, out, e, K::CE);
+        }
+    }
+    for (uint32_t t = nch * K::CE + lane; t < cnt; t += stk::kWave)
+        out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
+}
+
+template <class K>
+__device__ __forceinline__ void run_strided(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
+    const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src));
+    if ((a & (K::LG - 1)) == 0) unit_strided<K, true>(c, e0, cnt, 0, lane);
+    else unit_strided<K, false>(c, e0, cnt, a & 3u, lane);
+}
+
+// Every element of a unit through the exact path (descriptors the host marks exact-only).
+__device__ __forceinline__ void unit_exact(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t lane) {
+    Ctx c = c0;
+    uint16_t* out = ld_uniform<uint16_t*>(c.outs + c.D.out);
+    if (reinterpret_cast<uintptr_t>(out) & 1u) return;
+    for (uint32_t t = lane; t < cnt; t += stk::kWave) out[e0 + t] = uint16_t(elem_exact(c.blob, c.D, e0 + t));
 }
 
 template <class K, bool ALIGNED>
@@ -438,6 +538,10 @@ __device__ __forceinline__ void run_unit(const Ctx& c, uint64_t e0, uint32_t cnt
 
 // ------------------------------------------------------------------------- the kernel
 
+// SLICES: the instance that runs column slices through the strided fast path.  The plain instance
+// sends them (and exact-only descriptors) through the per-element exact path; keeping the strided
+// code out of it was measured to matter (2-5% on the whole-checkpoint decode).
+template <bool SLICES>
 __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __restrict__ blob,
                                                              const uint8_t* __restrict__ table, uint32_t units,
                                                              uint32_t groups, uint32_t desc_off,
@@ -468,6 +572,21 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     c.D = D;
     c.outs = outs;
     c.scale_al = (D.scale & 3u) == 0;
+    if ((D.pitch | D.flags) != 0) {  // column slices and exact-only descriptors
+        if (!SLICES || (D.flags & ST_DESC_EXACT)) {
+            unit_exact(c, e0, cnt, lane);
+            return;
+        }
+        switch (D.kind) {
+            case ST_KIND_FP8_TENSOR: run_strided<KFp8Tensor>(c, e0, cnt, lane); break;
+            case ST_KIND_FP8_BLOCK128: run_strided<KFp8Block>(c, e0, cnt, lane); break;
+            case ST_KIND_NVFP4: run_strided<KFp4>(c, e0, cnt, lane); break;
+            case ST_KIND_PASS_BF16: run_strided<KPass>(c, e0, cnt, lane); break;
+            case ST_KIND_CAST_F16: run_strided<KF16>(c, e0, cnt, lane); break;
+            default: run_strided<KF32>(c, e0, cnt, lane); break;
+        }
+        return;
+    }
     switch (D.kind) {
         case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor>(c, e0, cnt, lane); break;
         case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block>(c, e0, cnt, lane); break;
@@ -478,22 +597,32 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     }
 }
 
-}  // namespace
-
-extern "C" st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {
+template <bool SLICES>
+st_status launch(const char* who, const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {
     if (n == 0) return ST_OK;
-    if (!blob || !descs || !outs) return st_fail(ST_E_ARG, "st_materialize: null pointer");
+    if (!blob || !descs || !outs) return st_fail(ST_E_ARG, "%s: null pointer", who);
     if (reinterpret_cast<uintptr_t>(blob) % ST_BLOB_ALIGN)
-        return st_fail(ST_E_ARG, "st_materialize: blob is not %d-byte aligned", ST_BLOB_ALIGN);
-    if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "st_materialize: work table is not 64-byte aligned");
-    if (uint64_t(n) >= (uint64_t(1) << 32)) return st_fail(ST_E_ARG, "st_materialize: %zu work units (at most 2^32 - 1)", n);
+        return st_fail(ST_E_ARG, "%s: blob is not %d-byte aligned", who, ST_BLOB_ALIGN);
+    if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "%s: work table is not 64-byte aligned", who);
+    if (uint64_t(n) >= (uint64_t(1) << 32)) return st_fail(ST_E_ARG, "%s: %zu work units (at most 2^32 - 1)", who, n);
     const uint32_t groups = uint32_t((uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP);
     const uint32_t gx = groups < kMaxGridX ? groups : kMaxGridX;
     const uint32_t gy = (groups + gx - 1) / gx;
-    hipLaunchKernelGGL(materialize_kernel, dim3(gx, gy), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(materialize_kernel<SLICES>, dim3(gx, gy), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint8_t*>(blob), static_cast<const uint8_t*>(descs), uint32_t(n), groups,
                        uint32_t(stk::table_desc_offset(groups)), reinterpret_cast<uint16_t* const*>(outs));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return st_fail(ST_E_HIP, "st_materialize: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return st_fail(ST_E_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
     return ST_OK;
+}
+
+}  // namespace
+
+extern "C" st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {
+    return launch<false>("st_materialize", blob, descs, n, outs, stream);
+}
+
+extern "C" st_status st_materialize_slices(const void* blob, const void* descs, size_t n, void* const* outs,
+                                           void* stream) {
+    return launch<true>("st_materialize_slices", blob, descs, n, outs, stream);
 }

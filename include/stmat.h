@@ -129,17 +129,21 @@ typedef struct st_desc {
     uint64_t src;            /* weight bytes */
     uint64_t scale;          /* FP8_TENSOR fp32 scale / FP8_BLOCK128 fp32 grid / NVFP4 e4m3 block scales */
     uint64_t scale2;         /* NVFP4 fp32 global scale */
-    uint64_t numel;          /* output elements */
+    uint32_t pitch;          /* column slice: source elements from one output row to the next
+                                (the full row length); 0 = the output's source is contiguous */
+    uint32_t flags;          /* ST_DESC_EXACT: every element takes the exact per-element path */
     uint32_t unit_begin;     /* this output's first work unit in the table */
     uint32_t unit_end;       /* one past its last work unit */
     uint32_t tail;           /* elements in its last unit (1 .. 2^unit_shift) */
     uint32_t out;            /* index into the outs[] pointer array */
-    uint32_t cols;           /* FP8_BLOCK128: N, NVFP4: K, otherwise 0 */
-    uint32_t grid_cols;      /* FP8_BLOCK128: ceil(N / 128) */
-    uint32_t div_magic;      /* FP8_BLOCK128: multiplier of the exact division by N */
+    uint32_t cols;           /* FP8_BLOCK128: N, NVFP4: K, a column slice: its width; otherwise 0 */
+    uint32_t grid_cols;      /* FP8_BLOCK128: ceil(N / 128) of the whole tensor */
+    uint32_t div_magic;      /* FP8_BLOCK128 or a column slice: multiplier of the exact division
+                                by cols */
     uint32_t meta;           /* st_kind | unit_shift << 8 | div_shift << 16 (a unit is
                                 2^unit_shift elements; div_shift goes with div_magic) */
 } st_desc;                   /* 64 bytes */
+#define ST_DESC_EXACT 1u     /* st_desc.flags */
 
 /* Planning options; pass NULL for the defaults. */
 typedef struct st_plan_opts {
@@ -207,6 +211,33 @@ const void* st_index_table(const st_index* idx, size_t* bytes, uint64_t* units);
  * at least that size.  Used for on-demand loads of single tensors. */
 st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t k, void* dst,
                                 size_t dst_bytes, size_t* bytes, uint64_t* units);
+
+/* ---- Sliced materialisation (tensor-parallel shards) ---------------------------------------------
+ * A slice is a block of rows and columns of one output, seen as a matrix: an output of shape
+ * [d0, d1, ...] is [d0, d1 * d2 * ...] (a 1-d output [n] is [n, 1], a scalar [1, 1]).  Slice j
+ * materialises rows [row_begin, row_end) and columns [col_begin, col_end) as one contiguous
+ * row-major bf16 array of (row_end - row_begin) * (col_end - col_begin) elements, written to
+ * outs[j]; its values are exactly the corresponding elements of the whole output.  Row slices keep
+ * the source contiguous; column slices read every source row at a pitch (the pages name tensor
+ * slicing among the metadata an index must carry: "FastSageTensors capability audit").
+ * Cuts respect the scale blocks: FP8_BLOCK128 row_begin and col_begin are multiples of 128; NVFP4
+ * col_begin and the slice width are multiples of 16.  A column slice needs fewer than 2^32 output
+ * elements and a row length below 2^32.  Column slices whose chunks would cross rows or lose a
+ * common alignment take the exact per-element path (correct, slower). */
+typedef struct {
+    uint32_t output;         /* output index */
+    uint32_t reserved;       /* 0 */
+    int64_t row_begin, row_end;   /* row_end < 0: to the last row */
+    int64_t col_begin, col_end;   /* col_end < 0: to the last column */
+} st_slice;
+
+/* Work table for slices[0..k) over the data-section blob (descriptor j writes outs[j]).  Same
+ * size-query convention as st_index_table_subset.  ST_E_ARG for an out-of-range output or
+ * bounds, ST_E_SHAPE for a cut that splits a scale block or a column slice too large. */
+st_status st_index_table_slices(const st_index* idx, const st_slice* slices, size_t k, void* dst,
+                                size_t dst_bytes, size_t* bytes, uint64_t* units);
+/* Elements of slice `s` once its bounds are resolved (rows * cols), or ST_E_ARG. */
+st_status st_index_slice_numel(const st_index* idx, const st_slice* s, uint64_t* rows, uint64_t* cols);
 
 /* Stage the data section of the file at `path` into `blob_dev` (device memory of at least
  * st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned).  Reads the file in chunks into the
@@ -333,6 +364,13 @@ st_status st_read_plans(const char* path, const st_index* idx, const st_stream_p
  * n == 0 is a no-op. */
 st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs,
                          void* stream);
+
+/* st_materialize for tables that hold column slices (st_index_table_slices): the same arguments
+ * and results, with column slices on the strided fast path.  st_materialize decodes such tables
+ * correctly too, one element at a time; this entry point is a separate kernel so that the
+ * whole-output kernel carries no strided code. */
+st_status st_materialize_slices(const void* blob, const void* descs, size_t n, void* const* outs,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,124 @@
+"""GPU parity of sliced materialisation: each slice equals the same block of the oracle's whole
+output, bit for bit, for row slices, column slices (fast and exact-only), empty and edge slices of
+every kind; and tensor-parallel shards (8 row shards, 8 column shards where the cuts allow)
+reassemble the whole output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import device_checkpoint_dequantisation_amd as st
+from tests.st_files import make_file
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _staged(buf):
+    ix = st.SafeTensorIndex.from_bytes(buf)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    ck.load_bytes(buf[ix.data_offset:])
+    return ix, ck
+
+
+def _view(w):
+    """The oracle's whole output as the slicing matrix view."""
+    if w.ndim == 0:
+        return w.reshape(1, 1)
+    if w.ndim == 1:
+        return w.reshape(-1, 1)
+    return w.reshape(w.shape[0], -1)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _slices_for(o, rng):
+    """A spread of slices the cuts allow for output o."""
+    shape = o.shape
+    R = 1 if not shape else shape[0]
+    C = 1 if len(shape) <= 1 else int(np.prod(shape[1:]))
+    rq = 128 if o.kind == "FP8_BLOCK128" else 1
+    cq = 128 if o.kind == "FP8_BLOCK128" else 16 if o.kind == "NVFP4" else 1
+    wq = 16 if o.kind == "NVFP4" else 1
+    out = [(None, None), ((0, 0), None)]
+    for _ in range(4):
+        r0 = int(rng.integers(0, R // rq + 1)) * rq
+        r1 = int(rng.integers(r0, R + 1))
+        c0 = int(rng.integers(0, C // cq + 1)) * cq
+        wmax = (C - c0) // wq
+        c1 = c0 + int(rng.integers(0, wmax + 1)) * wq
+        out += [((r0, r1), None), ((r0, r1), (c0, c1)), (None, (c0, c1))]
+    if C >= 32 and o.kind not in ("FP8_BLOCK128",):
+        out.append(((0, min(R, 3)), (0, C // 2 // wq * wq)))
+    return out
+
+
+@pytest.mark.parametrize("strided_kernel", [True, False])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_slices_match_the_oracle(k, strided_kernel):
+    buf = synth.config_bytes(k, small=k != 1)
+    want = oracle.materialize(buf)
+    ix, ck = _staged(buf)
+    rng = np.random.default_rng(k)
+    outs = ix.outputs()
+    picks = range(len(outs)) if len(outs) <= 60 else rng.choice(len(outs), 60, replace=False)
+    slices = []
+    for kk in picks:
+        for rows, cols in _slices_for(outs[int(kk)], rng):
+            slices.append((int(kk), rows, cols))
+    print(f"slices c{k}: {len(slices)} (strided kernel {strided_kernel})", flush=True)
+    got = ck.materialize_slices(slices, strided_kernel=strided_kernel)
+    torch.cuda.synchronize()
+    for (kk, rows, cols), t in zip(slices, got):
+        w = _view(want[outs[kk].name])
+        r0, r1 = rows if rows else (0, w.shape[0])
+        c0, c1 = cols if cols else (0, w.shape[1])
+        assert tuple(t.shape) == (r1 - r0, c1 - c0)
+        assert np.array_equal(_bits(t).reshape(r1 - r0, c1 - c0), w[r0:r1, c0:c1]), (outs[kk].name, rows, cols)
+
+
+def test_exact_only_column_slices():
+    # rows of 60 (bf16) and 24 (f32) bytes break the word alignment; widths that split chunks
+    rng = np.random.default_rng(9)
+    b = rng.integers(0, 1 << 16, size=(7, 30), dtype=np.uint16)
+    b[b & 0x7F80 == 0x7F80] = 0x3F80   # no NaN payloads in the passthrough source
+    f = rng.standard_normal((5, 6)).astype(np.float32)
+    h = rng.standard_normal((4, 33)).astype(np.float16)
+    buf = make_file([("b", "BF16", (7, 30), b), ("f", "F32", (5, 6), f), ("h", "F16", (4, 33), h)])
+    want = oracle.materialize(buf)
+    ix, ck = _staged(buf)
+    slices = [(0, None, (2, 9)), (0, (1, 6), (0, 30)), (1, (0, 5), (1, 4)), (2, None, (5, 30)), (2, (3, 4), (0, 33))]
+    got = ck.materialize_slices(slices)
+    torch.cuda.synchronize()
+    names = [o.name for o in ix.outputs()]
+    for (kk, rows, cols), t in zip(slices, got):
+        w = _view(want[names[kk]])
+        r0, r1 = rows if rows else (0, w.shape[0])
+        c0, c1 = cols if cols else (0, w.shape[1])
+        assert np.array_equal(_bits(t).reshape(r1 - r0, c1 - c0), w[r0:r1, c0:c1]), (names[kk], rows, cols)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_tensor_parallel_shards_reassemble(k):
+    buf = synth.config_bytes(k, small=True)
+    want = oracle.materialize(buf)
+    ix, ck = _staged(buf)
+    for kk, o in enumerate(ix.outputs()):
+        if len(o.shape) != 2:
+            continue
+        R, C = o.shape
+        q = 128 if o.kind == "FP8_BLOCK128" else 16 if o.kind == "NVFP4" else 1
+        for axis, n in ((0, R), (1, C)):
+            if o.kind == "FP8_BLOCK128" and n % (8 * 128):
+                parts = [(b, min(n, b + 128)) for b in range(0, n, 128)]   # one shard per block row/col
+            else:
+                step = -(-n // 8 // q) * q if q > 1 else -(-n // 8)
+                parts = [(b, min(n, b + step)) for b in range(0, n, step)]
+            sl = [(kk, p, None) if axis == 0 else (kk, None, p) for p in parts]
+            got = ck.materialize_slices(sl)
+            torch.cuda.synchronize()
+            whole = np.concatenate([_bits(t).reshape(t.shape) for t in got], axis=axis)
+            assert np.array_equal(whole, want[o.name]), (o.name, axis)

@@ -61,7 +61,8 @@ def test_tiny_traffic_is_the_documented_figure():
 
 STEP_SHIFT = {"PASS_BF16": 10, "CAST_F16": 10, "CAST_F32": 9, "FP8_TENSOR": 10, "FP8_BLOCK128": 10, "NVFP4": 11}
 
-DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("numel", "<u8"), ("unit_begin", "<u4"),
+DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("pitch", "<u4"), ("flags", "<u4"),
+                 ("unit_begin", "<u4"),
                  ("unit_end", "<u4"), ("tail", "<u4"), ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"),
                  ("div_magic", "<u4"), ("kind", "u1"), ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1")])
 HEADER = np.dtype([("magic", "<u4"), ("n_desc", "<u4"), ("units", "<u8"), ("desc_offset", "<u8"),
@@ -78,12 +79,13 @@ def _table(raw: bytes):
     return h, d, m
 
 
-def _check_map(d, m, units):
+def _check_map(d, m, units, numels):
     # every group of 4 units maps to the descriptor holding its first unit
-    ends = d["unit_begin"].astype(np.int64) + (-(-d["numel"].astype(np.int64) // (1 << d["unit_shift"].astype(np.int64))))
+    numels = np.asarray(numels, dtype=np.int64)
+    ends = d["unit_begin"].astype(np.int64) + (-(-numels // (1 << d["unit_shift"].astype(np.int64))))
     assert np.array_equal(ends, d["unit_end"].astype(np.int64))
-    for row in d:   # the last unit's length
-        n, sh = int(row["numel"]), int(row["unit_shift"])
+    for row, n in zip(d, numels):   # the last unit's length
+        n, sh = int(n), int(row["unit_shift"])
         if n:
             assert row["tail"] == n - ((-(-n // (1 << sh)) - 1) << sh) and 1 <= row["tail"] <= 1 << sh
     for g, di in enumerate(m):
@@ -103,7 +105,7 @@ def test_table_invariants(scale):
     assert h["units"] == units and h["n_desc"] == len(outs) == len(d)
     pos = 0
     for k, (row, o) in enumerate(zip(d, outs)):
-        assert row["out"] == k and row["numel"] == o.numel and _lib.KINDS[row["kind"]] == o.kind
+        assert row["out"] == k and row["pitch"] == 0 and row["flags"] == 0 and _lib.KINDS[row["kind"]] == o.kind
         assert row["src"] == ents[o.tensor].begin
         if o.scale >= 0:
             assert row["scale"] == ents[o.scale].begin
@@ -115,7 +117,7 @@ def test_table_invariants(scale):
         if o.kind == "FP8_BLOCK128":
             assert row["cols"] == o.shape[1] and row["grid_cols"] == -(-o.shape[1] // 128)
     assert pos == units
-    _check_map(d, m, units)
+    _check_map(d, m, units, [o.numel for o in outs])
     # arena: 256-byte aligned, disjoint, in order
     offs = [o.offset for o in outs]
     assert all(x % 256 == 0 for x in offs)
@@ -128,10 +130,11 @@ def test_table_invariants(scale):
 def test_map_with_empty_and_tiny_outputs():
     f = make_file([("e", "BF16", (0,), b""), ("a", "F32", (3,), f32_bytes(1, 2, 3)), ("z", "F16", (0, 7), b""),
                    ("b", "BF16", (2000,), b"\0" * 4000), ("c", "BF16", (1,), b"\0\0"), ("y", "BF16", (0,), b"")])
-    raw, units = st.SafeTensorIndex.from_bytes(f).table()
+    ix = st.SafeTensorIndex.from_bytes(f)
+    raw, units = ix.table()
     h, d, m = _table(raw)
     assert units == 1 + 2 + 1
-    _check_map(d, m, units)
+    _check_map(d, m, units, [o.numel for o in ix.outputs()])
     raw, units = st.SafeTensorIndex.from_bytes(make_file([])).table()
     h, d, m = _table(raw)
     assert units == 0 and len(d) == 0 and len(m) == 0
@@ -167,12 +170,14 @@ def test_subset_table_is_self_contained():
     h, d, m = _table(raw)
     assert h["n_desc"] == 4
     pos = 0
+    outs = ix.outputs()
     for j, s in enumerate(sel):
-        assert d[j]["out"] == j and d[j]["src"] == full[s]["src"] and d[j]["numel"] == full[s]["numel"]
+        assert d[j]["out"] == j and d[j]["src"] == full[s]["src"] and d[j]["unit_end"] - d[j]["unit_begin"] == \
+            full[s]["unit_end"] - full[s]["unit_begin"] and d[j]["tail"] == full[s]["tail"]
         assert d[j]["unit_begin"] == pos
-        pos += -(-int(d[j]["numel"]) // (1 << int(d[j]["unit_shift"])))
+        pos += -(-outs[s].numel // (1 << int(d[j]["unit_shift"])))
     assert units == pos
-    _check_map(d, m, units)
+    _check_map(d, m, units, [outs[s].numel for s in sel])
     with pytest.raises(st.StError):
         ix.table_subset([10 ** 6])
 

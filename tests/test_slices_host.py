@@ -1,0 +1,97 @@
+"""Slice tables on the CPU (st_index_table_slices): matrix views, descriptor fields of row and
+column slices of every kind, the exact-only flag, and the cuts that are refused."""
+import numpy as np
+import pytest
+
+import synth
+import device_checkpoint_dequantisation_amd as st
+from device_checkpoint_dequantisation_amd import _lib
+from tests.st_files import f32_bytes, make_file
+from tests.test_index import _table
+
+
+@pytest.fixture(scope="module")
+def ix3():
+    return st.SafeTensorIndex.from_bytes(synth.config_bytes(3, small=True))
+
+
+def _k(ix, name):
+    return next(k for k, o in enumerate(ix.outputs()) if o.name == name)
+
+
+def test_matrix_views():
+    buf = make_file([("s", "BF16", (), b"\0\0"), ("v", "BF16", (10,), b"\0" * 20),
+                     ("t", "BF16", (2, 3, 4), b"\0" * 48), ("z", "BF16", (0, 5), b"")])
+    ix = st.SafeTensorIndex.from_bytes(buf)
+    assert ix.slice_shape(_k(ix, "s")) == (1, 1)
+    assert ix.slice_shape(_k(ix, "v")) == (10, 1) and ix.slice_shape(_k(ix, "v"), (2, 7)) == (5, 1)
+    assert ix.slice_shape(_k(ix, "t")) == (2, 12) and ix.slice_shape(_k(ix, "t"), (1, 2), (4, 10)) == (1, 6)
+    assert ix.slice_shape(_k(ix, "z")) == (0, 5)
+
+
+def test_row_and_column_slice_descriptors(ix3):
+    ents = ix3.tensors()
+    q = _k(ix3, "model.layers.0.self_attn.q_proj.weight")      # FP8_BLOCK128 [320, 320]
+    emb = _k(ix3, "model.embed_tokens.weight")                   # BF16 [1000, 320]
+    o_q, o_e = ix3.output(q), ix3.output(emb)
+    raw, units = ix3.table_slices([(q, (128, 320), None), (q, (0, 320), (128, 256)), (emb, (10, 20), (3, 11)),
+                                   (emb, (5, 6), None)])
+    h, d, m = _table(raw)
+    gc = -(-320 // 128)
+    # row slice of block FP8: contiguous, scale grid advanced by one block row
+    assert d[0]["pitch"] == 0 and d[0]["flags"] == 0 and d[0]["cols"] == 320
+    assert d[0]["src"] == ents[o_q.tensor].begin + 128 * 320
+    assert d[0]["scale"] == ents[o_q.scale].begin + 4 * (1 * gc)
+    # column slice of block FP8: pitch = row length, width = 128, grid advanced by one block column
+    assert d[1]["pitch"] == 320 and d[1]["cols"] == 128 and d[1]["flags"] == 0 and d[1]["grid_cols"] == gc
+    assert d[1]["src"] == ents[o_q.tensor].begin + 128 and d[1]["scale"] == ents[o_q.scale].begin + 4
+    # a bf16 column slice 8 wide: whole chunks, rows of 640 bytes: fast path
+    assert d[2]["pitch"] == 320 and d[2]["cols"] == 8 and d[2]["flags"] == 0
+    assert d[2]["src"] == ents[o_e.tensor].begin + 2 * (10 * 320 + 3)
+    assert d[3]["pitch"] == 0 and d[3]["src"] == ents[o_e.tensor].begin + 2 * 5 * 320
+    assert units == 60 + 40 + 1 + 1   # 1024-element units: 61440, 40960, 80 and 320 elements
+    numels = [192 * 320, 320 * 128, 10 * 8, 320]
+    from tests.test_index import _check_map
+    _check_map(d, m, units, numels)
+
+
+def test_exact_only_when_chunks_would_split():
+    w = np.arange(6 * 30, dtype=np.uint16)
+    buf = make_file([("b", "BF16", (6, 30), w), ("f", "F32", (4, 6), np.arange(24, dtype=np.float32))])
+    ix = st.SafeTensorIndex.from_bytes(buf)
+    raw, _ = ix.table_slices([(0, None, (0, 8)), (0, None, (2, 9)), (1, None, (0, 3))])
+    _, d, _ = _table(raw)
+    # bf16 rows of 60 bytes are not whole 16-byte words: exact only, whatever the width
+    assert d[0]["flags"] == _lib.DESC_EXACT and d[1]["flags"] == _lib.DESC_EXACT
+    assert d[2]["flags"] == _lib.DESC_EXACT   # width 3 is not a whole 8-element chunk
+
+
+def test_nvfp4_slices():
+    ix = st.SafeTensorIndex.from_bytes(synth.config_bytes(4, small=True))
+    k, o = next((k, o) for k, o in enumerate(ix.outputs()) if o.kind == "NVFP4")
+    ents = ix.tensors()
+    M, K = o.shape
+    raw, _ = ix.table_slices([(k, (3, 9), (16, 48))])
+    _, d, _ = _table(raw)
+    first = 3 * K + 16
+    assert d[0]["pitch"] == K and d[0]["cols"] == 32 and d[0]["flags"] == 0
+    assert d[0]["src"] == ents[o.tensor].begin + first // 2 and d[0]["scale"] == ents[o.scale].begin + first // 16
+    with pytest.raises(st.StError, match="multiples of 16"):
+        ix.table_slices([(k, None, (8, 40))])
+    with pytest.raises(st.StError, match="multiples of 16"):
+        ix.table_slices([(k, None, (16, 40))])
+
+
+def test_refused_cuts(ix3):
+    q = _k(ix3, "model.layers.0.self_attn.q_proj.weight")
+    with pytest.raises(st.StError, match="multiples of 128"):
+        ix3.table_slices([(q, (64, 320), None)])
+    with pytest.raises(st.StError, match="multiples of 128"):
+        ix3.table_slices([(q, None, (100, 200))])
+    with pytest.raises(st.StError, match="outside"):
+        ix3.table_slices([(q, (0, 321), None)])
+    with pytest.raises(st.StError, match="outside"):
+        ix3.table_slices([(q, (10, 5), None)])
+    with pytest.raises(st.StError, match="ST_E_ARG"):
+        ix3.table_slices([(10 ** 6, None, None)])
+    ix3.table_slices([(q, (128, 128), None)])   # empty slices are fine
