@@ -21,8 +21,8 @@ from dataclasses import dataclass
 from ._lib import (DTYPES, KINDS, PLAN_PACK, Desc, OutputInfo, PlanOpts, Slice, StError, StreamStats,  # noqa: F401
                    StreamStep, TensorMeta, check, lib)
 
-__all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "load", "materialize", "stage_file", "stream_file",
-           "read_plans", "StError", "KINDS"]
+__all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
+           "stage_file", "stream_file", "read_plans", "StError", "KINDS"]
 
 
 @dataclass(frozen=True)
@@ -321,6 +321,54 @@ def stream_file(path: str, index: SafeTensorIndex, plan: StreamPlan, blob, table
             "steps": st.steps, "launches": st.launches}
 
 
+@dataclass
+class QuantizedWeight:
+    """A quantised weight as stored, for consumers that compute on the quantised form (FP8 matrix
+    cores): no decode, the checkpoint's own bytes on the device.
+      FP8_TENSOR    data float8_e4m3fn [M, N...], scale fp32 []
+      FP8_BLOCK128  data float8_e4m3fn [M, N],    scale fp32 [ceil(M/128), ceil(N/128)] (multiplied)
+      NVFP4         data uint8 [M, K/2] (element 2k in the low nibble of byte k),
+                    scale float8_e4m3fn [M, K/16], scale2 fp32 []"""
+    name: str
+    kind: str
+    shape: tuple        # logical shape of the weight
+    data: object
+    scale: object
+    scale2: object = None
+
+
+def _quantized(index: SafeTensorIndex, blob, k: int, at, copy: bool) -> QuantizedWeight:
+    """QuantizedWeight of output k from a device blob in which tensor t's bytes start at at(t)."""
+    torch = _torch()
+    o = index.output(k)
+    if o.kind not in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4"):
+        raise ValueError(f"{o.name}: {o.kind} is not a quantised weight")
+    ents = index.tensors()
+
+    def raw(i):
+        e = ents[i]
+        return blob[at(i): at(i) + (e.end - e.begin)]
+
+    def f32(i, shape):  # fp32 scales may sit at any byte offset: always a copy
+        return raw(i).clone().view(torch.float32).view(shape)
+
+    w = raw(o.tensor)
+    if o.kind == "NVFP4":
+        m, kk = o.shape
+        data = w.view(m, kk // 2)
+        sc = raw(o.scale).view(torch.float8_e4m3fn).view(m, kk // 16)
+        if copy:
+            data, sc = data.clone(), sc.clone()
+        return QuantizedWeight(o.name, o.kind, tuple(o.shape), data, sc, f32(o.scale2, ()))
+    data = w.view(torch.float8_e4m3fn).view(o.shape)
+    if copy:
+        data = data.clone()
+    if o.kind == "FP8_TENSOR":
+        return QuantizedWeight(o.name, o.kind, tuple(o.shape), data, f32(o.scale, ()))
+    m, n = o.shape
+    return QuantizedWeight(o.name, o.kind, tuple(o.shape), data, f32(o.scale, (-(-m // 128), -(-n // 128))))
+
+
 class DeviceCheckpoint:
     """A checkpoint staged on one GPU: the blob, the descriptor table and a bf16 output arena in
     which every output starts on a 256-byte boundary."""
@@ -401,6 +449,16 @@ class DeviceCheckpoint:
         if data_section:
             host = torch.frombuffer(bytearray(data_section), dtype=torch.uint8)
             self.blob[: len(data_section)].copy_(host)
+
+    def quantized(self, names=None, copy: bool = True) -> dict:
+        """The quantised weights (FP8_TENSOR, FP8_BLOCK128, NVFP4 outputs) as stored, from the
+        staged blob: ``copy=True`` gives fresh, 256-byte aligned tensors; ``copy=False`` gives
+        views into the blob for the weight bytes (the fp32 scales are always copied)."""
+        outs = self.index.outputs()
+        pos = {o.name: k for k, o in enumerate(outs)}
+        want = [o.name for o in outs if o.kind in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4")] if names is None else names
+        ents = self.index.tensors()
+        return {n: _quantized(self.index, self.blob, pos[n], lambda i: ents[i].begin, copy) for n in want}
 
     def materialize_slices(self, slices, stream=None, strided_kernel: bool | None = None) -> list:
         """bf16 tensors [rows, cols] for slices of outputs (see SafeTensorIndex.table_slices),

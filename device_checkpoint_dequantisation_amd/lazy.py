@@ -20,7 +20,7 @@ import time
 from collections.abc import Mapping
 from dataclasses import dataclass
 
-from . import SafeTensorIndex, StreamPlan, _torch, materialize, read_plans, stream_file
+from . import SafeTensorIndex, StreamPlan, _quantized, _torch, materialize, read_plans, stream_file
 
 _ONE_STEP = 1 << 60  # chunk size that keeps a whole selection in one staging step
 
@@ -266,6 +266,22 @@ class StreamStateDict(Mapping):
             else:
                 self._load_direct(metas, outs, s)
         return outs
+
+    def load_quantized(self, names, stream=None) -> dict:
+        """The quantised weights ``names`` as stored (no decode), read with one packed plan into a
+        device blob that the returned weight tensors view; see QuantizedWeight."""
+        torch = _torch()
+        metas = [self._meta[n] for n in names]
+        plan = StreamPlan(self.index, _ONE_STEP, select=[m.index for m in metas], pack=True)
+        host = torch.empty(plan.blob_bytes, dtype=torch.uint8, pin_memory=True)
+        read_plans(self.path, self.index, [plan], [host])
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(s):
+            blob = torch.empty(plan.blob_bytes, dtype=torch.uint8, device=self.device)
+            blob.copy_(host, non_blocking=True)
+            ents = self.index.tensors()
+            return {m.name: _quantized(self.index, blob, m.index, lambda i: plan.tensor_offset(ents[i].begin), False)
+                    for m in metas}
 
     def _load_direct(self, metas, outs, s):
         """One packed plan over the outputs, streamed: the steps are read into a pinned ring, copied
