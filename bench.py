@@ -82,6 +82,8 @@ def parse():
                     help="also measure, for the main config, the serial vs streamed end-to-end load, on-demand "
                          "per-layer loads and tensor-parallel shard decodes (they launch the kernel on other tables, "
                          "so a kernel-trace summary of the default command covers only the timed decode)")
+    ap.add_argument("--out-types", action="store_true",
+                    help="also time the fp16 and fp32 output types on the same checkpoint")
     ap.add_argument("--tmpdir", default=None)
     ap.add_argument("--keep", action="store_true", help="keep generated checkpoint files")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -110,7 +112,7 @@ def gen(k, d, overrides=None):
     return path, dt
 
 
-def sampled_parity(path, ix, ck, rng, per_output=64):
+def sampled_parity(path, ix, ck, rng, per_output=64, out_dtype="bf16"):
     """GPU outputs at random flat indices (plus first and last) against the oracle computed
     element by element on the same indices."""
     import torch
@@ -123,9 +125,11 @@ def sampled_parity(path, ix, ck, rng, per_output=64):
         if o.numel == 0:
             continue
         idx = np.unique(np.concatenate([[0, o.numel - 1], rng.integers(0, o.numel, per_output)]))
-        want = oracle.decode(o, data, idx)
+        want = oracle.decode(o, data, idx, out_dtype)
         t = ck.tensors[o.name].reshape(-1)
-        got = t[torch.from_numpy(idx).to(t.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+        got = t[torch.from_numpy(idx).to(t.device)]
+        got = (got.view(torch.int32).cpu().numpy().view(np.uint32) if out_dtype == "f32"
+               else got.view(torch.int16).cpu().numpy().view(np.uint16))
         if not np.array_equal(got, want):
             return False, checked, o.name
         checked += len(idx)
@@ -200,6 +204,10 @@ def measure(k, d, args, rng, overrides=None):
     load = None
     if k == args.config and args.extras:
         load = end_to_end_loads(path, ix, ck, side, stream, args, rng)
+    types = None
+    if k == args.config and (args.extras or args.out_types):
+        types = out_types(path, ck, args, rng)
+        log(f"[bench] output types: {types}")
     res = {
         "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
         "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
@@ -208,12 +216,45 @@ def measure(k, d, args, rng, overrides=None):
                        "file_to_device_GBps": ix.data_size / stage_s / 1e9, "page_cache": "warm (file just written)"},
                       **(load or {})),
         "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
-        "shards": shards,
+        "shards": shards, "out_types": types,
     }
     res["GBps"] = traffic / (res["ms_per_step"] * 1e-3) / 1e9
     res["kernel_GBps"] = traffic / (res["kernel_ms_mean"] * 1e-3) / 1e9
     del ck
     torch.cuda.empty_cache()
+    return res
+
+
+def out_types(path, ck, args, rng):
+    """The same decode into fp16 and fp32 outputs: tables planned for each type, the blob copied
+    from the bf16 checkpoint, sampled parity against the oracle's rounding to that type, and GB/s
+    over that type's algorithmic bytes (bytes read + 2 or 4 bytes per element written)."""
+    import torch
+    import device_checkpoint_dequantisation_amd as st
+    res = {}
+    for dt in ("f16", "f32"):
+        ix = st.SafeTensorIndex.open(path, args.unit_scale, dt)
+        ck2 = st.DeviceCheckpoint(ix, None, ck.device)
+        ck2.blob.copy_(ck.blob)
+        stream = torch.cuda.current_stream(ck.device)
+        for _ in range(args.warmup):
+            ck2.materialize(stream)
+        torch.cuda.synchronize()
+        ok, checked, bad = sampled_parity(path, ix, ck2, rng, out_dtype=dt)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            ck2.materialize(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[dt] = {"kernel_ms_mean": round(ms, 4), "traffic_bytes": ix.traffic_bytes,
+                   "GBps": round(ix.traffic_bytes / (ms * 1e-3) / 1e9, 2),
+                   "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked}
+        del ck2
+        ix.close()
+        torch.cuda.empty_cache()
     return res
 
 
@@ -392,6 +433,8 @@ def main():
         line["lazy_loads"] = r["lazy"]
     if r.get("shards"):
         line["tp_shards"] = r["shards"]
+    if r.get("out_types"):
+        line["output_types"] = r["out_types"]
     if aligned is not None:
         line["scaled_fp8_all_weights_16B_aligned"] = {"GBps": round(aligned["GBps"], 2),
                                                       "kernel_ms_mean": round(aligned["kernel_ms_mean"], 4),

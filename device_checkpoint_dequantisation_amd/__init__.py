@@ -18,8 +18,8 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import (DTYPES, KINDS, PLAN_PACK, Desc, OutputInfo, PlanOpts, Slice, StError, StreamStats,  # noqa: F401
-                   StreamStep, TensorMeta, check, lib)
+from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, Desc, OutputInfo, PlanOpts, Slice,  # noqa: F401
+                   StError, StreamStats, StreamStep, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
            "stage_file", "stream_file", "read_plans", "StError", "KINDS"]
@@ -53,18 +53,21 @@ class SafeTensorIndex:
         self._h = C.c_void_p(handle)
 
     @classmethod
-    def open(cls, path: str, unit_log2_scale: int = 0) -> "SafeTensorIndex":
+    def open(cls, path: str, unit_log2_scale: int = 0, out_dtype: str = "bf16") -> "SafeTensorIndex":
+        """Index of the file at ``path``; every output is planned as ``out_dtype`` (bf16, f16 or
+        f32)."""
         h = C.c_void_p()
-        opts = PlanOpts(unit_log2_scale, 0)
+        opts = PlanOpts(unit_log2_scale, OUT_DTYPES.index(out_dtype))
         check(lib().st_index_open(os.fsencode(path), C.byref(opts), C.byref(h)), f"st_index_open({path})")
         return cls(h.value)
 
     @classmethod
-    def from_bytes(cls, buf: bytes, file_size: int | None = None, unit_log2_scale: int = 0) -> "SafeTensorIndex":
+    def from_bytes(cls, buf: bytes, file_size: int | None = None, unit_log2_scale: int = 0,
+                   out_dtype: str = "bf16") -> "SafeTensorIndex":
         """Index from the leading bytes of a file (at least 8 + N) of ``file_size`` bytes
         (default: ``buf`` is the whole file)."""
         h = C.c_void_p()
-        opts = PlanOpts(unit_log2_scale, 0)
+        opts = PlanOpts(unit_log2_scale, OUT_DTYPES.index(out_dtype))
         size = len(buf) if file_size is None else file_size
         raw = C.create_string_buffer(bytes(buf), len(buf))
         check(lib().st_index_build(raw, len(buf), size, C.byref(opts), C.byref(h)), "st_index_build")
@@ -82,6 +85,16 @@ class SafeTensorIndex:
             pass
 
     # ---- sizes
+    @property
+    def out_dtype(self) -> str:
+        """Output element type the index plans for: "bf16", "f16" or "f32"."""
+        return OUT_DTYPES[lib().st_index_out_dtype(self._h)]
+
+    @property
+    def torch_dtype(self):
+        torch = _torch()
+        return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[self.out_dtype]
+
     @property
     def data_offset(self) -> int:
         return lib().st_index_data_offset(self._h)
@@ -284,15 +297,16 @@ def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> 
     return secs.value
 
 
-def materialize(blob, table, units: int, outs, stream=None, slices: bool = False):
-    """Enqueue the grouped kernel: ``blob`` (the staged data section), ``table`` (a work table) and
-    ``outs`` (device pointers, int64) are device tensors; ``units`` is the table's work-unit count.
-    ``slices`` selects the kernel with the strided path for column slices (st_materialize_slices)."""
+def materialize(blob, table, units: int, outs, stream=None, slices: bool = False, out_dtype: str = "bf16"):
+    """Enqueue the grouped kernel (st_materialize_as): ``blob`` (the staged data section),
+    ``table`` (a work table) and ``outs`` (device pointers, int64) are device tensors; ``units`` is
+    the table's work-unit count; ``out_dtype`` the output type the table was planned for;
+    ``slices`` selects the kernel with the strided path for column slices."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
-    fn, name = (lib().st_materialize_slices, "st_materialize_slices") if slices else (lib().st_materialize, "st_materialize")
-    check(fn(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units, C.c_void_p(outs.data_ptr()),
-             C.c_void_p(s.cuda_stream)), name)
+    check(lib().st_materialize_as(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
+                                  C.c_void_p(outs.data_ptr()), OUT_DTYPES.index(out_dtype), MAT_SLICES if slices else 0,
+                                  C.c_void_p(s.cuda_stream)), "st_materialize_as")
 
 
 def read_plans(path: str, index: SafeTensorIndex, plans, hosts) -> float:
@@ -389,13 +403,15 @@ class DeviceCheckpoint:
         table, units = index.table()
         self.units = units
         self.table = torch.frombuffer(bytearray(table), dtype=torch.uint8).to(self.device)
-        self.arena = torch.empty(max(1, index.arena_bytes // 2), dtype=torch.bfloat16, device=self.device)
+        dt = index.torch_dtype
+        esize = 4 if index.out_dtype == "f32" else 2
+        self.arena = torch.empty(max(1, index.arena_bytes // esize), dtype=dt, device=self.device)
         outs = index.outputs()
         base = self.arena.data_ptr()
         self.outs = torch.tensor([base + o.offset for o in outs] or [0], dtype=torch.int64).to(self.device)
         self.tensors = {}
         for o in outs:
-            start = o.offset // 2
+            start = o.offset // esize
             self.tensors[o.name] = self.arena[start: start + o.numel].view(o.shape)
         self.stage_seconds_read = None
         if path is not None:
@@ -468,27 +484,29 @@ class DeviceCheckpoint:
         torch = _torch()
         slices = list(slices)
         shapes = [self.index.slice_shape(*((sl + (None, None))[:3] if isinstance(sl, tuple) else (sl,))) for sl in slices]
-        outs = [torch.empty(shp, dtype=torch.bfloat16, device=self.device) for shp in shapes]
+        outs = [torch.empty(shp, dtype=self.index.torch_dtype, device=self.device) for shp in shapes]
         raw, units = self.index.table_slices(slices)
         if strided_kernel is None:
             strided_kernel = self.index.has_column_slices(slices)
         table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
         ptrs = torch.tensor([o.data_ptr() for o in outs] or [0], dtype=torch.int64).to(self.device)
         if units:
-            materialize(self.blob, table, units, ptrs, stream, slices=strided_kernel)
+            materialize(self.blob, table, units, ptrs, stream, slices=strided_kernel, out_dtype=self.index.out_dtype)
         return outs
 
     def materialize(self, stream=None):
         if self.units:
-            materialize(self.blob, self.table, self.units, self.outs, stream)
+            materialize(self.blob, self.table, self.units, self.outs, stream, out_dtype=self.index.out_dtype)
         return self.tensors
 
 
-def load(path: str, device="cuda", unit_log2_scale: int = 0, streamed: bool = True, chunk_mb: int = 128) -> dict:
-    """Every output of the checkpoint at ``path`` as a bf16 tensor on ``device``.  By default the
-    overlapped pipeline decodes each staging step while later steps are read and copied;
-    ``streamed=False`` stages the whole data section first and then decodes it in one launch."""
-    idx = SafeTensorIndex.open(path, unit_log2_scale)
+def load(path: str, device="cuda", unit_log2_scale: int = 0, streamed: bool = True, chunk_mb: int = 128,
+         out_dtype: str = "bf16") -> dict:
+    """Every output of the checkpoint at ``path`` as a tensor on ``device`` (bf16 by default, or
+    ``out_dtype`` f16 / f32).  By default the overlapped pipeline decodes each staging step while
+    later steps are read and copied; ``streamed=False`` stages the whole data section first and
+    then decodes it in one launch."""
+    idx = SafeTensorIndex.open(path, unit_log2_scale, out_dtype)
     ck = DeviceCheckpoint(idx, None, device)
     if streamed:
         ck.stream(path, chunk_mb=chunk_mb)

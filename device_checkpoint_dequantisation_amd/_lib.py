@@ -9,6 +9,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstmat.so
 
 ST_MAX_NDIM = 8
 KINDS = ("PASS_BF16", "CAST_F16", "CAST_F32", "FP8_TENSOR", "FP8_BLOCK128", "NVFP4")
+OUT_DTYPES = ("bf16", "f16", "f32")   # st_out_dtype codes 0, 1, 2
+MAT_SLICES = 1
 DTYPES = ("BOOL", "U8", "I8", "F8_E4M3", "F8_E5M2", "F8_E8M0", "I16", "U16", "F16", "BF16", "I32", "U32", "F32",
           "I64", "U64", "F64", "F4", "F6_E2M3", "F6_E3M2")
 STATUS = {0: "ST_OK", -1: "ST_E_ARG", -2: "ST_E_IO", -3: "ST_E_HEADER", -4: "ST_E_JSON", -5: "ST_E_DTYPE",
@@ -38,7 +40,8 @@ assert C.sizeof(Desc) == 64
 
 class TableHeader(C.Structure):
     _fields_ = [("magic", C.c_uint32), ("n_desc", C.c_uint32), ("units", C.c_uint64), ("desc_offset", C.c_uint64),
-                ("map_offset", C.c_uint64), ("bytes", C.c_uint64), ("reserved", C.c_uint64 * 3)]
+                ("map_offset", C.c_uint64), ("bytes", C.c_uint64), ("out_dtype", C.c_uint32), ("reserved0", C.c_uint32),
+                ("reserved", C.c_uint64 * 2)]
 
 
 assert C.sizeof(TableHeader) == 64
@@ -112,6 +115,9 @@ SIGNATURES = {
                                 C.POINTER(C.c_double)]),
     "st_materialize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "st_materialize_slices": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "st_materialize_as": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32, C.c_uint32,
+                                    C.c_void_p]),
+    "st_index_out_dtype": (C.c_uint32, [C.c_void_p]),
     "st_stream_plan_build": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p)]),
     "st_stream_plan_select": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_uint64, C.c_uint32,
                                         C.POINTER(C.c_void_p)]),

@@ -580,7 +580,7 @@ namespace {
 
 // A work table from descriptors whose unit ranges are set, `units` in total: header, map,
 // descriptors.
-std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units) {
+std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units, uint32_t out_dtype) {
     const size_t k = descs.size();
     const uint64_t groups = (units + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
     st_table_header h;
@@ -591,6 +591,7 @@ std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t 
     h.map_offset = sizeof(st_table_header);
     h.desc_offset = stk::table_desc_offset(groups);
     h.bytes = h.desc_offset + k * sizeof(st_desc);
+    h.out_dtype = out_dtype;
     std::vector<unsigned char> t(h.bytes, 0);
     memcpy(t.data(), &h, sizeof h);
     if (k) memcpy(t.data() + h.desc_offset, descs.data(), k * sizeof(st_desc));
@@ -617,7 +618,7 @@ std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* 
         if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
     }
     *units_out = pos;
-    return assemble(descs, pos);
+    return assemble(descs, pos, ix.out_dtype);
 }
 
 namespace {
@@ -716,7 +717,7 @@ st_status plan(st_index& ix) {
     ix.out_offset.resize(ix.outputs.size());
     for (size_t k = 0; k < ix.outputs.size(); ++k) {
         ix.out_offset[k] = pos;
-        pos = round_up(pos + ix.outputs[k].numel * 2, 256);
+        pos = round_up(pos + ix.outputs[k].numel * sti::out_bytes(ix), 256);
     }
     ix.arena_bytes = pos;
     std::vector<uint32_t> all(ix.outputs.size());
@@ -751,9 +752,10 @@ extern "C" st_status st_index_build(const void* header_bytes, uint64_t header_le
     if (!out) return st_fail(ST_E_ARG, "st_index_build: out is null");
     *out = nullptr;
     if (!header_bytes && header_len) return st_fail(ST_E_ARG, "st_index_build: header_bytes is null");
-    if (opts && (opts->flags != 0 || opts->unit_log2_scale > 6))
-        return st_fail(ST_E_ARG, "st_plan_opts: flags must be 0 and unit_log2_scale at most 6 (got %u, %u)", opts->flags,
-                       opts->unit_log2_scale);
+    if (opts && ((opts->flags & ~3u) != 0 || (opts->flags & 3u) > ST_OUT_F32 || opts->unit_log2_scale > 6))
+        return st_fail(ST_E_ARG,
+                       "st_plan_opts: flags hold only an output type (0..2) and unit_log2_scale is at most 6 (got 0x%x, %u)",
+                       opts->flags, opts->unit_log2_scale);
     if (header_len < 8 || file_size < 8)
         return st_fail(ST_E_HEADER, "file shorter than the 8-byte header length (%llu bytes)",
                        (unsigned long long)std::min(header_len, file_size));
@@ -773,6 +775,7 @@ extern "C" st_status st_index_build(const void* header_bytes, uint64_t header_le
     ix->header_len = n;
     ix->data_size = file_size - hb;
     ix->unit_log2_scale = opts ? opts->unit_log2_scale : 0;
+    ix->out_dtype = opts ? (opts->flags & 3u) : ST_OUT_BF16;
     try {
         JVal root;
         if (st_status r = JsonReader(text, n).parse(root)) return r;
@@ -878,7 +881,7 @@ extern "C" uint64_t st_index_output_arena_bytes(const st_index* idx) { return id
 extern "C" uint64_t st_index_traffic_bytes(const st_index* idx) {
     if (!idx) return 0;
     uint64_t w = 0;
-    for (const Output& o : idx->outputs) w += o.numel * 2;
+    for (const Output& o : idx->outputs) w += o.numel * sti::out_bytes(*idx);
     return idx->data_size + w;
 }
 
@@ -949,7 +952,7 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
             pos += u;
             if (pos >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "st_index_table_slices: 2^32 or more work units");
         }
-        t = assemble(descs, pos);
+        t = assemble(descs, pos, idx->out_dtype);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
     }
@@ -961,3 +964,5 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
     memcpy(dst, t.data(), t.size());
     return ST_OK;
 }
+
+extern "C" uint32_t st_index_out_dtype(const st_index* idx) { return idx ? idx->out_dtype : ST_OUT_BF16; }

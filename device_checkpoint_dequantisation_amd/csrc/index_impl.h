@@ -54,4 +54,10 @@ struct st_index {
     std::vector<unsigned char> table;  // header, group map, descriptors
     uint64_t total_units = 0;
     uint32_t unit_log2_scale = 0;
+    uint32_t out_dtype = ST_OUT_BF16;  // st_out_dtype of every output
 };
+
+namespace sti {
+// Bytes per output element.
+inline uint64_t out_bytes(const st_index& ix) { return ix.out_dtype == ST_OUT_F32 ? 4 : 2; }
+}  // namespace sti

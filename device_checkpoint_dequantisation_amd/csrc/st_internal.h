@@ -44,13 +44,14 @@ constexpr uint32_t words_per_lane(uint32_t kind) {
          : kind == ST_KIND_NVFP4                                 ? kWordsFp4
                                                                  : kWordsFp8;
 }
-// The kernel's chunk geometry per kind: output elements per chunk, and the load word size that
-// a source must be aligned to for the fast path.  A column slice keeps the fast path when its
+// The kernel's chunk geometry per kind: output elements per chunk (8 for every kind: one 16-byte
+// word of a 2-byte output type), and the load word size that a source must be aligned to for the
+// fast path (a chunk's source bytes, at most 16).  A column slice keeps the fast path when its
 // width is a whole number of chunks and its row length in bytes is a whole number of load words.
-constexpr uint32_t chunk_elems(uint32_t kind) {
-    return kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_FP8_BLOCK128 ? 16 : 8;
+constexpr uint32_t chunk_elems(uint32_t) { return 8; }
+constexpr uint32_t load_word_bytes(uint32_t kind) {
+    return kind == ST_KIND_NVFP4 ? 4 : kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_FP8_BLOCK128 ? 8 : 16;
 }
-constexpr uint32_t load_word_bytes(uint32_t kind) { return kind == ST_KIND_NVFP4 ? 4 : 16; }
 // Source bits per element.
 constexpr uint32_t source_bits(uint32_t kind) {
     return kind == ST_KIND_CAST_F32 ? 32

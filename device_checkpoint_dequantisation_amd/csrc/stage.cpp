@@ -292,8 +292,9 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
                 status = st_fail(ST_E_HIP, "st_stream_file: hipStreamWaitEvent failed");
                 break;
             }
-            status = st_materialize(blob_dev, static_cast<const char*>(tables_dev) + step.table_offset, size_t(step.units),
-                                    outs_dev + step.first_out, compute_stream);
+            status = st_materialize_as(blob_dev, static_cast<const char*>(tables_dev) + step.table_offset,
+                                       size_t(step.units), outs_dev + step.first_out, st_index_out_dtype(idx), 0,
+                                       compute_stream);
             if (status != ST_OK) break;
             ++st.launches;
         }

@@ -39,9 +39,12 @@ class OutputMeta:
     source_dtype: str   # safetensors dtype of the stored weight
     source_bytes: int   # bytes read to materialise it (weight and scale tensors)
 
+    out_dtype: str = "bf16"  # output element type: bf16, f16 or f32
+
     @property
     def dtype(self):
-        return _torch().bfloat16
+        torch = _torch()
+        return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[self.out_dtype]
 
     @property
     def numel(self) -> int:
@@ -209,15 +212,17 @@ class StreamStateDict(Mapping):
     ``ram_cache_bytes`` > 0 the checkpoint bytes of recently loaded outputs stay in pinned host
     memory (LRU) and later loads of them skip the file."""
 
-    def __init__(self, path: str, device="cuda", ram_cache_bytes: int = 0, index: SafeTensorIndex | None = None):
+    def __init__(self, path: str, device="cuda", ram_cache_bytes: int = 0, index: SafeTensorIndex | None = None,
+                 out_dtype: str = "bf16"):
         self.path = path
-        self.index = index if index is not None else SafeTensorIndex.open(path)
+        self.index = index if index is not None else SafeTensorIndex.open(path, out_dtype=out_dtype)
         self.device = _torch().device(device)
         ents = self.index.tensors()
         self._meta = {}
         for k, o in enumerate(self.index.outputs()):
             src = sum(ents[i].end - ents[i].begin for i in (o.tensor, o.scale, o.scale2) if i >= 0)
-            self._meta[o.name] = OutputMeta(o.name, k, tuple(o.shape), o.kind, ents[o.tensor].dtype, src)
+            self._meta[o.name] = OutputMeta(o.name, k, tuple(o.shape), o.kind, ents[o.tensor].dtype, src,
+                                            self.index.out_dtype)
         self._keys = list(self._meta)
         self.ram = RamCache(ram_cache_bytes)
         self.stats = collections.Counter()
@@ -260,7 +265,7 @@ class StreamStateDict(Mapping):
         if not names:
             return {}
         with torch.cuda.stream(s):
-            outs = {m.name: torch.empty(m.shape, dtype=torch.bfloat16, device=self.device) for m in metas}
+            outs = {m.name: torch.empty(m.shape, dtype=m.dtype, device=self.device) for m in metas}
             if self.ram.max_bytes > 0:
                 self._load_cached(metas, outs, s)
             else:
@@ -377,7 +382,8 @@ class StreamStateDict(Mapping):
                 e.last_use = ev
                 for step in e.plan.steps:
                     if step.units:
-                        materialize(blob[off:], e.table_dev[step.table_offset:], step.units, ptrs[j:], s)
+                        materialize(blob[off:], e.table_dev[step.table_offset:], step.units, ptrs[j:], s,
+                                    out_dtype=self.index.out_dtype)
                         self.stats["launches"] += 1
         finally:
             self.ram.protected.clear()
@@ -530,8 +536,8 @@ class LazyModuleLoader:
     parameter: before the submodule runs, all of its meta parameters are decoded in one
     ``state_dict.load`` call.  With ``max_resident_bytes`` the materialised parameters form an LRU
     (by submodule) on the device; going over the bound turns the least recently used submodules'
-    parameters back into meta tensors (their DiskRefs stay).  Parameters become bf16 and do not
-    require grad."""
+    parameters back into meta tensors (their DiskRefs stay).  Parameters take the state dict's
+    output type (bf16 unless the index plans f16 or f32) and do not require grad."""
 
     def __init__(self, module, state_dict, max_resident_bytes: int | None = None, strict: bool = True):
         torch = _torch()

@@ -72,6 +72,12 @@ typedef enum st_kind {
     ST_KIND_FP8_TENSOR = 3, ST_KIND_FP8_BLOCK128 = 4, ST_KIND_NVFP4 = 5
 } st_kind;
 
+/* Output element type, chosen per index (st_plan_opts.flags).  Every output element is the fp32
+ * result of its definition rounded to nearest-even in this type (fp32: the result itself); any NaN
+ * becomes the type's canonical quiet NaN (bf16 0x7FC0, fp16 0x7E00, fp32 0x7FC00000); no
+ * subnormal flushing.  A bf16 source copied to a bf16 output keeps its bits. */
+typedef enum st_out_dtype { ST_OUT_BF16 = 0, ST_OUT_F16 = 1, ST_OUT_F32 = 2 } st_out_dtype;
+
 #define ST_MAX_NDIM 8
 #define ST_HEADER_CAP 100000000ull   /* largest accepted JSON header, bytes */
 #define ST_BLOB_ALIGN 256            /* required alignment of the device blob */
@@ -122,7 +128,9 @@ typedef struct st_table_header {
     uint64_t desc_offset;    /* bytes from the table start to st_desc[0] */
     uint64_t map_offset;     /* bytes from the table start to map[0] (always 64) */
     uint64_t bytes;          /* size of the whole table */
-    uint64_t reserved[3];
+    uint32_t out_dtype;      /* st_out_dtype the outputs were planned for */
+    uint32_t reserved0;
+    uint64_t reserved[2];
 } st_table_header;           /* 64 bytes */
 
 typedef struct st_desc {
@@ -148,7 +156,8 @@ typedef struct st_desc {
 /* Planning options; pass NULL for the defaults. */
 typedef struct st_plan_opts {
     uint32_t unit_log2_scale;  /* work unit = (kind's default unit) << this; 0..6, default 0 */
-    uint32_t flags;            /* reserved, must be 0 */
+    uint32_t flags;            /* bits 0-1: st_out_dtype of every output (default ST_OUT_BF16);
+                                  the other bits must be 0 */
 } st_plan_opts;
 
 typedef struct st_index st_index;   /* opaque, host memory, owned by the library */
@@ -189,12 +198,14 @@ const char* st_index_metadata_json(const st_index* idx);
 
 size_t st_index_num_outputs(const st_index* idx);
 st_status st_index_output(const st_index* idx, size_t k, st_output_info* out);
+/* The output element type the index plans for (st_plan_opts.flags). */
+uint32_t st_index_out_dtype(const st_index* idx);
 /* Byte offset of output k inside one output arena in which every output starts on a
- * 256-byte boundary, and the arena's total size. */
+ * 256-byte boundary, and the arena's total size (2 or 4 bytes per element). */
 uint64_t st_index_output_offset(const st_index* idx, size_t k);
 uint64_t st_index_output_arena_bytes(const st_index* idx);
-/* Bytes read + bytes written by materialising every output (the data section plus 2 bytes
- * per output element). */
+/* Bytes read + bytes written by materialising every output (the data section plus 2 or 4
+ * bytes per output element). */
 uint64_t st_index_traffic_bytes(const st_index* idx);
 /* Device memory the whole load needs: blob + work table + pointer array + arena.
  * Compare with the free device memory before allocating; the requirement is arithmetic. */
@@ -371,6 +382,16 @@ st_status st_materialize(const void* blob, const void* descs, size_t n, void* co
  * whole-output kernel carries no strided code. */
 st_status st_materialize_slices(const void* blob, const void* descs, size_t n, void* const* outs,
                                 void* stream);
+
+#define ST_MAT_SLICES 1u     /* st_materialize_as: the instance with the strided column-slice path */
+
+/* The general entry point: st_materialize for a table planned with output type out_dtype
+ * (st_out_dtype; outs then point to arrays of that type, aligned to it), flags 0 or
+ * ST_MAT_SLICES.  One kernel instance per output type: a table planned for another type than
+ * out_dtype makes every wavefront return without writing.  ST_E_ARG for an unknown type or
+ * flag.  st_materialize = (ST_OUT_BF16, 0); st_materialize_slices = (ST_OUT_BF16, ST_MAT_SLICES). */
+st_status st_materialize_as(const void* blob, const void* descs, size_t n, void* const* outs,
+                            uint32_t out_dtype, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

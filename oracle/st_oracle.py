@@ -14,10 +14,12 @@ infinities, NaN at S.1111.111), OCP-MX E2M1, and IEEE-754 binary32 arithmetic wi
 round-to-nearest-even followed by round-to-nearest-even to bfloat16.
 
 Readings where the pages are silent (each listed in the design notes):
-  * one fp32 multiply per scale, each rounded RNE, then RNE to bf16 (double rounding);
+  * one fp32 multiply per scale, each rounded RNE, then RNE to bf16 (double rounding); the fp16
+    and fp32 output variants round the same fp32 result RNE to fp16, or keep it;
   * NVFP4 multiplies left to right: (e2m1 * block_scale) * global_scale;
   * ``weight_scale_inv`` is multiplied, despite its name;
-  * every NaN result becomes bf16 0x7FC0; bf16 passthrough copies bits unchanged;
+  * every NaN result becomes the output type's canonical quiet NaN (bf16 0x7FC0, fp16 0x7E00,
+    fp32 0x7FC00000); bf16 passthrough to a bf16 output copies bits unchanged;
   * no flush of subnormals anywhere;
   * packed e2m1: element 2k in bits 0-3, element 2k+1 in bits 4-7 of byte k;
   * tensor names: ``X.weight`` + ``X.scale_weight`` (fp32 scalar) = per-tensor scaled FP8;
@@ -302,6 +304,24 @@ def bf16_rne(y: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(y), np.uint64(0x7FC0), r).astype(np.uint16)
 
 
+def f16_rne(y: np.ndarray) -> np.ndarray:
+    """binary32 -> binary16 bits, round to nearest, ties to even (NumPy's IEEE conversion: overflow
+    to infinity, subnormals kept); any NaN -> 0x7E00."""
+    y = np.asarray(y, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = y.astype(np.float16).view(np.uint16)
+    return np.where(np.isnan(y), np.uint16(0x7E00), h).astype(np.uint16)
+
+
+def f32_bits(y: np.ndarray) -> np.ndarray:
+    """binary32 bits of y; any NaN -> 0x7FC00000."""
+    y = np.asarray(y, dtype=np.float32)
+    return np.where(np.isnan(y), np.uint32(0x7FC00000), y.view(np.uint32)).astype(np.uint32)
+
+
+OUT_ROUND = {"bf16": bf16_rne, "f16": f16_rne, "f32": f32_bits}
+
+
 # ----------------------------------------------------------------------------- decoding
 
 def _gather_le(data: np.ndarray, base: int, itemsize: int, idx: np.ndarray) -> np.ndarray:
@@ -317,34 +337,26 @@ def _f32_at(data, base, idx):
     return _gather_le(data, base, 4, idx).astype(np.uint32).view(np.float32)
 
 
-def decode(o: Output, data, idx=None) -> np.ndarray:
-    """bf16 bits of output ``o`` at flat element indices ``idx`` (all elements if None).
-    ``data`` is the data section (bytes after the header) as a uint8 array."""
-    data = np.asarray(data, dtype=np.uint8)
-    flat = idx is None
-    if flat:
-        idx = np.arange(o.numel, dtype=np.int64)
-    idx = np.asarray(idx, dtype=np.int64)
+def value(o: Output, data, idx) -> np.ndarray:
+    """The exact binary32 result of output ``o`` at flat element indices ``idx``, before the
+    output rounding: each scale applied by one RNE fp32 multiply, in the pages' order."""
     b = o.src.begin
     if o.kind == "PASS_BF16":
-        out = _gather_le(data, b, 2, idx).astype(np.uint16)
-    elif o.kind == "CAST_F16":
-        y = _gather_le(data, b, 2, idx).astype(np.uint16).view(np.float16).astype(np.float32)
-        out = bf16_rne(y)
-    elif o.kind == "CAST_F32":
-        out = bf16_rne(_f32_at(data, b, idx))
-    elif o.kind == "FP8_TENSOR":
+        return (_gather_le(data, b, 2, idx).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if o.kind == "CAST_F16":
+        return _gather_le(data, b, 2, idx).astype(np.uint16).view(np.float16).astype(np.float32)
+    if o.kind == "CAST_F32":
+        return _f32_at(data, b, idx)
+    if o.kind == "FP8_TENSOR":
         s = _f32_at(data, o.scale.begin, np.zeros(1, np.int64))[0]
-        w = E4M3[_gather_le(data, b, 1, idx).astype(np.int64)]
-        out = bf16_rne(w * s)
-    elif o.kind == "FP8_BLOCK128":
+        return E4M3[_gather_le(data, b, 1, idx).astype(np.int64)] * s
+    if o.kind == "FP8_BLOCK128":
         m, n = o.shape
         gn = -(-n // 128)
         i, j = idx // n, idx % n
         S = _f32_at(data, o.scale.begin, (i // 128) * gn + j // 128)
-        w = E4M3[_gather_le(data, b, 1, idx).astype(np.int64)]
-        out = bf16_rne(w * S)
-    elif o.kind == "NVFP4":
+        return E4M3[_gather_le(data, b, 1, idx).astype(np.int64)] * S
+    if o.kind == "NVFP4":
         m, k = o.shape
         i, j = idx // k, idx % k
         byte = _gather_le(data, b, 1, idx // 2)
@@ -352,15 +364,30 @@ def decode(o: Output, data, idx=None) -> np.ndarray:
         bs = E4M3[_gather_le(data, o.scale.begin, 1, i * (k // 16) + j // 16).astype(np.int64)]
         g = _f32_at(data, o.scale2.begin, np.zeros(1, np.int64))[0]
         t = E2M1[nib.astype(np.int64)] * bs
-        out = bf16_rne(t * g)
+        return t * g
+    raise OracleError(f"unknown kind {o.kind}")
+
+
+def decode(o: Output, data, idx=None, out_dtype: str = "bf16") -> np.ndarray:
+    """Output bits of ``o`` at flat element indices ``idx`` (all elements if None): uint16 for bf16
+    and f16 outputs, uint32 for f32.  ``data`` is the data section (bytes after the header) as a
+    uint8 array."""
+    data = np.asarray(data, dtype=np.uint8)
+    flat = idx is None
+    if flat:
+        idx = np.arange(o.numel, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    if o.kind == "PASS_BF16" and out_dtype == "bf16":
+        out = _gather_le(data, o.src.begin, 2, idx).astype(np.uint16)
     else:
-        raise OracleError(f"unknown kind {o.kind}")
+        with np.errstate(invalid="ignore", over="ignore"):
+            out = OUT_ROUND[out_dtype](value(o, data, idx))
     return out.reshape(o.shape) if flat else out
 
 
-def materialize(buf) -> dict:
-    """{name: uint16 array of the logical shape} for every output of a whole file's bytes."""
+def materialize(buf, out_dtype: str = "bf16") -> dict:
+    """{name: output bits of the logical shape} for every output of a whole file's bytes."""
     h, outs = plan(buf)
     data = np.frombuffer(memoryview(buf), dtype=np.uint8, offset=h.data_offset)
     with np.errstate(invalid="ignore", over="ignore"):
-        return {o.name: decode(o, data) for o in outs}
+        return {o.name: decode(o, data, out_dtype=out_dtype) for o in outs}

@@ -62,20 +62,19 @@ SPECIAL_SCALES = [0x3F6471C8, 0x3C23D70A, 0x00000001, 0x00400000, 0x7F7FFFFF, 0x
                   0x7FC00000, 0x80000000, 0x00000000, 0xBF800000, 0x3B2D27D2]
 
 
-@pytest.mark.parametrize("shift", [0, 1, 2, 3, 5, 9, 12, 15])
-def test_fp8_tensor_every_code_every_alignment(shift):
-    codes = np.tile(np.arange(256, dtype=np.uint8), 40)   # 10240 elements: full units + a ragged tail
+def fp8_every_code_file(shift):
+    """Every e4m3 code (10240 elements: full units and a ragged tail) under special fp32 scales."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), 40)
     tensors = list(_pad(shift))
     for i, s in enumerate(SPECIAL_SCALES):
         tensors += [(f"q{i}.weight", "F8_E4M3", (len(codes),), np.roll(codes, i)),
                     (f"q{i}.scale_weight", "F32", (), np.array([s], np.uint32).tobytes())]
-    assert_parity(make_file(tensors))
+    return make_file(tensors)
 
 
-@pytest.mark.parametrize("shift", [0, 1, 3, 6])
-def test_nvfp4_every_nibble_every_block_scale(shift):
-    # rows of K = 48 (K % 32 == 16): every e2m1 code against every e4m3 block-scale code,
-    # including NaN codes and subnormals, under several global scales.
+def nvfp4_every_code_file(shift):
+    """Rows of K = 48 (K % 32 == 16): every e2m1 code against every e4m3 block-scale code,
+    including NaN codes and subnormals, under several global scales."""
     sc = np.arange(256, dtype=np.uint8)
     M, K = 256 * 2, 48
     nib = np.tile(np.arange(16, dtype=np.uint8), M * K // 16)
@@ -85,12 +84,11 @@ def test_nvfp4_every_nibble_every_block_scale(shift):
     for i, g in enumerate([0x3B2D27D2, 0x3F800000, 0x00000001, 0x7F7FFFFF, 0x7F800000, 0x7FC00000, 0x00000000]):
         tensors += [(f"n{i}.weight", "U8", (M, K // 2), packed), (f"n{i}.weight_scale", "F8_E4M3", (M, K // 16), np.roll(bs, i)),
                     (f"n{i}.weight_scale_2", "F32", (), np.array([g], np.uint32).tobytes())]
-    assert_parity(make_file(tensors))
+    return make_file(tensors)
 
 
-@pytest.mark.parametrize("M,N", [(300, 200), (5, 1), (130, 7), (257, 129), (128, 4096), (1, 16), (129, 48)])
-@pytest.mark.parametrize("shift", [0, 2, 7])
-def test_block_fp8_ragged_shapes(M, N, shift):
+def block_fp8_file(M, N, shift):
+    """Random codes in [M, N] with 128x128 scales, one huge, one NaN and one infinite."""
     rng = np.random.default_rng(M * 1000 + N)
     w = rng.integers(0, 256, size=M * N, dtype=np.uint64).astype(np.uint8)
     gm, gn = -(-M // 128), -(-N // 128)
@@ -100,11 +98,11 @@ def test_block_fp8_ragged_shapes(M, N, shift):
         S[1] = np.float32("nan")
         S[2] = np.float32("inf")
     tensors = list(_pad(shift)) + [("b.weight", "F8_E4M3", (M, N), w), ("b.weight_scale_inv", "F32", (gm, gn), S)]
-    assert_parity(make_file(tensors))
+    return make_file(tensors)
 
 
-@pytest.mark.parametrize("shift", [0, 1, 2, 3, 7])
-def test_f16_every_code_and_f32_specials(shift):
+def float_every_code_file(shift):
+    """Every fp16 code, random fp32 words with their specials, random bf16 words."""
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     rng = np.random.default_rng(5)
     f = rng.integers(0, 2 ** 32, size=50_001, dtype=np.uint64).astype(np.uint32)
@@ -112,7 +110,28 @@ def test_f16_every_code_and_f32_specials(shift):
               0x3F808000, 0x3F818000, 0x00008000, 0x00018000]
     bf = rng.integers(0, 2 ** 16, size=9_999, dtype=np.uint64).astype(np.uint16)
     tensors = list(_pad(shift)) + [("h", "F16", (256, 256), h), ("f", "F32", (50_001,), f), ("p", "BF16", (9_999,), bf)]
-    assert_parity(make_file(tensors))
+    return make_file(tensors)
+
+
+@pytest.mark.parametrize("shift", [0, 1, 2, 3, 5, 9, 12, 15])
+def test_fp8_tensor_every_code_every_alignment(shift):
+    assert_parity(fp8_every_code_file(shift))
+
+
+@pytest.mark.parametrize("shift", [0, 1, 3, 6])
+def test_nvfp4_every_nibble_every_block_scale(shift):
+    assert_parity(nvfp4_every_code_file(shift))
+
+
+@pytest.mark.parametrize("M,N", [(300, 200), (5, 1), (130, 7), (257, 129), (128, 4096), (1, 16), (129, 48)])
+@pytest.mark.parametrize("shift", [0, 2, 7])
+def test_block_fp8_ragged_shapes(M, N, shift):
+    assert_parity(block_fp8_file(M, N, shift))
+
+
+@pytest.mark.parametrize("shift", [0, 1, 2, 3, 7])
+def test_f16_every_code_and_f32_specials(shift):
+    assert_parity(float_every_code_file(shift))
 
 
 def test_many_small_full_stress_config():

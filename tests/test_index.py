@@ -66,7 +66,8 @@ DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("pitch", 
                  ("unit_end", "<u4"), ("tail", "<u4"), ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"),
                  ("div_magic", "<u4"), ("kind", "u1"), ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1")])
 HEADER = np.dtype([("magic", "<u4"), ("n_desc", "<u4"), ("units", "<u8"), ("desc_offset", "<u8"),
-                   ("map_offset", "<u8"), ("bytes", "<u8"), ("reserved", "<u8", 3)])
+                   ("map_offset", "<u8"), ("bytes", "<u8"), ("out_dtype", "<u4"), ("reserved0", "<u4"),
+                   ("reserved", "<u8", 2)])
 
 
 def _table(raw: bytes):
@@ -257,3 +258,39 @@ def test_random_header_mutations_accept_and_reject_alike():
             assert [e.name for e in ix.tensors()] == list(h.entries)
             assert [o.name for o in ix.outputs()] == [o.name for o in outs]
     assert agree == 600
+
+
+@pytest.mark.parametrize("dt,esize,code", [("bf16", 2, 0), ("f16", 2, 1), ("f32", 4, 2)])
+def test_output_types_size_the_arena_and_mark_the_tables(dt, esize, code):
+    buf = synth.config_bytes(5, small=True)
+    ix = st.SafeTensorIndex.from_bytes(buf, out_dtype=dt)
+    outs = ix.outputs()
+    assert ix.out_dtype == dt
+    offs = [o.offset for o in outs]
+    assert all(x % 256 == 0 for x in offs)
+    assert all(offs[i] + esize * outs[i].numel <= offs[i + 1] for i in range(len(offs) - 1))
+    assert ix.traffic_bytes == ix.data_size + esize * sum(o.numel for o in outs)
+    for raw in (ix.table()[0], ix.table_subset([1, 2])[0], ix.table_slices([(3, None, None)])[0]):
+        assert _table(raw)[0]["out_dtype"] == code
+    plan = st.StreamPlan(ix, 64 << 10)
+    for step in plan.steps:
+        if step.outputs:
+            assert np.frombuffer(plan.tables, HEADER, count=1, offset=step.table_offset)[0]["out_dtype"] == code
+
+
+def test_bad_plan_options_are_refused():
+    buf = synth.config_bytes(1)
+    with pytest.raises(st.StError, match="ST_E_ARG"):
+        _build(buf, 3, 0)
+    with pytest.raises(st.StError, match="ST_E_ARG"):
+        _build(buf, 4, 0)
+    with pytest.raises(st.StError, match="ST_E_ARG"):
+        _build(buf, 0, 7)
+
+
+def _build(buf, flags, scale):
+    import ctypes as C
+    h = C.c_void_p()
+    opts = _lib.PlanOpts(scale, flags)
+    raw = C.create_string_buffer(bytes(buf), len(buf))
+    st.check(_lib.lib().st_index_build(raw, len(buf), len(buf), C.byref(opts), C.byref(h)), "st_index_build")
