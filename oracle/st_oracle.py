@@ -26,6 +26,9 @@ Readings where the pages are silent (each listed in the design notes):
     ``X.weight`` + ``X.weight_scale_inv`` (fp32 [ceil(M/128), ceil(N/128)]) = block FP8;
     ``X.weight`` (U8 [M, K/2] or F4 [M, K]) + ``X.weight_scale`` (e4m3 [M, K/16]) +
     ``X.weight_scale_2`` (fp32 scalar) = NVFP4;
+    ``X.weight`` (F8_E4M3 [M, K]; or U8 [M, K/2] / F4 [M, K]) + ``X.weight_scale`` (F8_E8M0
+    [M, K/32]) = MXFP8 / MXFP4, the OCP Microscaling formats: blocks of 32 consecutive elements
+    of a row share one E8M0 scale 2^(e - 127) (e = 255 is NaN), applied by one fp32 multiply;
   * any byte offset is legal for any dtype; header length capped at 100,000,000 bytes;
   * header integers must fit in a signed 64-bit value; at most 8 dimensions.
 
@@ -220,9 +223,13 @@ def classify(h: Header) -> list:
                 raise OracleError(f"{name}: float8 tensor without a scale (not named X.weight)")
             x = name[: -len(".weight")]
             st, sb = ents.get(x + ".scale_weight"), ents.get(x + ".weight_scale_inv")
-            if st is not None and sb is not None:
-                raise OracleError(f"{name}: both scale_weight and weight_scale_inv present")
-            if st is not None:
+            sm = ents.get(x + ".weight_scale")
+            if sum(v is not None for v in (st, sb, sm)) > 1:
+                raise OracleError(f"{name}: more than one of scale_weight, weight_scale_inv, weight_scale present")
+            if sm is not None:
+                outs.append(_mx_output(name, e, sm, ents.get(x + ".weight_scale_2"), "MXFP8", e.shape))
+                used.add(sm.name)
+            elif st is not None:
                 if st.dtype != "F32" or not _is_scalar(st):
                     raise OracleError(f"{st.name}: scale_weight must be an fp32 scalar")
                 outs.append(Output(name, "FP8_TENSOR", e.shape, e, st))
@@ -237,7 +244,7 @@ def classify(h: Header) -> list:
                 outs.append(Output(name, "FP8_BLOCK128", e.shape, e, sb))
                 used.add(sb.name)
             else:
-                raise OracleError(f"{name}: float8 weight has no scale_weight or weight_scale_inv")
+                raise OracleError(f"{name}: float8 weight has no scale_weight, weight_scale_inv or weight_scale")
         elif e.dtype in ("U8", "F4"):
             if not name.endswith(".weight"):
                 raise OracleError(f"{name}: {e.dtype} tensor is not an NVFP4 weight")
@@ -246,9 +253,13 @@ def classify(h: Header) -> list:
                 raise OracleError(f"{name}: NVFP4 weight must be 2-D")
             m = e.shape[0]
             k = e.shape[1] * 2 if e.dtype == "U8" else e.shape[1]
+            bs, g = ents.get(x + ".weight_scale"), ents.get(x + ".weight_scale_2")
+            if bs is not None and bs.dtype == "F8_E8M0":
+                outs.append(_mx_output(name, e, bs, g, "MXFP4", (m, k)))
+                used.add(bs.name)
+                continue
             if k % 16:
                 raise OracleError(f"{name}: NVFP4 K={k} is not a multiple of 16")
-            bs, g = ents.get(x + ".weight_scale"), ents.get(x + ".weight_scale_2")
             if bs is None or g is None:
                 raise OracleError(f"{name}: NVFP4 weight needs weight_scale and weight_scale_2")
             if bs.dtype != "F8_E4M3" or bs.shape != (m, k // 16):
@@ -264,6 +275,20 @@ def classify(h: Header) -> list:
             raise OracleError(f"{name}: scale tensor with no matching weight")
     outs.sort(key=lambda o: (o.src.begin, o.name))
     return outs
+
+
+def _mx_output(name: str, e: Entry, sc: Entry, g, kind: str, shape: tuple) -> Output:
+    """An MX weight of logical shape [M, K] with its E8M0 scale [M, K/32]."""
+    if len(shape) != 2:
+        raise OracleError(f"{name}: {kind} weight must be 2-D")
+    m, k = shape
+    if k % 32:
+        raise OracleError(f"{name}: {kind} K={k} is not a multiple of 32")
+    if g is not None:
+        raise OracleError(f"{g.name}: an E8M0-scaled weight takes no weight_scale_2")
+    if sc.dtype != "F8_E8M0" or sc.shape != (m, k // 32):
+        raise OracleError(f"{sc.name}: must be F8_E8M0 [{m}, {k // 32}], got {sc.dtype}{list(sc.shape)}")
+    return Output(name, kind, (m, k), e, sc)
 
 
 def plan(buf):
@@ -284,6 +309,12 @@ def e4m3_value(c: int) -> float:
     return -v if s else v
 
 
+def e8m0_value(c: int) -> float:
+    """OCP-MX E8M0 scale code -> exact value: 8 exponent bits, bias 127, no sign or mantissa;
+    0xFF is NaN.  Code 0 is 2^-127, a binary32 subnormal."""
+    return math.nan if c == 255 else 2.0 ** (c - 127)
+
+
 def e2m1_value(c: int) -> float:
     """OCP-MX E2M1 code -> exact value: sign bit, 2 exponent bits (bias 1), 1 mantissa bit;
     exponent field 0 is subnormal (0 or 0.5); no NaN or infinities."""
@@ -294,6 +325,7 @@ def e2m1_value(c: int) -> float:
 
 E4M3 = np.array([e4m3_value(c) for c in range(256)], dtype=np.float32)
 E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float32)
+E8M0 = np.array([e8m0_value(c) for c in range(256)], dtype=np.float32)
 
 
 def bf16_rne(y: np.ndarray) -> np.ndarray:
@@ -356,6 +388,15 @@ def value(o: Output, data, idx) -> np.ndarray:
         i, j = idx // n, idx % n
         S = _f32_at(data, o.scale.begin, (i // 128) * gn + j // 128)
         return E4M3[_gather_le(data, b, 1, idx).astype(np.int64)] * S
+    if o.kind in ("MXFP8", "MXFP4"):
+        m, k = o.shape
+        i, j = idx // k, idx % k
+        S = E8M0[_gather_le(data, o.scale.begin, 1, i * (k // 32) + j // 32).astype(np.int64)]
+        if o.kind == "MXFP8":
+            return E4M3[_gather_le(data, b, 1, idx).astype(np.int64)] * S
+        byte = _gather_le(data, b, 1, idx // 2)
+        nib = (byte >> (np.uint64(4) * (idx & 1).astype(np.uint64))) & np.uint64(15)
+        return E2M1[nib.astype(np.int64)] * S
     if o.kind == "NVFP4":
         m, k = o.shape
         i, j = idx // k, idx % k

@@ -11,8 +11,12 @@ needed, only their shapes, dtypes, value distributions and byte layout.
 * ``nvfp4``      packed e2m1 weights (U8 [M, K/2]) with e4m3fn ``weight_scale`` per 16
                  elements along K and an fp32 ``weight_scale_2`` per tensor.
 * ``many_small`` 20,000 tensors of 64 B - 64 KB, mixed dtypes, packed unaligned.
+* ``mxfp8``      the block-FP8 layer shapes as OCP MXFP8: e4m3fn weights with one E8M0
+                 ``weight_scale`` per 32 elements along K.
+* ``mxfp4``      the NVFP4 layer shapes as OCP MXFP4: packed e2m1 (U8 [M, K/2]) with one E8M0
+                 ``weight_scale`` per 32 elements along K.
 
-Seeds: the checkpoint's seed defaults to its config number (1..5); every group of tensors
+Seeds: the checkpoint's seed defaults to its config number (1..7); every group of tensors
 draws from ``default_rng([seed, group_index])`` so generation can run in parallel and stays
 reproducible.  Weights are N(0, 0.02) before quantisation; quantised weights are
 ``e4m3(clip(w / scale, -448, 448))`` with torch's round-to-nearest-even float8_e4m3fn cast.
@@ -148,6 +152,42 @@ def g_nvfp4(prefix, shape, seed, storage="U8"):
                   TensorSpec(prefix + ".weight_scale_2", "F32", ())], make, seed, cost=M * K // 2)
 
 
+def g_mxfp8(prefix, shape, seed):
+    """OCP MXFP8 weight [M, K]: N(0, 0.02) values quantised per block of 32 along K with the
+    spec's shared exponent floor(log2(amax)) - 8 (8 = E4M3's largest exponent), stored as E8M0
+    code exponent + 127, and elements e4m3(clip(v / 2^exponent, -448, 448))."""
+    M, K = shape
+    assert K % 32 == 0
+
+    def make(rng):
+        w = _normal(rng, M * K).reshape(M, K // 32, 32)
+        amax = np.abs(w).max(axis=2)
+        ex = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, np.float32(1e-30)))) - 8, -127)
+        code = np.clip(ex + 127, 0, 254).astype(np.uint8)
+        q = w / np.exp2(code.astype(np.float64) - 127)[:, :, None].astype(np.float32)
+        np.clip(q, -E4M3_MAX, E4M3_MAX, out=q)
+        return [_e4m3(q.reshape(-1)), code.reshape(-1)]
+
+    return Group([TensorSpec(prefix + ".weight", "F8_E4M3", (M, K)),
+                  TensorSpec(prefix + ".weight_scale", "F8_E8M0", (M, K // 32))], make, seed, cost=M * K)
+
+
+def g_mxfp4(prefix, shape, seed, storage="U8"):
+    """OCP MXFP4 weight of logical shape [M, K]: packed bytes uniform over all 256 values, and
+    ``weight_scale`` E8M0 [M, K/32] with exponents uniform in [-12, 2] (codes 115..129)."""
+    M, K = shape
+    assert K % 32 == 0
+    wshape = (M, K // 2) if storage == "U8" else (M, K)
+
+    def make(rng):
+        packed = np.frombuffer(rng.bytes(M * K // 2), dtype=np.uint8)
+        code = rng.integers(115, 130, size=M * K // 32, dtype=np.int64).astype(np.uint8)
+        return [packed, code]
+
+    return Group([TensorSpec(prefix + ".weight", storage, wshape),
+                  TensorSpec(prefix + ".weight_scale", "F8_E8M0", (M, K // 32))], make, seed, cost=M * K // 2)
+
+
 # ----------------------------------------------------------------------------- the families
 
 def tiny(seed=1):
@@ -239,6 +279,42 @@ def nvfp4(seed=4, layers=40, big=25600, small=5120, storage="U8"):
     return gs, {"synthetic": "nvfp4", "seed": seed}, True
 
 
+def mxfp8(seed=6, layers=28, hidden=4096, inter=12288):
+    gs = []
+    k = 0
+
+    def sd():
+        nonlocal k
+        k += 1
+        return (seed, k)
+
+    for l in range(layers):
+        p = f"model.layers.{l}."
+        gs.append(g_plain(p + "input_layernorm.weight", "BF16", (hidden,), sd()))
+        for n in ("q_proj", "k_proj", "v_proj", "o_proj"):
+            gs.append(g_mxfp8(p + "self_attn." + n, (hidden, hidden), sd()))
+        gs.append(g_mxfp8(p + "mlp.gate_proj", (inter, hidden), sd()))
+        gs.append(g_mxfp8(p + "mlp.up_proj", (inter, hidden), sd()))
+        gs.append(g_mxfp8(p + "mlp.down_proj", (hidden, inter), sd()))
+    return gs, {"synthetic": "mxfp8", "seed": seed}, True
+
+
+def mxfp4(seed=7, layers=40, big=25600, small=5120, storage="U8"):
+    gs = []
+    k = 0
+
+    def sd():
+        nonlocal k
+        k += 1
+        return (seed, k)
+
+    for l in range(layers):
+        p = f"model.layers.{l}.mlp."
+        gs.append(g_mxfp4(p + "up_proj", (big, small), sd(), storage))
+        gs.append(g_mxfp4(p + "down_proj", (small, big), sd(), storage))
+    return gs, {"synthetic": "mxfp4", "seed": seed}, True
+
+
 def _divisors(n):
     out = []
     i = 1
@@ -279,6 +355,8 @@ CONFIGS = {
     3: ("block_fp8", block_fp8),
     4: ("nvfp4", nvfp4),
     5: ("many_small", many_small),
+    6: ("mxfp8", mxfp8),
+    7: ("mxfp4", mxfp4),
 }
 
 # Scaled-down variants that keep every structural feature (ragged 128-blocks, K % 32 == 16,
@@ -289,11 +367,13 @@ SMALL = {
     3: {"layers": 2, "hidden": 320, "inter": 960, "vocab": 1000},
     4: {"layers": 2, "big": 400, "small": 208},
     5: {"count": 2000},
+    6: {"layers": 2, "hidden": 320, "inter": 960},
+    7: {"layers": 2, "big": 416, "small": 224},
 }
 
 
 def make_config(k, seed=None, small=False, **overrides):
-    """Groups, metadata and header padding flag of config ``k`` (1..5)."""
+    """Groups, metadata and header padding flag of config ``k`` (1..7)."""
     name, fn = CONFIGS[k]
     kw = dict(SMALL[k]) if small else {}
     kw.update(overrides)

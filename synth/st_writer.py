@@ -24,7 +24,7 @@ import numpy as np
 
 # Bits per element of the safetensors dtype strings the writer accepts.
 DTYPE_BITS = {
-    "BOOL": 8, "U8": 8, "I8": 8, "F8_E4M3": 8, "F8_E5M2": 8,
+    "BOOL": 8, "U8": 8, "I8": 8, "F8_E4M3": 8, "F8_E5M2": 8, "F8_E8M0": 8,
     "I16": 16, "U16": 16, "F16": 16, "BF16": 16,
     "I32": 32, "U32": 32, "F32": 32,
     "I64": 64, "U64": 64, "F64": 64,
