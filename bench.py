@@ -6,8 +6,8 @@ blob is already resident in HBM (staging is measured separately).  Prints ONE JS
     python bench.py [--steps K] [--warmup W] [--config 2] [--all] [--no-cpu]
 
 Default workload: the scaled-FP8 DiT-style checkpoint (57 blocks of e4m3fn weights with per-tensor
-fp32 scales plus bf16 vectors).  ``--all`` adds the other four checkpoint families to the line
-under "formats".
+fp32 scales plus bf16 vectors).  ``--all`` adds the other checkpoint families (including the MXFP8
+and MXFP4 ones) to the line under "formats".
 """
 from __future__ import annotations
 
@@ -32,6 +32,10 @@ WORKLOADS = {
     4: "NVFP4 checkpoint: 40 layers of [25600,5120] and [5120,25600] packed e2m1 with e4m3fn scale per 16 "
        "elements and fp32 global scale",
     5: "many-small-tensor stress blob: 20,000 tensors of 64 B - 64 KB, bf16/fp16/fp32/scaled-e4m3fn, unaligned",
+    6: "MXFP8 LLM checkpoint: 28 layers, hidden 4096, e4m3fn q/k/v/o [4096,4096], gate/up [12288,4096], "
+       "down [4096,12288] with an E8M0 scale per 32 elements along K, bf16 norms",
+    7: "MXFP4 checkpoint: 40 layers of [25600,5120] and [5120,25600] packed e2m1 with an E8M0 scale per 32 "
+       "elements along K",
 }
 
 
@@ -71,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also measure the other checkpoint families")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
@@ -305,7 +309,8 @@ def tp_shards(ix, ck, steps, n=8):
                 slices.append((k, None, None))
                 continue
             dim = o.shape[axis]
-            q = 128 if o.kind == "FP8_BLOCK128" else 16 if (o.kind == "NVFP4" and axis == 1) else 1
+            q = (128 if o.kind == "FP8_BLOCK128" else 16 if (o.kind == "NVFP4" and axis == 1)
+                 else 32 if (o.kind in ("MXFP8", "MXFP4") and axis == 1) else 1)
             step = max(q, -(-dim // n // q) * q)
             for b in range(0, dim, step):
                 part = (b, min(dim, b + step))
@@ -388,7 +393,7 @@ def main():
         sys.exit(2)
     rng = np.random.default_rng(0)
     d = args.tmpdir or tempfile.mkdtemp(prefix="stmat_bench_")
-    configs = [args.config] + ([k for k in (1, 2, 3, 4, 5) if k != args.config] if args.all else [])
+    configs = [args.config] + ([k for k in sorted(WORKLOADS) if k != args.config] if args.all else [])
     results = {}
     cpu = None
     for k in configs:

@@ -22,7 +22,7 @@ from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, Desc, Outpu
                    StError, StreamStats, StreamStep, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
-           "stage_file", "stream_file", "read_plans", "StError", "KINDS"]
+           "stage_file", "stream_file", "read_plans", "StError", "KINDS", "QUANTIZED_KINDS"]
 
 
 @dataclass(frozen=True)
@@ -342,7 +342,9 @@ class QuantizedWeight:
       FP8_TENSOR    data float8_e4m3fn [M, N...], scale fp32 []
       FP8_BLOCK128  data float8_e4m3fn [M, N],    scale fp32 [ceil(M/128), ceil(N/128)] (multiplied)
       NVFP4         data uint8 [M, K/2] (element 2k in the low nibble of byte k),
-                    scale float8_e4m3fn [M, K/16], scale2 fp32 []"""
+                    scale float8_e4m3fn [M, K/16], scale2 fp32 []
+      MXFP8         data float8_e4m3fn [M, K],    scale float8_e8m0fnu [M, K/32]
+      MXFP4         data uint8 [M, K/2] (as NVFP4), scale float8_e8m0fnu [M, K/32]"""
     name: str
     kind: str
     shape: tuple        # logical shape of the weight
@@ -351,11 +353,14 @@ class QuantizedWeight:
     scale2: object = None
 
 
+QUANTIZED_KINDS = ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4", "MXFP8", "MXFP4")
+
+
 def _quantized(index: SafeTensorIndex, blob, k: int, at, copy: bool) -> QuantizedWeight:
     """QuantizedWeight of output k from a device blob in which tensor t's bytes start at at(t)."""
     torch = _torch()
     o = index.output(k)
-    if o.kind not in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4"):
+    if o.kind not in QUANTIZED_KINDS:
         raise ValueError(f"{o.name}: {o.kind} is not a quantised weight")
     ents = index.tensors()
 
@@ -367,6 +372,13 @@ def _quantized(index: SafeTensorIndex, blob, k: int, at, copy: bool) -> Quantize
         return raw(i).clone().view(torch.float32).view(shape)
 
     w = raw(o.tensor)
+    if o.kind in ("MXFP8", "MXFP4"):
+        m, kk = o.shape
+        data = w.view(m, kk // 2) if o.kind == "MXFP4" else w.view(torch.float8_e4m3fn).view(m, kk)
+        sc = raw(o.scale).view(torch.float8_e8m0fnu).view(m, kk // 32)
+        if copy:
+            data, sc = data.clone(), sc.clone()
+        return QuantizedWeight(o.name, o.kind, tuple(o.shape), data, sc)
     if o.kind == "NVFP4":
         m, kk = o.shape
         data = w.view(m, kk // 2)
@@ -467,12 +479,12 @@ class DeviceCheckpoint:
             self.blob[: len(data_section)].copy_(host)
 
     def quantized(self, names=None, copy: bool = True) -> dict:
-        """The quantised weights (FP8_TENSOR, FP8_BLOCK128, NVFP4 outputs) as stored, from the
+        """The quantised weights (FP8_TENSOR, FP8_BLOCK128, NVFP4, MXFP8, MXFP4 outputs) as stored, from the
         staged blob: ``copy=True`` gives fresh, 256-byte aligned tensors; ``copy=False`` gives
         views into the blob for the weight bytes (the fp32 scales are always copied)."""
         outs = self.index.outputs()
         pos = {o.name: k for k, o in enumerate(outs)}
-        want = [o.name for o in outs if o.kind in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4")] if names is None else names
+        want = [o.name for o in outs if o.kind in QUANTIZED_KINDS] if names is None else names
         ents = self.index.tensors()
         return {n: _quantized(self.index, self.blob, pos[n], lambda i: ents[i].begin, copy) for n in want}
 

@@ -8,7 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstmat.so")
 
 ST_MAX_NDIM = 8
-KINDS = ("PASS_BF16", "CAST_F16", "CAST_F32", "FP8_TENSOR", "FP8_BLOCK128", "NVFP4")
+KINDS = ("PASS_BF16", "CAST_F16", "CAST_F32", "FP8_TENSOR", "FP8_BLOCK128", "NVFP4", "MXFP8", "MXFP4")
 OUT_DTYPES = ("bf16", "f16", "f32")   # st_out_dtype codes 0, 1, 2
 MAT_SLICES = 1
 DTYPES = ("BOOL", "U8", "I8", "F8_E4M3", "F8_E5M2", "F8_E8M0", "I16", "U16", "F16", "BF16", "I32", "U32", "F32",

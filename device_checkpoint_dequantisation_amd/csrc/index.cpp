@@ -455,6 +455,29 @@ const Tensor* find(const st_index& ix, const std::string& name, int64_t* idx = n
     return &ix.tensors[it->second];
 }
 
+// An MX weight (kind MXFP8 or MXFP4) of K logical columns (-1: not 2-D) with its E8M0 scale
+// [M, K/32]; fills the output's kind, shape and scale.
+st_status mx_output(const st_index& ix, const Tensor& t, const std::string& x, const Tensor& sc, int64_t sci,
+                    st_kind kind, int64_t k, Output& o) {
+    const char* kn = kind == ST_KIND_MXFP8 ? "MXFP8" : "MXFP4";
+    if (t.shape.size() != 2 || k < 0)
+        return st_fail(ST_E_SHAPE, "%s: %s weight must be 2-D, got %s", t.name.c_str(), kn, shape_str(t.shape).c_str());
+    if (k % 32) return st_fail(ST_E_SHAPE, "%s: %s K=%lld is not a multiple of 32", t.name.c_str(), kn, (long long)k);
+    if (find(ix, x + ".weight_scale_2"))
+        return st_fail(ST_E_SCALE, "%s.weight_scale_2: an E8M0-scaled weight takes no weight_scale_2", x.c_str());
+    const int64_t m = t.shape[0];
+    if (sc.dtype != ST_DT_F8_E8M0 || sc.shape.size() != 2 || sc.shape[0] != m || sc.shape[1] != k / 32)
+        return st_fail(ST_E_SCALE, "%s: must be F8_E8M0 [%lld,%lld], got %s%s", sc.name.c_str(), (long long)m,
+                       (long long)(k / 32), kDtypes[sc.dtype].name, shape_str(sc.shape).c_str());
+    if (k >= (int64_t(1) << 32))
+        return st_fail(ST_E_SHAPE, "%s: %s K of 2^32 or more is not supported", t.name.c_str(), kn);
+    o.kind = kind;
+    o.shape = {m, k};
+    o.numel = uint64_t(m) * uint64_t(k);
+    o.scale = sci;
+    return ST_OK;
+}
+
 st_status classify(st_index& ix) {
     std::vector<bool> used(ix.tensors.size(), false);
     for (uint32_t ti = 0; ti < ix.tensors.size(); ++ti) {
@@ -472,11 +495,17 @@ st_status classify(st_index& ix) {
             if (!ends_with(t.name, ".weight"))
                 return st_fail(ST_E_SCALE, "%s: float8 tensor without a scale (not named X.weight)", t.name.c_str());
             std::string x = t.name.substr(0, t.name.size() - 7);
-            int64_t si = -1, bi = -1;
+            int64_t si = -1, bi = -1, mi = -1;
             const Tensor* st = find(ix, x + ".scale_weight", &si);
             const Tensor* sb = find(ix, x + ".weight_scale_inv", &bi);
-            if (st && sb) return st_fail(ST_E_SCALE, "%s: both scale_weight and weight_scale_inv present", t.name.c_str());
-            if (st) {
+            const Tensor* sm = find(ix, x + ".weight_scale", &mi);
+            if (int(st != nullptr) + int(sb != nullptr) + int(sm != nullptr) > 1)
+                return st_fail(ST_E_SCALE, "%s: more than one of scale_weight, weight_scale_inv, weight_scale present",
+                               t.name.c_str());
+            if (sm) {
+                if (st_status r = mx_output(ix, t, x, *sm, mi, ST_KIND_MXFP8, t.shape.size() == 2 ? t.shape[1] : -1, o))
+                    return r;
+            } else if (st) {
                 if (st->dtype != ST_DT_F32 || !is_scalar(*st))
                     return st_fail(ST_E_SCALE, "%s: scale_weight must be an fp32 scalar, got %s%s", st->name.c_str(),
                                    kDtypes[st->dtype].name, shape_str(st->shape).c_str());
@@ -496,34 +525,42 @@ st_status classify(st_index& ix) {
                 o.kind = ST_KIND_FP8_BLOCK128;
                 o.scale = bi;
             } else {
-                return st_fail(ST_E_SCALE, "%s: float8 weight has no scale_weight or weight_scale_inv", t.name.c_str());
+                return st_fail(ST_E_SCALE, "%s: float8 weight has no scale_weight, weight_scale_inv or weight_scale",
+                               t.name.c_str());
             }
         } else if (t.dtype == ST_DT_U8 || t.dtype == ST_DT_F4) {
             if (!ends_with(t.name, ".weight"))
-                return st_fail(ST_E_DTYPE, "%s: %s tensor is not an NVFP4 weight", t.name.c_str(), dn);
+                return st_fail(ST_E_DTYPE, "%s: %s tensor is not an NVFP4 or MXFP4 weight", t.name.c_str(), dn);
             if (t.shape.size() != 2)
-                return st_fail(ST_E_SHAPE, "%s: NVFP4 weight must be 2-D, got %s", t.name.c_str(), shape_str(t.shape).c_str());
+                return st_fail(ST_E_SHAPE, "%s: packed fp4 weight must be 2-D, got %s", t.name.c_str(),
+                               shape_str(t.shape).c_str());
             std::string x = t.name.substr(0, t.name.size() - 7);
             int64_t m = t.shape[0];
             int64_t k = t.dtype == ST_DT_U8 ? t.shape[1] * 2 : t.shape[1];
-            if (k % 16) return st_fail(ST_E_SHAPE, "%s: NVFP4 K=%lld is not a multiple of 16", t.name.c_str(), (long long)k);
             int64_t bsi = -1, gi = -1;
             const Tensor* bs = find(ix, x + ".weight_scale", &bsi);
             const Tensor* g = find(ix, x + ".weight_scale_2", &gi);
-            if (!bs || !g)
-                return st_fail(ST_E_SCALE, "%s: NVFP4 weight needs weight_scale and weight_scale_2", t.name.c_str());
-            if (bs->dtype != ST_DT_F8_E4M3 || bs->shape.size() != 2 || bs->shape[0] != m || bs->shape[1] != k / 16)
-                return st_fail(ST_E_SCALE, "%s: must be F8_E4M3 [%lld,%lld], got %s%s", bs->name.c_str(), (long long)m,
-                               (long long)(k / 16), kDtypes[bs->dtype].name, shape_str(bs->shape).c_str());
-            if (g->dtype != ST_DT_F32 || !is_scalar(*g))
-                return st_fail(ST_E_SCALE, "%s: weight_scale_2 must be an fp32 scalar", g->name.c_str());
-            if (k >= (int64_t(1) << 32))
-                return st_fail(ST_E_SHAPE, "%s: NVFP4 K of 2^32 or more is not supported", t.name.c_str());
-            o.kind = ST_KIND_NVFP4;
-            o.shape = {m, k};
-            o.numel = uint64_t(m) * uint64_t(k);
-            o.scale = bsi;
-            o.scale2 = gi;
+            if (bs && bs->dtype == ST_DT_F8_E8M0) {  // MXFP4
+                if (st_status r = mx_output(ix, t, x, *bs, bsi, ST_KIND_MXFP4, k, o)) return r;
+            } else {  // NVFP4
+                if (k % 16)
+                    return st_fail(ST_E_SHAPE, "%s: NVFP4 K=%lld is not a multiple of 16", t.name.c_str(), (long long)k);
+                if (!bs || !g)
+                    return st_fail(ST_E_SCALE, "%s: NVFP4 weight needs weight_scale and weight_scale_2", t.name.c_str());
+                if (bs->dtype != ST_DT_F8_E4M3 || bs->shape.size() != 2 || bs->shape[0] != m || bs->shape[1] != k / 16)
+                    return st_fail(ST_E_SCALE, "%s: must be F8_E4M3 [%lld,%lld], got %s%s", bs->name.c_str(),
+                                   (long long)m, (long long)(k / 16), kDtypes[bs->dtype].name,
+                                   shape_str(bs->shape).c_str());
+                if (g->dtype != ST_DT_F32 || !is_scalar(*g))
+                    return st_fail(ST_E_SCALE, "%s: weight_scale_2 must be an fp32 scalar", g->name.c_str());
+                if (k >= (int64_t(1) << 32))
+                    return st_fail(ST_E_SHAPE, "%s: NVFP4 K of 2^32 or more is not supported", t.name.c_str());
+                o.kind = ST_KIND_NVFP4;
+                o.shape = {m, k};
+                o.numel = uint64_t(m) * uint64_t(k);
+                o.scale = bsi;
+                o.scale2 = gi;
+            }
         } else {
             return st_fail(ST_E_DTYPE, "%s: dtype %s cannot be materialised as bf16", t.name.c_str(), dn);
         }
@@ -563,7 +600,7 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
             d.div_magic = stk::div_magic(n);
             div_shift = stk::div_shift(n);
         }
-    } else if (o.kind == ST_KIND_NVFP4) {
+    } else if (o.kind == ST_KIND_NVFP4 || o.kind == ST_KIND_MXFP8 || o.kind == ST_KIND_MXFP4) {
         d.cols = uint32_t(o.shape[1]);
     }
     d.meta = uint32_t(o.kind) | unit_shift << 8 | div_shift << 16;
@@ -661,6 +698,9 @@ st_status resolve_slice(const st_index& ix, const st_slice& sl, Slice& g) {
     if (o.kind == ST_KIND_NVFP4 && (g.c0 % 16 || g.cols() % 16))
         return st_fail(ST_E_SHAPE, "%s: NVFP4 column slices start at and span multiples of 16 (cols [%llu, %llu))",
                        name.c_str(), (unsigned long long)g.c0, (unsigned long long)g.c1);
+    if ((o.kind == ST_KIND_MXFP8 || o.kind == ST_KIND_MXFP4) && (g.c0 % 32 || g.cols() % 32))
+        return st_fail(ST_E_SHAPE, "%s: MX column slices start at and span multiples of 32 (cols [%llu, %llu))",
+                       name.c_str(), (unsigned long long)g.c0, (unsigned long long)g.c1);
     if (g.strided() && (g.rows() * g.cols() >= (uint64_t(1) << 32) || g.C >= (uint64_t(1) << 32)))
         return st_fail(ST_E_SHAPE, "%s: a column slice needs fewer than 2^32 elements and rows shorter than 2^32",
                        name.c_str());
@@ -685,8 +725,12 @@ st_desc make_slice_desc(const st_index& ix, const Output& o, const Slice& g, uin
         d.scale += 4 * ((g.r0 / 128) * d.grid_cols + g.c0 / 128);
     } else if (o.kind == ST_KIND_NVFP4) {
         d.scale += first / 16;
+    } else if (o.kind == ST_KIND_MXFP8 || o.kind == ST_KIND_MXFP4) {
+        d.scale += first / 32;
     }
-    if (o.kind == ST_KIND_FP8_BLOCK128 || o.kind == ST_KIND_NVFP4 || g.strided()) d.cols = uint32_t(width);
+    if (o.kind == ST_KIND_FP8_BLOCK128 || o.kind == ST_KIND_NVFP4 || o.kind == ST_KIND_MXFP8 ||
+        o.kind == ST_KIND_MXFP4 || g.strided())
+        d.cols = uint32_t(width);
     if ((o.kind == ST_KIND_FP8_BLOCK128 || g.strided()) && width) {
         d.div_magic = stk::div_magic(uint32_t(width));
         div_shift = stk::div_shift(uint32_t(width));

@@ -3,8 +3,9 @@
 //
 // What it computes is fixed by the checkpoint formats the pages name ("Resident Modal LLM
 // Architecture", "Current Backend Boundary": Qwen block-FP8, ModelOpt NVFP4; "Disk tier
-// safetensors streaming design audit", "Mandatory research audit": ComfyUI scaled FP8) read as
-// OCP E4M3 / OCP-MX E2M1 codes, one IEEE binary32 round-to-nearest-even multiply per scale and a
+// safetensors streaming design audit", "Mandatory research audit": ComfyUI scaled FP8), plus the
+// OCP Microscaling formats MXFP8 / MXFP4 (E8M0 scale per 32 elements), read as OCP E4M3 /
+// OCP-MX E2M1 codes, one IEEE binary32 round-to-nearest-even multiply per scale and a
 // round-to-nearest-even narrowing to the output type (bfloat16 by default; NaN -> the type's
 // canonical quiet NaN; no subnormal flushing).  A bf16 source copied to a bf16 output keeps its
 // bits.
@@ -96,19 +97,16 @@ __device__ __forceinline__ uint32_t rne_hi(float f) {
 __device__ __forceinline__ uint32_t bf16_canon(float f) { return f != f ? 0x7FC0u : rne_hi(f) >> 16; }
 
 // fp16 bits of f rounded to nearest, ties to even, from the IEEE definition (NaN -> 0x7E00;
-// subnormal results kept; magnitudes from 65520 up -> infinity).
+// subnormal results kept; magnitudes from 65520 up -> infinity).  Below 2^-14 the fp16 code is
+// |f| / 2^-24 rounded to an integer: |f| * 2^24 is exact and below 2^10, and adding then
+// subtracting 2^23 rounds it to nearest even in binary32 (a code of 1024 is the smallest normal).
 __device__ __forceinline__ uint32_t f16_canon(float f) {
     const uint32_t u = as_u32(f), sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
     if (a > 0x7F800000u) return 0x7E00u;
     if (a >= 0x477FF000u) return sign | 0x7C00u;
-    if (a < 0x38800000u) {  // below 2^-14: an fp16 subnormal, or zero
-        const uint32_t e = a >> 23;
-        if (e < 102) return sign;  // below 2^-25 (2^-25 itself ties to zero)
-        const uint32_t m = (a & 0x7FFFFFu) | 0x800000u, sh = 126 - e;  // 14 <= sh <= 24
-        uint32_t q = m >> sh;
-        const uint32_t rem = m & ((1u << sh) - 1), half = 1u << (sh - 1);
-        if (rem > half || (rem == half && (q & 1u))) ++q;
-        return sign | q;
+    if (a < 0x38800000u) {
+        const float y = as_f32(a) * 16777216.0f + 8388608.0f;
+        return sign | uint32_t(y - 8388608.0f);
     }
     const uint32_t t = a + 0xFFFu + ((a >> 13) & 1u);
     return sign | ((t >> 13) - (112u << 10));
@@ -127,6 +125,11 @@ __device__ __forceinline__ float e4m3_exact(uint32_t c) {
     return (c & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : e4m3_x2m8(c) * 256.0f;
 }
 __device__ __forceinline__ float e2m1_exact(uint32_t n) { return e2m1_x2m14(n) * 16384.0f; }
+// E8M0 scale code -> 2^(c - 127) as binary32: exponent field c, or for c = 0 the subnormal 2^-127
+// (mantissa bit 22); 0xFF is NaN.  Used on both paths: the value is exact either way.
+__device__ __forceinline__ float e8m0_exact(uint32_t c) {
+    return c == 0xFFu ? __builtin_nanf("") : as_f32(c != 0 ? c << 23 : 0x00400000u);
+}
 
 // True if any byte of x is an e4m3 NaN code (0x7F or 0xFF).
 __device__ __forceinline__ bool has_nan_code(uint32_t x) {
@@ -246,12 +249,17 @@ __device__ __forceinline__ float kind_value(const uint8_t* __restrict__ blob, co
         const uint32_t col = e32 - row * D.cols;
         const float S = as_f32(ld_u32_any(blob + D.scale + 4ull * ((row >> 7) * D.grid_cols + (col >> 7))));
         return e4m3_exact(ld_u8(s + x)) * S;
-    } else {  // NVFP4: K % 16 == 0, so block scale (i, j / 16) sits at flat source index x / 16
+    } else if constexpr (KIND == ST_KIND_NVFP4) {  // K % 16 == 0: block scale (i, j / 16) at flat index x / 16
         const uint32_t nib = (ld_u8(s + (x >> 1)) >> ((x & 1) * 4)) & 15u;
         const float bs = e4m3_exact(ld_u8(blob + D.scale + (x >> 4)));
         const float g = as_f32(ld_u32_any(blob + D.scale2));
         const float t = e2m1_exact(nib) * bs;
         return t * g;
+    } else {  // MXFP8 / MXFP4: K % 32 == 0: scale (i, j / 32) at flat index x / 32
+        static_assert(KIND == ST_KIND_MXFP8 || KIND == ST_KIND_MXFP4, "kind");
+        const float S = e8m0_exact(ld_u8(blob + D.scale + (x >> 5)));
+        if constexpr (KIND == ST_KIND_MXFP8) return e4m3_exact(ld_u8(s + x)) * S;
+        else return e2m1_exact((ld_u8(s + (x >> 1)) >> ((x & 1) * 4)) & 15u) * S;
     }
 }
 
@@ -410,8 +418,42 @@ struct KFp4 : Geom<ST_KIND_NVFP4> {
     }
 };
 
-static_assert(KPass::IB == 16 && KF32::IB == 32 && KFp8Tensor::IB == 8 && KFp4::IB == 4, "chunk geometry");
-static_assert(KPass::CH == 2 && KF32::CH == 1 && KFp8Tensor::CH == 2 && KFp4::CH == 4, "chunks per lane");
+// OCP Microscaling: 8 elements from source element xs (a multiple of 8) share the E8M0 scale of
+// their 32-element block, applied by one RNE multiply; an NaN scale or element code takes the
+// exact path.
+struct KMx8 : Geom<ST_KIND_MXFP8> {
+    static constexpr int SCALE = 0;  // no scalar scale
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
+    template <class O>
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
+        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
+        if (code == 0xFFu) return false;
+        return fp8_chunk<O>(in, e8m0_exact(code), w);
+    }
+};
+
+struct KMx4 : Geom<ST_KIND_MXFP4> {
+    static constexpr int SCALE = 0;  // no scalar scale
+    static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
+    template <class O>
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
+        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
+        if (code == 0xFFu) return false;
+        const float S = e8m0_exact(code);
+        const uint32_t x = in[0];
+        const f32x2 p0 = fp4x2<0>(x), p1 = fp4x2<1>(x), p2 = fp4x2<2>(x), p3 = fp4x2<3>(x);
+        put2<O>(w, 0, p0.x * S, p0.y * S);
+        put2<O>(w, 1, p1.x * S, p1.y * S);
+        put2<O>(w, 2, p2.x * S, p2.y * S);
+        put2<O>(w, 3, p3.x * S, p3.y * S);
+        return true;
+    }
+};
+
+static_assert(KPass::IB == 16 && KF32::IB == 32 && KFp8Tensor::IB == 8 && KFp4::IB == 4 && KMx8::IB == 8 &&
+                  KMx4::IB == 4, "chunk geometry");
+static_assert(KPass::CH == 2 && KF32::CH == 1 && KFp8Tensor::CH == 2 && KFp4::CH == 4 && KMx8::CH == 2 &&
+                  KMx4::CH == 4, "chunks per lane");
 
 // ------------------------------------------------------------------------- loads
 
@@ -692,6 +734,8 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
                 case ST_KIND_NVFP4: unit_exact<ST_KIND_NVFP4, O>(c, e0, cnt, lane); break;
                 case ST_KIND_PASS_BF16: unit_exact<ST_KIND_PASS_BF16, O>(c, e0, cnt, lane); break;
                 case ST_KIND_CAST_F16: unit_exact<ST_KIND_CAST_F16, O>(c, e0, cnt, lane); break;
+                case ST_KIND_MXFP8: unit_exact<ST_KIND_MXFP8, O>(c, e0, cnt, lane); break;
+                case ST_KIND_MXFP4: unit_exact<ST_KIND_MXFP4, O>(c, e0, cnt, lane); break;
                 default: unit_exact<ST_KIND_CAST_F32, O>(c, e0, cnt, lane); break;
             }
             return;
@@ -702,6 +746,8 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
             case ST_KIND_NVFP4: run_strided<KFp4, O>(c, e0, cnt, lane); break;
             case ST_KIND_PASS_BF16: run_strided<KPass, O>(c, e0, cnt, lane); break;
             case ST_KIND_CAST_F16: run_strided<KF16, O>(c, e0, cnt, lane); break;
+            case ST_KIND_MXFP8: run_strided<KMx8, O>(c, e0, cnt, lane); break;
+            case ST_KIND_MXFP4: run_strided<KMx4, O>(c, e0, cnt, lane); break;
             default: run_strided<KF32, O>(c, e0, cnt, lane); break;
         }
         return;
@@ -712,6 +758,8 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
         case ST_KIND_NVFP4: run_unit<KFp4, O>(c, e0, cnt, lane); break;
         case ST_KIND_PASS_BF16: run_unit<KPass, O>(c, e0, cnt, lane); break;
         case ST_KIND_CAST_F16: run_unit<KF16, O>(c, e0, cnt, lane); break;
+        case ST_KIND_MXFP8: run_unit<KMx8, O>(c, e0, cnt, lane); break;
+        case ST_KIND_MXFP4: run_unit<KMx4, O>(c, e0, cnt, lane); break;
         default: run_unit<KF32, O>(c, e0, cnt, lane); break;
     }
 }

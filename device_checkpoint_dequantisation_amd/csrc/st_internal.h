@@ -41,7 +41,7 @@ constexpr uint32_t ilog2(uint32_t x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 constexpr uint32_t words_per_lane(uint32_t kind) {
     return kind == ST_KIND_PASS_BF16 || kind == ST_KIND_CAST_F16 ? kWordsPass
          : kind == ST_KIND_CAST_F32                              ? kWordsF32
-         : kind == ST_KIND_NVFP4                                 ? kWordsFp4
+         : kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4        ? kWordsFp4
                                                                  : kWordsFp8;
 }
 // The kernel's chunk geometry per kind: output elements per chunk (8 for every kind: one 16-byte
@@ -50,14 +50,16 @@ constexpr uint32_t words_per_lane(uint32_t kind) {
 // width is a whole number of chunks and its row length in bytes is a whole number of load words.
 constexpr uint32_t chunk_elems(uint32_t) { return 8; }
 constexpr uint32_t load_word_bytes(uint32_t kind) {
-    return kind == ST_KIND_NVFP4 ? 4 : kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_FP8_BLOCK128 ? 8 : 16;
+    return kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4 ? 4
+         : kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_FP8_BLOCK128 || kind == ST_KIND_MXFP8 ? 8
+                                                                                               : 16;
 }
 // Source bits per element.
 constexpr uint32_t source_bits(uint32_t kind) {
     return kind == ST_KIND_CAST_F32 ? 32
          : kind == ST_KIND_PASS_BF16 || kind == ST_KIND_CAST_F16 ? 16
-         : kind == ST_KIND_NVFP4 ? 4
-                                 : 8;
+         : kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4 ? 4
+                                                           : 8;
 }
 
 // Where the descriptors start in a work table of `groups` map entries.

@@ -35,7 +35,7 @@ class OutputMeta:
     name: str
     index: int          # output index in the checkpoint
     shape: tuple
-    kind: str           # PASS_BF16, CAST_F16, CAST_F32, FP8_TENSOR, FP8_BLOCK128, NVFP4
+    kind: str           # PASS_BF16, CAST_F16, CAST_F32, FP8_TENSOR, FP8_BLOCK128, NVFP4, MXFP8, MXFP4
     source_dtype: str   # safetensors dtype of the stored weight
     source_bytes: int   # bytes read to materialise it (weight and scale tensors)
 

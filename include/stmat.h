@@ -30,7 +30,13 @@
  *   NVFP4         bf16((e2m1(q[i,j]) * e4m3(bs[i,j/16])) * g)
  *                 X.weight U8 [M,K/2] (element 2k in the low nibble of byte k) or F4 [M,K] +
  *                 X.weight_scale F8_E4M3 [M,K/16] + X.weight_scale_2 F32 []
- * e4m3 is OCP E4M3 "fn" (bias 7, no infinities, NaN at S.1111.111); e2m1 is OCP-MX E2M1.
+ *   MXFP8         bf16(e4m3(w[i,j]) * e8m0(s[i,j/32]))  X.weight F8_E4M3 [M,K] +
+ *                                                  X.weight_scale F8_E8M0 [M,K/32]
+ *   MXFP4         bf16(e2m1(q[i,j]) * e8m0(s[i,j/32]))  X.weight U8 [M,K/2] or F4 [M,K] +
+ *                                                  X.weight_scale F8_E8M0 [M,K/32]
+ * e4m3 is OCP E4M3 "fn" (bias 7, no infinities, NaN at S.1111.111); e2m1 is OCP-MX E2M1; e8m0 is
+ * the OCP Microscaling scale 2^(e-127), NaN at 0xFF (the formats of the OCP Microscaling
+ * specification: 32 consecutive elements of a row share a scale; K must be a multiple of 32).
  *
  * Errors.  Every call returns ST_OK (0) or a negative st_status; nothing throws across the ABI.
  * st_last_error() then names the tensor, the field and the measured values.
@@ -69,7 +75,8 @@ typedef enum st_dtype {
 
 typedef enum st_kind {
     ST_KIND_PASS_BF16 = 0, ST_KIND_CAST_F16 = 1, ST_KIND_CAST_F32 = 2,
-    ST_KIND_FP8_TENSOR = 3, ST_KIND_FP8_BLOCK128 = 4, ST_KIND_NVFP4 = 5
+    ST_KIND_FP8_TENSOR = 3, ST_KIND_FP8_BLOCK128 = 4, ST_KIND_NVFP4 = 5,
+    ST_KIND_MXFP8 = 6, ST_KIND_MXFP4 = 7
 } st_kind;
 
 /* Output element type, chosen per index (st_plan_opts.flags).  Every output element is the fp32

@@ -23,7 +23,7 @@ import device_checkpoint_dequantisation_amd as st
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-QUANT = ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4")
+QUANT = ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4", "MXFP8", "MXFP4")
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
 
 
@@ -32,7 +32,7 @@ def _sample_idx(shape, numel, rng, n_rand=256):
     if len(shape) == 2:
         rows, cols = shape
         for r in (0, 127, 128, rows // 2, rows - 1):
-            for c in (0, 15, 16, 127, 128, cols // 2, cols - 1):
+            for c in (0, 15, 16, 31, 32, 127, 128, cols // 2, cols - 1):
                 if r < rows and c < cols:
                     idx.append(r * cols + c)
     return np.unique(np.array(idx, dtype=np.int64))
@@ -70,10 +70,18 @@ def _torch_reference(kind, shape, blob, src, scale, scale2):
         table = torch.tensor(E2M1, dtype=torch.float32, device=blob.device)
         bs = _e4m3(blob[scale: scale + numel // 16]).repeat_interleave(16)
         return ((table[nib] * bs) * _f32(blob, scale2, 1)).to(torch.bfloat16)
+    if kind in ("MXFP8", "MXFP4"):   # E8M0 scale per 32 elements, decoded by torch on the CPU
+        S = blob[scale: scale + numel // 32].cpu().view(torch.float8_e8m0fnu).float().to(blob.device)
+        S = S.repeat_interleave(32)
+        if kind == "MXFP8":
+            return (_e4m3(blob[src: src + numel]) * S).to(torch.bfloat16)
+        packed = blob[src: src + numel // 2]
+        nib = torch.stack([packed & 15, packed >> 4], dim=1).view(-1).long()
+        return (torch.tensor(E2M1, dtype=torch.float32, device=blob.device)[nib] * S).to(torch.bfloat16)
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
+@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 7])
 def test_full_size_checkpoint(k, tmp_path):
     path = str(tmp_path / f"c{k}.safetensors")
     print(f"full-size config {k}: writing", flush=True)

@@ -26,7 +26,7 @@ def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_every_key_matches_the_oracle(k, tmp_path):
     path, buf = _file(tmp_path, k)
     want = oracle.materialize(buf)

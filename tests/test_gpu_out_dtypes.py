@@ -10,8 +10,10 @@ import torch
 import oracle
 import synth
 import device_checkpoint_dequantisation_amd as st
-from tests.test_gpu_parity import block_fp8_file, float_every_code_file, fp8_every_code_file, nvfp4_every_code_file
+from tests.test_gpu_parity import (block_fp8_file, float_every_code_file, fp8_every_code_file, mx_every_code_file,
+                                   nvfp4_every_code_file)
 from tests.test_gpu_slices import _slices_for, _view
+from tests.st_files import make_file
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -55,7 +57,7 @@ def assert_parity(buf, out_dtype, **kw):
 
 
 @pytest.mark.parametrize("out_dtype", TYPES)
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_configs_small(k, out_dtype):
     assert_parity(synth.config_bytes(k, small=k != 1), out_dtype)
 
@@ -91,6 +93,13 @@ def test_float_sources_every_code(shift, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", TYPES)
+@pytest.mark.parametrize("kind", ["MXFP8", "MXFP4"])
+@pytest.mark.parametrize("shift", [0, 3])
+def test_mx_every_code(kind, shift, out_dtype):
+    assert_parity(mx_every_code_file(kind, shift), out_dtype)
+
+
+@pytest.mark.parametrize("out_dtype", TYPES)
 def test_outputs_not_aligned_to_16_bytes(out_dtype):
     """Every output shifted by one element: the exact path writes them one at a time."""
     buf = synth.config_bytes(2, small=True)
@@ -123,7 +132,7 @@ def test_output_type_mismatch_writes_nothing(planned, launch):
 
 @pytest.mark.parametrize("strided_kernel", [True, False])
 @pytest.mark.parametrize("out_dtype", TYPES)
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
+@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 7])
 def test_slices(k, out_dtype, strided_kernel):
     buf = synth.config_bytes(k, small=True)
     want = oracle.materialize(buf, out_dtype)
@@ -176,3 +185,34 @@ def test_lazy_loads(k, out_dtype, tmp_path):
                 _assert_equal((ram, name), _bits(got[name]).reshape(w.shape), w)
         for name in names[:: max(1, len(names) // 10)]:
             _assert_equal(name, _bits(sd[name]).reshape(want[name].shape), want[name])
+
+
+def _f16_rounding_file():
+    """fp32 inputs covering every fp16 rounding class: every finite fp16 value, every midpoint
+    between neighbours (ties, including the subnormal ties down to 2^-25), one fp32 ulp either
+    side of each midpoint, the overflow boundary, and both signs."""
+    codes = np.arange(0x7C00, dtype=np.uint32)
+    vals = codes.astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    mid32 = mids.astype(np.float32)
+    extra = np.array([2.0 ** -25, 65504.0, 65519.99, 65520.0, 1e30], dtype=np.float32)
+    x = np.concatenate([vals.astype(np.float32), mid32, np.nextafter(mid32, np.float32(np.inf)),
+                        np.nextafter(mid32, np.float32(0)), extra])
+    x = np.concatenate([x, -x])
+    return make_file([("f", "F32", (x.size,), x)])
+
+
+@pytest.mark.parametrize("shift", [0, 1])
+def test_f16_rounding_every_class_both_paths(shift):
+    """Aligned outputs take the vector conversion; outputs shifted by one element take the exact
+    path's software rounding.  Both must equal the oracle on every rounding class."""
+    buf = _f16_rounding_file()
+    ix, ck = _staged(buf, "f16")
+    want = oracle.materialize(buf, "f16")["f"]
+    o = ix.outputs()[0]
+    arena = torch.empty(o.numel + 64, dtype=torch.float16, device=DEV)
+    arena.view(torch.int16).fill_(0x5A5A)
+    ptrs = torch.tensor([arena.data_ptr() + 2 * shift], dtype=torch.int64).to(DEV)
+    st.materialize(ck.blob, ck.table, ck.units, ptrs, out_dtype="f16")
+    torch.cuda.synchronize()
+    _assert_equal(("f16 rounding", shift), _bits(arena[shift: shift + o.numel]), want)

@@ -40,12 +40,12 @@ def assert_parity(buf: bytes, **kw):
     return ck
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_configs_small(k):
     assert_parity(synth.config_bytes(k, small=k != 1))
 
 
-@pytest.mark.parametrize("k", [1, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("scale", [1, 3, 6])
 def test_larger_work_units(k, scale):
     assert_parity(synth.config_bytes(k, small=k != 1), unit_log2_scale=scale)
@@ -101,6 +101,26 @@ def block_fp8_file(M, N, shift):
     return make_file(tensors)
 
 
+def mx_every_code_file(kind, shift, storage="U8"):
+    """MXFP8: rows of K = 288 (9 scale blocks), every e4m3 code against every E8M0 scale code
+    (NaN and the subnormal 2^-127 included); MXFP4: every e2m1 code against every scale code."""
+    if kind == "MXFP8":
+        M, K = 256, 288
+        codes = np.tile(np.arange(256, dtype=np.uint8), M * K // 256 + 1)[: M * K]
+        scales = np.arange(M * K // 32, dtype=np.uint32).astype(np.uint8)
+        tensors = list(_pad(shift)) + [("x.weight", "F8_E4M3", (M, K), codes),
+                                       ("x.weight_scale", "F8_E8M0", (M, K // 32), scales)]
+    else:
+        M, K = 256, 96
+        nib = np.tile(np.arange(16, dtype=np.uint8), M * K // 16)
+        packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+        scales = np.roll(np.arange(M * K // 32, dtype=np.uint32).astype(np.uint8), 7)
+        shape = (M, K // 2) if storage == "U8" else (M, K)
+        tensors = list(_pad(shift)) + [("x.weight", storage, shape, packed),
+                                       ("x.weight_scale", "F8_E8M0", (M, K // 32), scales)]
+    return make_file(tensors)
+
+
 def float_every_code_file(shift):
     """Every fp16 code, random fp32 words with their specials, random bf16 words."""
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
@@ -132,6 +152,12 @@ def test_block_fp8_ragged_shapes(M, N, shift):
 @pytest.mark.parametrize("shift", [0, 1, 2, 3, 7])
 def test_f16_every_code_and_f32_specials(shift):
     assert_parity(float_every_code_file(shift))
+
+
+@pytest.mark.parametrize("kind,storage", [("MXFP8", None), ("MXFP4", "U8"), ("MXFP4", "F4")])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3, 5, 9])
+def test_mx_every_code_every_scale(kind, storage, shift):
+    assert_parity(mx_every_code_file(kind, shift, storage or "U8"))
 
 
 def test_many_small_full_stress_config():

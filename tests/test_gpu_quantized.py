@@ -22,12 +22,18 @@ def _decode(q):
         S = q.scale.repeat_interleave(128, 0)[:m].repeat_interleave(128, 1)[:, :n]
         return (q.data.float() * S).to(torch.bfloat16)
     m, k = q.shape
+    if q.kind in ("MXFP8", "MXFP4"):   # torch's E8M0 decoding, on the CPU
+        S = q.scale.cpu().float().to(q.data.device).repeat_interleave(32, 1)
+        if q.kind == "MXFP8":
+            return (q.data.float() * S).to(torch.bfloat16)
+        nib = torch.stack([q.data & 15, q.data >> 4], dim=-1).reshape(m, k).long()
+        return (torch.tensor(E2M1, device=q.data.device)[nib] * S).to(torch.bfloat16)
     nib = torch.stack([q.data & 15, q.data >> 4], dim=-1).reshape(m, k).long()
     t = torch.tensor(E2M1, device=q.data.device)[nib] * q.scale.float().repeat_interleave(16, 1)
     return (t * q.scale2).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("k", [2, 3, 4, 6, 7])
 @pytest.mark.parametrize("copy", [True, False])
 def test_quantized_passthrough(k, copy, tmp_path):
     buf = synth.config_bytes(k, small=True)
@@ -40,7 +46,7 @@ def test_quantized_passthrough(k, copy, tmp_path):
     data = np.frombuffer(buf, np.uint8)[ix.data_offset:]
     ents = ix.tensors()
     outs = {o.name: o for o in ix.outputs()}
-    assert qs and set(qs) == {n for n, o in outs.items() if o.kind in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4")}
+    assert qs and set(qs) == {n for n, o in outs.items() if o.kind in st.QUANTIZED_KINDS}
     for name, q in qs.items():
         o = outs[name]
         w = ents[o.tensor]
@@ -52,7 +58,7 @@ def test_quantized_passthrough(k, copy, tmp_path):
         else:
             assert q.data.data_ptr() == ck.blob.data_ptr() + w.begin
         assert torch.equal(_decode(q).view(torch.int16), ck.tensors[name].view(torch.int16)), name
-    plain = [n for n, o in outs.items() if o.kind not in ("FP8_TENSOR", "FP8_BLOCK128", "NVFP4")]
+    plain = [n for n, o in outs.items() if o.kind not in st.QUANTIZED_KINDS]
     if plain:
         with pytest.raises(ValueError):
             ck.quantized(plain[:1])

@@ -40,9 +40,10 @@ def _slices_for(o, rng):
     shape = o.shape
     R = 1 if not shape else shape[0]
     C = 1 if len(shape) <= 1 else int(np.prod(shape[1:]))
+    mx = o.kind in ("MXFP8", "MXFP4")
     rq = 128 if o.kind == "FP8_BLOCK128" else 1
-    cq = 128 if o.kind == "FP8_BLOCK128" else 16 if o.kind == "NVFP4" else 1
-    wq = 16 if o.kind == "NVFP4" else 1
+    cq = 128 if o.kind == "FP8_BLOCK128" else 16 if o.kind == "NVFP4" else 32 if mx else 1
+    wq = 16 if o.kind == "NVFP4" else 32 if mx else 1
     out = [(None, None), ((0, 0), None)]
     for _ in range(4):
         r0 = int(rng.integers(0, R // rq + 1)) * rq
@@ -57,7 +58,7 @@ def _slices_for(o, rng):
 
 
 @pytest.mark.parametrize("strided_kernel", [True, False])
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_slices_match_the_oracle(k, strided_kernel):
     buf = synth.config_bytes(k, small=k != 1)
     want = oracle.materialize(buf)

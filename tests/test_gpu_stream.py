@@ -32,7 +32,7 @@ def _stream(path, chunk_mb=None, chunk_bytes=None, stream=None):
     return ck, stats
 
 
-@pytest.mark.parametrize("variant", ["c1", "c2", "c3", "c4", "c5", "c2_scales_last"])
+@pytest.mark.parametrize("variant", ["c1", "c2", "c3", "c4", "c5", "c6", "c7", "c2_scales_last"])
 @pytest.mark.parametrize("chunk", [64 << 10, 300_000])
 def test_stream_small_matches_oracle(variant, chunk, tmp_path):
     k = int(variant[1])

@@ -32,7 +32,7 @@ def _index(buf):
     return st.SafeTensorIndex.from_bytes(buf)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_index_matches_oracle_on_configs(k):
     buf = synth.config_bytes(k, small=True)
     h, outs = oracle.plan(buf)
@@ -233,11 +233,19 @@ def _mutations(buf: bytes, rng, count):
         yield len(h).to_bytes(8, "little") + bytes(h) + data
 
 
-def test_random_header_mutations_accept_and_reject_alike():
+MUTATION_BASES = {
+    "fp8": make_file([("a.weight", "F8_E4M3", (2, 3), b"\x01" * 6), ("a.scale_weight", "F32", (), f32_bytes(0.5)),
+                      ("b", "BF16", (2,), b"\0" * 4), ("c", "F16", (1, 1), b"\0\0")], metadata={"x": "y"}),
+    "mx": make_file([("a.weight", "F8_E4M3", (2, 32), b"\x01" * 64), ("a.weight_scale", "F8_E8M0", (2, 1), b"\x7f" * 2),
+                     ("m.weight", "U8", (1, 16), b"\x21" * 16), ("m.weight_scale", "F8_E8M0", (1, 1), b"\x80")]),
+}
+
+
+@pytest.mark.parametrize("base", sorted(MUTATION_BASES))
+def test_random_header_mutations_accept_and_reject_alike(base):
     # The C reader and the oracle must agree on acceptance for corrupted headers and, when both
     # accept, on the parsed entries.
-    base = make_file([("a.weight", "F8_E4M3", (2, 3), b"\x01" * 6), ("a.scale_weight", "F32", (), f32_bytes(0.5)),
-                      ("b", "BF16", (2,), b"\0" * 4), ("c", "F16", (1, 1), b"\0\0")], metadata={"x": "y"})
+    base = MUTATION_BASES[base]
     rng = np.random.default_rng(11)
     agree = accepted = 0
     for m in _mutations(base, rng, 600):
@@ -294,3 +302,15 @@ def _build(buf, flags, scale):
     opts = _lib.PlanOpts(scale, flags)
     raw = C.create_string_buffer(bytes(buf), len(buf))
     st.check(_lib.lib().st_index_build(raw, len(buf), len(buf), C.byref(opts), C.byref(h)), "st_index_build")
+
+
+def test_mx_rejections_match_the_oracle():
+    from tests.test_oracle_mx import test_mx_malformed_is_rejected as case
+    for mark in case.pytestmark:
+        if mark.name == "parametrize":
+            for tensors, _ in mark.args[1]:
+                buf = make_file(tensors)
+                with pytest.raises(oracle.OracleError):
+                    oracle.plan(buf)
+                with pytest.raises(st.StError):
+                    _index(buf)

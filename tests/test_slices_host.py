@@ -82,6 +82,25 @@ def test_nvfp4_slices():
         ix.table_slices([(k, None, (16, 40))])
 
 
+@pytest.mark.parametrize("k,kind", [(6, "MXFP8"), (7, "MXFP4")])
+def test_mx_slices(k, kind):
+    ix = st.SafeTensorIndex.from_bytes(synth.config_bytes(k, small=True))
+    kk, o = next((kk, o) for kk, o in enumerate(ix.outputs()) if o.kind == kind)
+    ents = ix.tensors()
+    M, K = o.shape
+    raw, _ = ix.table_slices([(kk, (3, 9), (32, 96)), (kk, (5, 7), None)])
+    _, d, _ = _table(raw)
+    first = 3 * K + 32
+    nbits = 8 if kind == "MXFP8" else 4
+    assert d[0]["pitch"] == K and d[0]["cols"] == 64 and d[0]["flags"] == 0
+    assert d[0]["src"] == ents[o.tensor].begin + first * nbits // 8
+    assert d[0]["scale"] == ents[o.scale].begin + first // 32
+    assert d[1]["pitch"] == 0 and d[1]["scale"] == ents[o.scale].begin + 5 * K // 32
+    for cols in ((16, 48), (32, 48)):
+        with pytest.raises(st.StError, match="multiples of 32"):
+            ix.table_slices([(kk, None, cols)])
+
+
 def test_refused_cuts(ix3):
     q = _k(ix3, "model.layers.0.self_attn.q_proj.weight")
     with pytest.raises(st.StError, match="multiples of 128"):
