@@ -598,45 +598,51 @@ __device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cn
         store_elem<O>(out, e0 + t, kind_exact<K::KIND, O>(c.blob, c.D, e0 + t));
 }
 
-// A unit of a column slice: chunk starts are mapped to their source elements one by one (the
-// host guarantees that a chunk never crosses a row and that every chunk has the alignment of the
-// slice's first source byte, or marks the descriptor exact-only).  A whole unit issues all of a
-// lane's loads before decoding, like unit_full; a partial one walks its chunks.
+// A whole unit of a column slice: chunk starts are mapped to their source elements one by one
+// (the host guarantees that a chunk never crosses a row and that every chunk has the alignment of
+// the slice's first source byte, or marks the descriptor exact-only).  All of a lane's loads are
+// issued before decoding, like unit_full.
 template <class K, class O, bool ALIGNED>
-__device__ __forceinline__ void unit_strided(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+__device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
     using F = Fetch<K, ALIGNED>;
     constexpr uint32_t NW = K::CE * O::BYTES / 4;
     const uint8_t* base = c0.blob + c0.D.src - sh;
-    if (cnt == K::CE * K::CH * stk::kWave) {
-        uint32_t raw[K::CH][F::RW];
-        uint64_t xs[K::CH];
+    uint32_t raw[K::CH][F::RW];
+    uint64_t xs[K::CH];
 #pragma unroll
-        for (uint32_t j = 0; j < K::CH; ++j) {
-            xs[j] = src_elem(c0.D, e0 + uint64_t(j * stk::kWave + lane) * K::CE);
-            F::load(base + K::src_off(xs[j]), 0, raw[j]);
-        }
-        Ctx c = c0;
-        uint8_t* out;
-        if (!finish_ctx<K, O>(c, out)) return;
-        uint8_t* const ob = out + e0 * O::BYTES;
-        bool ok[K::CH];
-#pragma unroll
-        for (uint32_t j = 0; j < K::CH; ++j) {
-            uint32_t in[F::N], w[NW];
-            F::align(raw[j], sh, in);
-            const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-            ok[j] = c.vec && K::template fast<O>(c, in, e, xs[j], w);
-            if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
-        }
-        bool all = true;
-#pragma unroll
-        for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
-        if (__builtin_amdgcn_ballot_w64(!all) == 0) return;
-#pragma unroll
-        for (uint32_t j = 0; j < K::CH; ++j)
-            if (!ok[j]) run_exact<K::KIND, O>(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
-        return;
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        xs[j] = src_elem(c0.D, e0 + uint64_t(j * stk::kWave + lane) * K::CE);
+        F::load(base + K::src_off(xs[j]), 0, raw[j]);
     }
+    Ctx c = c0;
+    uint8_t* out;
+    if (!finish_ctx<K, O>(c, out)) return;
+    uint8_t* const ob = out + e0 * O::BYTES;
+    bool ok[K::CH];
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        uint32_t in[F::N], w[NW];
+        F::align(raw[j], sh, in);
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        ok[j] = c.vec && K::template fast<O>(c, in, e, xs[j], w);
+        if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
+    }
+    bool all = true;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+    if (__builtin_amdgcn_ballot_w64(!all) == 0) return;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j)
+        if (!ok[j]) run_exact<K::KIND, O>(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
+}
+
+// A partial unit of a column slice (or any unit of a larger unit size): the lane walks its chunks,
+// then the elements past the last whole chunk.  Unaligned loads, correct at any alignment.
+template <class K, class O>
+__device__ __forceinline__ void unit_strided_any(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, false>;
+    constexpr uint32_t NW = K::CE * O::BYTES / 4;
+    const uint8_t* base = c0.blob + c0.D.src - sh;
     Ctx c = c0;
     uint8_t* out;
     if (!finish_ctx<K, O>(c, out)) return;
@@ -659,8 +665,9 @@ __device__ __forceinline__ void unit_strided(const Ctx& c0, uint64_t e0, uint32_
 template <class K, class O>
 __device__ __forceinline__ void run_strided(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
     const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src));
-    if ((a & (K::LG - 1)) == 0) unit_strided<K, O, true>(c, e0, cnt, 0, lane);
-    else unit_strided<K, O, false>(c, e0, cnt, a & 3u, lane);
+    if (cnt != K::CE * K::CH * stk::kWave) unit_strided_any<K, O>(c, e0, cnt, a & 3u, lane);
+    else if ((a & (K::LG - 1)) == 0) unit_strided_full<K, O, true>(c, e0, 0, lane);
+    else unit_strided_full<K, O, false>(c, e0, a & 3u, lane);
 }
 
 // Every element of a unit through the exact path (descriptors the host marks exact-only).
@@ -672,19 +679,17 @@ __device__ __forceinline__ void unit_exact(const Ctx& c, uint64_t e0, uint32_t c
     for (uint32_t t = lane; t < cnt; t += stk::kWave) store_elem<O>(out, e0 + t, kind_exact<KIND, O>(c.blob, c.D, e0 + t));
 }
 
-template <class K, class O, bool ALIGNED>
-__device__ __forceinline__ void unit_dispatch(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
-    if (cnt == K::CE * K::CH * stk::kWave) unit_full<K, O, ALIGNED>(c, e0, sh, lane);
-    else unit_any<K, O, ALIGNED>(c, e0, cnt, sh, lane);
-}
-
-// Aligned: the unit's source starts on an LG-byte boundary; otherwise sh = its offset within a
-// 4-byte word (0 for a 4-byte-aligned source that is not 16-byte aligned).
+// A whole unit takes the aligned or unaligned fast path by its source alignment; a partial unit (an
+// output's last, or any unit of a larger unit size) always takes the unaligned form, which is
+// correct at any alignment, so that the kernel holds one copy of it per kind.  Aligned: the source
+// starts on an LG-byte boundary; otherwise sh = its offset within a 4-byte word (0 for a
+// 4-byte-aligned source that is not LG-aligned).
 template <class K, class O>
 __device__ __forceinline__ void run_unit(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
     const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)));
-    if ((a & (K::LG - 1)) == 0) unit_dispatch<K, O, true>(c, e0, cnt, 0, lane);
-    else unit_dispatch<K, O, false>(c, e0, cnt, a & 3u, lane);
+    if (cnt != K::CE * K::CH * stk::kWave) unit_any<K, O, false>(c, e0, cnt, a & 3u, lane);
+    else if ((a & (K::LG - 1)) == 0) unit_full<K, O, true>(c, e0, 0, lane);
+    else unit_full<K, O, false>(c, e0, a & 3u, lane);
 }
 
 // ------------------------------------------------------------------------- the kernel
