@@ -405,7 +405,6 @@ struct KFp4 : Geom<ST_KIND_NVFP4> {
     template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 4));  // block scale of these 8 elements
-        if (!finite(c.s) || (code & 0x7Fu) == 0x7Fu) return false;
         const float bs = fp8x2<false>(code).x;
         const float g = c.s;
         const uint32_t x = in[0];
@@ -414,7 +413,7 @@ struct KFp4 : Geom<ST_KIND_NVFP4> {
         put2<O>(w, 1, (p1.x * bs) * g, (p1.y * bs) * g);
         put2<O>(w, 2, (p2.x * bs) * g, (p2.y * bs) * g);
         put2<O>(w, 3, (p3.x * bs) * g, (p3.y * bs) * g);
-        return true;
+        return finite(g) & ((code & 0x7Fu) != 0x7Fu);  // decided last: see unit_full
     }
 };
 
@@ -427,8 +426,7 @@ struct KMx8 : Geom<ST_KIND_MXFP8> {
     template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
-        if (code == 0xFFu) return false;
-        return fp8_chunk<O>(in, e8m0_exact(code), w);
+        return fp8_chunk<O>(in, e8m0_exact(code), w);  // a NaN scale code fails its finite check
     }
 };
 
@@ -438,7 +436,6 @@ struct KMx4 : Geom<ST_KIND_MXFP4> {
     template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
-        if (code == 0xFFu) return false;
         const float S = e8m0_exact(code);
         const uint32_t x = in[0];
         const f32x2 p0 = fp4x2<0>(x), p1 = fp4x2<1>(x), p2 = fp4x2<2>(x), p3 = fp4x2<3>(x);
@@ -446,7 +443,7 @@ struct KMx4 : Geom<ST_KIND_MXFP4> {
         put2<O>(w, 1, p1.x * S, p1.y * S);
         put2<O>(w, 2, p2.x * S, p2.y * S);
         put2<O>(w, 3, p3.x * S, p3.y * S);
-        return true;
+        return code != 0xFFu;  // decided last: see unit_full
     }
 };
 
@@ -552,9 +549,16 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
     uint32_t raw[K::CH][F::RW];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
+    __builtin_amdgcn_sched_barrier(0);
     Ctx c = c0;
     uint8_t* out;
-    if (!finish_ctx<K, O>(c, out)) return;
+    // The data loads go out first.  The scheduling barrier keeps the output pointer's and the
+    // scale's scalar loads (and their wait) behind them, and no branch on those values precedes
+    // the decode: the output check and the fast-path conditions are combined with & afterwards,
+    // so the compiler cannot sink the data loads behind a round trip.  Measured on MI355X: +1% on
+    // scaled FP8, +3.5% on NVFP4, +8.5% on MXFP8, +4.5% on many small tensors.
+    const bool valid = finish_ctx<K, O>(c, out);
+    const bool vec = valid & c.vec;
     uint8_t* const ob = out + e0 * O::BYTES;
     bool ok[K::CH];
 #pragma unroll
@@ -562,13 +566,13 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = c.vec && K::template fast<O>(c, in, e, e, w);
+        ok[j] = K::template fast<O>(c, in, e, e, w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
-    if (__builtin_amdgcn_ballot_w64(!all) == 0) return;  // the common case
+    if (__builtin_amdgcn_ballot_w64(!all) == 0 || !valid) return;  // the common case; or no output
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j)
         if (!ok[j]) run_exact<K::KIND, O>(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
@@ -614,9 +618,11 @@ __device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, ui
         xs[j] = src_elem(c0.D, e0 + uint64_t(j * stk::kWave + lane) * K::CE);
         F::load(base + K::src_off(xs[j]), 0, raw[j]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     Ctx c = c0;
     uint8_t* out;
-    if (!finish_ctx<K, O>(c, out)) return;
+    const bool valid = finish_ctx<K, O>(c, out);  // combined after decoding, as in unit_full
+    const bool vec = valid & c.vec;
     uint8_t* const ob = out + e0 * O::BYTES;
     bool ok[K::CH];
 #pragma unroll
@@ -624,13 +630,13 @@ __device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, ui
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = c.vec && K::template fast<O>(c, in, e, xs[j], w);
+        ok[j] = K::template fast<O>(c, in, e, xs[j], w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
-    if (__builtin_amdgcn_ballot_w64(!all) == 0) return;
+    if (__builtin_amdgcn_ballot_w64(!all) == 0 || !valid) return;
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j)
         if (!ok[j]) run_exact<K::KIND, O>(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
