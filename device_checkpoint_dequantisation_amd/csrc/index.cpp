@@ -644,16 +644,97 @@ std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t 
 
 }  // namespace
 
+// Work-unit order.  The kernel gives XCD x the x-th contiguous eighth of the units.  Formats carry
+// different bytes per unit (about 3 KB for fp8, 4 KB for a bf16 copy, 5 KB for NVFP4), so in file
+// order an eighth that holds, say, a whole bf16 embedding carries more bytes than the rest and
+// finishes last.  When the file-order eighths differ by more than kImbalance in bytes, every
+// output of at least kPieceMinUnits units is cut into 8 equal pieces, piece p placed in the p-th
+// eighth (slot p), and the smaller outputs fill the slots in file order, an eighth of their units
+// each: each XCD then streams through one eighth of every large tensor.  Otherwise the file order
+// is kept, since jumping between tensors costs a homogeneous checkpoint about 1% (measured on
+// MI355X; the pieces gained 4.6% on a block-FP8 checkpoint with a bf16 embedding).
+// A piece is one descriptor: unit_begin is set so that the kernel's element offset
+// (unit - unit_begin) << shift lands inside the whole output (computed modulo 2^32), and only
+// the output's last piece ends in its partial unit.
+constexpr uint64_t kPieceMinUnits = 2048;
+constexpr uint32_t kSlots = 8;
+constexpr double kImbalance = 1.05;
+
+// Bytes of the heaviest file-order eighth over the mean (1 when balanced).
+double eighth_imbalance(const st_index& ix, const uint32_t* sel, size_t k, const std::vector<uint64_t>& nu,
+                        uint64_t total) {
+    if (total < kSlots) return 1.0;
+    double eighth[kSlots] = {0};
+    uint64_t pos = 0;
+    double sum = 0;
+    for (size_t j = 0; j < k; ++j) {
+        if (!nu[j]) continue;
+        const Output& o = ix.outputs[sel[j]];
+        double bytes = double(o.numel) * double(sti::out_bytes(ix)) +
+                       double(ix.tensors[o.tensor].end - ix.tensors[o.tensor].begin);
+        if (o.scale >= 0) bytes += double(ix.tensors[size_t(o.scale)].end - ix.tensors[size_t(o.scale)].begin);
+        const double per_unit = bytes / double(nu[j]);
+        sum += bytes;
+        uint64_t u = pos, end = pos + nu[j];
+        while (u < end) {  // spread the output over the eighths its units fall in
+            const uint32_t x = uint32_t(std::min<uint64_t>(kSlots - 1, u * kSlots / total));
+            const uint64_t xe = x + 1 == kSlots ? end : std::min<uint64_t>(end, (uint64_t(x) + 1) * total / kSlots);
+            const uint64_t stop = std::max<uint64_t>(xe, u + 1);
+            eighth[x] += per_unit * double(stop - u);
+            u = stop;
+        }
+        pos = end;
+    }
+    double mx = 0;
+    for (double e : eighth) mx = std::max(mx, e);
+    return sum > 0 ? mx / (sum / kSlots) : 1.0;
+}
+
 std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* sel, size_t k, uint64_t* units_out,
                                             const uint64_t* at) {
-    std::vector<st_desc> descs(k);
-    uint64_t pos = 0;
+    std::vector<st_desc> whole(k);
+    std::vector<uint64_t> nu(k);
+    uint64_t total = 0;
     for (size_t j = 0; j < k; ++j) {
-        uint64_t units = 0;
-        descs[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), pos, &units, at);
-        pos += units;
-        if (pos >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
+        whole[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), 0, &nu[j], at);
+        total += nu[j];
+        if (total >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
     }
+    const bool cut = eighth_imbalance(ix, sel, k, nu, total) > kImbalance;
+    uint64_t small = 0;  // units of the outputs that are not cut
+    for (size_t j = 0; j < k; ++j)
+        if (!(cut && nu[j] >= kPieceMinUnits)) small += nu[j];
+    struct Piece {
+        size_t j;
+        uint64_t first, count;
+    };
+    std::vector<std::vector<Piece>> slot(kSlots);
+    uint64_t filled = 0;  // units of small outputs placed so far
+    for (size_t j = 0; j < k; ++j) {
+        if (cut && nu[j] >= kPieceMinUnits) {
+            for (uint32_t p = 0; p < kSlots; ++p) {
+                const uint64_t a = nu[j] * p / kSlots, e = nu[j] * (p + 1) / kSlots;
+                slot[p].push_back({j, a, e - a});
+            }
+        } else {
+            const uint64_t s = small ? std::min<uint64_t>(kSlots - 1, filled * kSlots / small) : 0;
+            slot[s].push_back({j, 0, nu[j]});
+            filled += nu[j];
+        }
+    }
+    std::vector<st_desc> descs;
+    descs.reserve(k + 8 * k);
+    uint64_t pos = 0;
+    for (const auto& sl : slot)
+        for (const Piece& pc : sl) {
+            st_desc d = whole[pc.j];
+            const uint32_t shift = (d.meta >> 8) & 0xFFu;
+            d.unit_begin = uint32_t(pos - pc.first);  // modulo 2^32, as the kernel subtracts
+            d.unit_end = uint32_t(pos + pc.count);
+            if (pc.first + pc.count != nu[pc.j]) d.tail = uint32_t(1) << shift;  // not the output's last unit
+            descs.push_back(d);
+            pos += pc.count;
+        }
     *units_out = pos;
     return assemble(descs, pos, ix.out_dtype);
 }

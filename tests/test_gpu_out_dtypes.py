@@ -11,7 +11,7 @@ import oracle
 import synth
 import device_checkpoint_dequantisation_amd as st
 from tests.test_gpu_parity import (block_fp8_file, float_every_code_file, fp8_every_code_file, mx_every_code_file,
-                                   nvfp4_every_code_file)
+                                   nvfp4_every_code_file, pieces_file)
 from tests.test_gpu_slices import _slices_for, _view
 from tests.st_files import make_file
 
@@ -216,3 +216,8 @@ def test_f16_rounding_every_class_both_paths(shift):
     st.materialize(ck.blob, ck.table, ck.units, ptrs, out_dtype="f16")
     torch.cuda.synchronize()
     _assert_equal(("f16 rounding", shift), _bits(arena[shift: shift + o.numel]), want)
+
+
+@pytest.mark.parametrize("out_dtype", TYPES)
+def test_large_outputs_cut_into_pieces(out_dtype):
+    assert_parity(pieces_file(), out_dtype)

@@ -235,3 +235,27 @@ def test_staging_from_file_matches_bytes(tmp_path):
         out = st.load(str(p), DEV, streamed=streamed)
         for name, w in want.items():
             assert np.array_equal(out[name].view(torch.int16).cpu().numpy().view(np.uint16), w), (streamed, name)
+
+
+def pieces_file():
+    """Outputs of at least 2048 units, which the planner cuts into 8 pieces, between small ones and
+    at odd byte offsets: bf16 (2049 units, the last partial), scaled FP8 (3001 units) and NVFP4
+    (2080 units of 2048 elements)."""
+    rng = np.random.default_rng(9)
+    nb, nf = 2048 * 1024 + 5, 3000 * 1024 + 77
+    M, K = 1024, 4160
+    tensors = list(_pad(3))
+    tensors += [("a", "BF16", (nb,), rng.integers(0, 2 ** 16, nb, dtype=np.uint64).astype(np.uint16))]
+    tensors += [(f"s{i}", "F16", (100 + 7 * i,), rng.standard_normal(100 + 7 * i).astype(np.float16)) for i in range(9)]
+    tensors += [("q.weight", "F8_E4M3", (nf,), rng.integers(0, 256, nf, dtype=np.uint64).astype(np.uint8)),
+                ("q.scale_weight", "F32", (), f32_bytes(0.013))]
+    tensors += [("n.weight", "U8", (M, K // 2), rng.integers(0, 256, M * K // 2, dtype=np.uint64).astype(np.uint8)),
+                ("n.weight_scale", "F8_E4M3", (M, K // 16), np.full(M * K // 16, 0x38, np.uint8)),
+                ("n.weight_scale_2", "F32", (), f32_bytes(0.25))]
+    return make_file(tensors)
+
+
+def test_large_outputs_cut_into_pieces():
+    ck = assert_parity(pieces_file())
+    h = np.frombuffer(ck.table.cpu().numpy().tobytes()[:64], dtype=np.uint32)
+    assert ck.units > 7000 and h[1] > len(ck.tensors)   # n_desc: the large outputs were cut

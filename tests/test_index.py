@@ -81,17 +81,39 @@ def _table(raw: bytes):
 
 
 def _check_map(d, m, units, numels):
-    # every group of 4 units maps to the descriptor holding its first unit
+    """Table invariants: descriptors cover consecutive ranges of the unit sequence; each output's
+    pieces (one descriptor each, or one for the whole output) cover its units exactly once, and
+    the kernel's element offset (unit - unit_begin) << shift (modulo 2^32) lands on the right
+    units; only the piece holding an output's last unit ends in its partial tail; every group of 4
+    units maps to the descriptor holding its first unit."""
     numels = np.asarray(numels, dtype=np.int64)
-    ends = d["unit_begin"].astype(np.int64) + (-(-numels // (1 << d["unit_shift"].astype(np.int64))))
-    assert np.array_equal(ends, d["unit_end"].astype(np.int64))
-    for row, n in zip(d, numels):   # the last unit's length
-        n, sh = int(n), int(row["unit_shift"])
-        if n:
-            assert row["tail"] == n - ((-(-n // (1 << sh)) - 1) << sh) and 1 <= row["tail"] <= 1 << sh
+    ends = d["unit_end"].astype(np.int64)
+    starts = np.concatenate([[0], ends[:-1]])
+    assert np.all(ends >= starts)
+    covered = {}
+    for i, row in enumerate(d):
+        sh, out = int(row["unit_shift"]), int(row["out"])
+        n = int(numels[out])
+        nu = -(-n // (1 << sh))
+        first = (int(starts[i]) - int(row["unit_begin"])) % (1 << 32)
+        count = int(ends[i] - starts[i])
+        assert first + count <= nu, (i, first, count, nu)
+        covered.setdefault(out, []).append((first, count))
+        if count:
+            last = first + count == nu
+            want_tail = n - ((nu - 1) << sh) if last else 1 << sh
+            assert row["tail"] == want_tail and 1 <= row["tail"] <= 1 << sh, (i, int(row["tail"]), want_tail)
+    for out, parts in covered.items():
+        parts.sort()
+        pos = 0
+        for first, count in parts:
+            assert first == pos, (out, parts)
+            pos += count
+        n = int(numels[out])
+        assert pos == -(-n // (1 << int(d[[int(r["out"]) for r in d].index(out)]["unit_shift"])))
     for g, di in enumerate(m):
         u = g * _lib.UNITS_PER_GROUP
-        assert d[di]["unit_begin"] <= u < ends[di], (g, di)
+        assert starts[di] <= u < ends[di], (g, di)
     assert ends.max(initial=0) == units
 
 
@@ -314,3 +336,52 @@ def test_mx_rejections_match_the_oracle():
                     oracle.plan(buf)
                 with pytest.raises(st.StError):
                     _index(buf)
+
+
+def test_large_outputs_are_cut_into_eight_pieces():
+    """When the file-order eighths of the unit sequence carry unequal bytes (here a bf16 copy at
+    4 KB per unit, then fp8 at 3 KB), outputs of at least 2048 units are cut into 8 equal pieces,
+    piece p in the p-th eighth; small outputs fill the eighths in file order."""
+    rng = np.random.default_rng(2)
+    big_bf16 = 2048 * 1024 + 5              # 2049 units, the last one partial
+    big_fp8 = 3000 * 1024                   # 3000 units
+    tensors = [("a", "BF16", (big_bf16,), rng.integers(0, 2 ** 16, big_bf16, dtype=np.uint64).astype(np.uint16))]
+    tensors += [(f"s{i}", "F32", (3000 + i,), rng.standard_normal(3000 + i).astype(np.float32)) for i in range(20)]
+    tensors += [("q.weight", "F8_E4M3", (big_fp8,), np.full(big_fp8, 0x38, np.uint8)),
+                ("q.scale_weight", "F32", (), f32_bytes(0.5))]
+    buf = make_file(tensors)
+    ix = _index(buf)
+    raw, units = ix.table()
+    h, d, m = _table(raw)
+    outs = ix.outputs()
+    _check_map(d, m, units, [o.numel for o in outs])
+    kk = {o.name: k for k, o in enumerate(outs)}
+    for name in ("a", "q.weight"):
+        rows = [i for i, r in enumerate(d) if r["out"] == kk[name]]
+        assert len(rows) == 8
+        ends = d["unit_end"].astype(np.int64)
+        starts = np.concatenate([[0], ends[:-1]])
+        for p, i in enumerate(rows):          # piece p sits in eighth p of the sequence
+            assert p * units // 8 - 64 <= starts[i] <= (p + 1) * units // 8, (name, p, starts[i], units)
+    small = [i for i, r in enumerate(d) if outs[int(r["out"])].name.startswith("s")]
+    assert [outs[int(d[i]["out"])].name for i in small] == [f"s{i}" for i in range(20)]   # file order kept
+    # a subset table of the two large outputs is still unbalanced, and cut; one output alone is not
+    raw, units = ix.table_subset([kk["a"], kk["q.weight"]])
+    h, d, m = _table(raw)
+    assert len(d) == 16 and units == 2049 + 3000
+    _check_map(d, m, units, [outs[kk["a"]].numel, outs[kk["q.weight"]].numel])
+    raw, units = ix.table_subset([kk["a"]])
+    h, d, m = _table(raw)
+    assert len(d) == 1 and units == 2049
+
+
+def test_balanced_checkpoints_keep_file_order():
+    # two large fp8 outputs: every eighth carries the same bytes, so nothing is cut
+    n = 3000 * 1024
+    buf = make_file([("a.weight", "F8_E4M3", (n,), np.full(n, 0x38, np.uint8)), ("a.scale_weight", "F32", (), f32_bytes(1.0)),
+                     ("b.weight", "F8_E4M3", (n,), np.full(n, 0x38, np.uint8)), ("b.scale_weight", "F32", (), f32_bytes(1.0))])
+    ix = _index(buf)
+    raw, units = ix.table()
+    h, d, m = _table(raw)
+    assert len(d) == 2 and list(d["unit_begin"]) == [0, 3000]
+    _check_map(d, m, units, [o.numel for o in ix.outputs()])
