@@ -449,8 +449,9 @@ struct KMx4 : Geom<ST_KIND_MXFP4> {
 
 static_assert(KPass::IB == 16 && KF32::IB == 32 && KFp8Tensor::IB == 8 && KFp4::IB == 4 && KMx8::IB == 8 &&
                   KMx4::IB == 4, "chunk geometry");
-static_assert(KPass::CH == 2 && KF32::CH == 1 && KFp8Tensor::CH == 2 && KFp4::CH == 4 && KMx8::CH == 2 &&
-                  KMx4::CH == 4, "chunks per lane");
+static_assert(KPass::CH == stk::kWordsPass && KF32::CH == stk::kWordsF32 && KFp8Tensor::CH == stk::kWordsFp8 &&
+                  KFp4::CH == stk::kWordsFp4 && KMx8::CH == stk::kWordsFp8 && KMx4::CH == stk::kWordsFp4,
+              "one 8-element chunk per output word of the unit");
 
 // ------------------------------------------------------------------------- loads
 
