@@ -294,115 +294,128 @@ struct Ctx {
     bool vec;        // the output is 16-byte aligned (vector stores)
 };
 
-// CE, IB, LG from the kind's geometry (shared with the host planner); CH chunks per lane in a
-// unit of the default size.
-template <uint32_t KIND_>
+// Chunk geometry of kind KIND_ for output type O.  A chunk is one 16-byte output word: 8 elements
+// of a 2-byte type, or 4 elements of fp32, so that a store instruction of a wavefront covers
+// contiguous output for every output type (measured on MI355X: lanes storing two adjacent fp32
+// words lose about 20%).  Packed fp4 keeps 8-element chunks for fp32 too (4-byte loads).  IB
+// source bytes per chunk, loaded as naturally aligned LG-byte words (IB, at most 16); N = IB / 4
+// dwords; CH chunks per lane in a unit of the default size.  For 2-byte outputs CE and LG are the
+// host planner's chunk_elems and load_word_bytes, whose column-slice rules are therefore also
+// sufficient for the 4-element fp32 chunks.
+template <uint32_t KIND_, class O>
 struct Geom {
-    static constexpr uint32_t KIND = KIND_, CE = stk::chunk_elems(KIND_), LG = stk::load_word_bytes(KIND_),
-                              IB = CE * stk::source_bits(KIND_) / 8,
+    static constexpr bool FP4 = KIND_ == ST_KIND_NVFP4 || KIND_ == ST_KIND_MXFP4;
+    static constexpr uint32_t KIND = KIND_, CE = (O::BYTES == 4 && !FP4) ? 4 : 8,
+                              IB = CE * stk::source_bits(KIND_) / 8, LG = IB < 16 ? IB : 16, N = IB / 4,
                               CH = stk::words_per_lane(KIND_) * stk::kWordElems / CE;
+    static_assert(O::BYTES == 4 || (CE == stk::chunk_elems(KIND_) && LG == stk::load_word_bytes(KIND_)),
+                  "2-byte outputs use the host planner's geometry");
 };
 
-struct KPass : Geom<ST_KIND_PASS_BF16> {
+template <class O>
+struct KPass : Geom<ST_KIND_PASS_BF16, O> {
+    using G = Geom<ST_KIND_PASS_BF16, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
         if constexpr (O::CODE == ST_OUT_BF16) {  // the bits themselves
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[k] = in[k];
+            for (uint32_t k = 0; k < G::N; ++k) w[k] = in[k];
             return true;
         } else {
             bool nan = false;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) nan |= (in[k] & 0x7FFFu) > 0x7F80u || (in[k] & 0x7FFF0000u) > 0x7F800000u;
-            if (nan) return false;
+            for (uint32_t k = 0; k < G::N; ++k)
+                nan |= (in[k] & 0x7FFFu) > 0x7F80u || (in[k] & 0x7FFF0000u) > 0x7F800000u;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) put2<O>(w, k, as_f32(in[k] << 16), as_f32(in[k] & 0xFFFF0000u));
-            return true;
+            for (uint32_t k = 0; k < G::N; ++k) put2<O>(w, k, as_f32(in[k] << 16), as_f32(in[k] & 0xFFFF0000u));
+            return !nan;
         }
     }
 };
 
-struct KF16 : Geom<ST_KIND_CAST_F16> {
+template <class O>
+struct KF16 : Geom<ST_KIND_CAST_F16, O> {
+    using G = Geom<ST_KIND_CAST_F16, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
         bool nan = false;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) nan |= (in[k] & 0x7FFFu) > 0x7C00u || (in[k] & 0x7FFF0000u) > 0x7C000000u;
-        if (nan) return false;
+        for (uint32_t k = 0; k < G::N; ++k) nan |= (in[k] & 0x7FFFu) > 0x7C00u || (in[k] & 0x7FFF0000u) > 0x7C000000u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (uint32_t k = 0; k < G::N; ++k) {
             if constexpr (O::CODE == ST_OUT_F16) w[k] = in[k];  // fp16 to fp16: the value is exact
             else put2<O>(w, k, h2f(in[k] & 0xFFFFu), h2f(in[k] >> 16));
         }
-        return true;
+        return !nan;
     }
 };
 
-struct KF32 : Geom<ST_KIND_CAST_F32> {
+template <class O>
+struct KF32 : Geom<ST_KIND_CAST_F32, O> {
+    using G = Geom<ST_KIND_CAST_F32, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 4; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
         bool nan = false;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) nan |= (in[k] & 0x7FFFFFFFu) > 0x7F800000u;
-        if (nan) return false;
+        for (uint32_t k = 0; k < G::N; ++k) nan |= (in[k] & 0x7FFFFFFFu) > 0x7F800000u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) put2<O>(w, k, as_f32(in[2 * k]), as_f32(in[2 * k + 1]));
-        return true;
+        for (uint32_t k = 0; k < G::N / 2; ++k) put2<O>(w, k, as_f32(in[2 * k]), as_f32(in[2 * k + 1]));
+        return !nan;
     }
 };
 
-// 8 e4m3 codes times s -> output words; exact path if any code is NaN or s is not finite (so no
+// 4N e4m3 codes times s -> output words; exact path if any code is NaN or s is not finite (so no
 // product is NaN)
-template <class O>
+template <class O, uint32_t N>
 __device__ __forceinline__ bool fp8_chunk(const uint32_t* in, float s, uint32_t* w) {
-    const uint32_t t = ((in[0] & 0x7F7F7F7Fu) + 0x01010101u) | ((in[1] & 0x7F7F7F7Fu) + 0x01010101u);
-    if ((t & 0x80808080u) != 0 || !finite(s)) return false;
+    uint32_t t = 0;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (uint32_t k = 0; k < N; ++k) t |= (in[k] & 0x7F7F7F7Fu) + 0x01010101u;
+#pragma unroll
+    for (uint32_t k = 0; k < N; ++k) {
         const f32x2 a = fp8x2<false>(in[k]), b = fp8x2<true>(in[k]);
         put2<O>(w, 2 * k, a.x * s, a.y * s);
         put2<O>(w, 2 * k + 1, b.x * s, b.y * s);
     }
-    return true;
+    return ((t & 0x80808080u) == 0) & finite(s);
 }
 
-struct KFp8Tensor : Geom<ST_KIND_FP8_TENSOR> {
+template <class O>
+struct KFp8Tensor : Geom<ST_KIND_FP8_TENSOR, O> {
+    using G = Geom<ST_KIND_FP8_TENSOR, O>;
     static constexpr int SCALE = 1;  // D.scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
-        return fp8_chunk<O>(in, c.s, w);
+        return fp8_chunk<O, G::N>(in, c.s, w);
     }
 };
 
-struct KFp8Block : Geom<ST_KIND_FP8_BLOCK128> {
+template <class O>
+struct KFp8Block : Geom<ST_KIND_FP8_BLOCK128, O> {
+    using G = Geom<ST_KIND_FP8_BLOCK128, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
     // e: first output element of the chunk (a multiple of CE); with cols % CE == 0 the chunk lies
     // in one row and one 128-column block, otherwise it takes the exact path.
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, uint64_t, uint32_t* w) {
-        if ((c.D.cols & (CE - 1)) != 0) return false;
+        if ((c.D.cols & (G::CE - 1)) != 0) return false;
         const uint32_t e32 = uint32_t(e);
         const uint32_t row = stk::div_apply(e32, c.D.div_magic, c.D.div_shift);
         const uint32_t col = e32 - row * c.D.cols;
         const float S = ld_f32(c.blob + c.D.scale + 4ull * ((row >> 7) * c.D.grid_cols + (col >> 7)), c.scale_al);
-        return fp8_chunk<O>(in, S, w);
+        return fp8_chunk<O, G::N>(in, S, w);
     }
 };
 
-struct KFp4 : Geom<ST_KIND_NVFP4> {
+template <class O>
+struct KFp4 : Geom<ST_KIND_NVFP4, O> {
     static constexpr int SCALE = 2;  // D.scale2
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
     // 8 elements from source element xs: (e2m1 * block scale) is exact in fp32, then one RNE
     // multiply by g
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 4));  // block scale of these 8 elements
         const float bs = fp8x2<false>(code).x;
@@ -417,23 +430,24 @@ struct KFp4 : Geom<ST_KIND_NVFP4> {
     }
 };
 
-// OCP Microscaling: 8 elements from source element xs (a multiple of 8) share the E8M0 scale of
-// their 32-element block, applied by one RNE multiply; an NaN scale or element code takes the
-// exact path.
-struct KMx8 : Geom<ST_KIND_MXFP8> {
+// OCP Microscaling: the chunk's elements from source element xs (a multiple of the chunk size)
+// share the E8M0 scale of their 32-element block, applied by one RNE multiply; an NaN scale or
+// element code takes the exact path.
+template <class O>
+struct KMx8 : Geom<ST_KIND_MXFP8, O> {
+    using G = Geom<ST_KIND_MXFP8, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
-        return fp8_chunk<O>(in, e8m0_exact(code), w);  // a NaN scale code fails its finite check
+        return fp8_chunk<O, G::N>(in, e8m0_exact(code), w);  // a NaN scale code fails its finite check
     }
 };
 
-struct KMx4 : Geom<ST_KIND_MXFP4> {
+template <class O>
+struct KMx4 : Geom<ST_KIND_MXFP4, O> {
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
-    template <class O>
     static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
         const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
         const float S = e8m0_exact(code);
@@ -447,11 +461,12 @@ struct KMx4 : Geom<ST_KIND_MXFP4> {
     }
 };
 
-static_assert(KPass::IB == 16 && KF32::IB == 32 && KFp8Tensor::IB == 8 && KFp4::IB == 4 && KMx8::IB == 8 &&
-                  KMx4::IB == 4, "chunk geometry");
-static_assert(KPass::CH == stk::kWordsPass && KF32::CH == stk::kWordsF32 && KFp8Tensor::CH == stk::kWordsFp8 &&
-                  KFp4::CH == stk::kWordsFp4 && KMx8::CH == stk::kWordsFp8 && KMx4::CH == stk::kWordsFp4,
-              "one 8-element chunk per output word of the unit");
+static_assert(KPass<OutBf16>::IB == 16 && KF32<OutBf16>::IB == 32 && KFp8Tensor<OutBf16>::IB == 8 &&
+                  KFp4<OutBf16>::IB == 4 && KMx8<OutBf16>::IB == 8 && KMx4<OutBf16>::IB == 4,
+              "chunk geometry, 2-byte outputs");
+static_assert(KPass<OutF32>::IB == 8 && KF32<OutF32>::IB == 16 && KFp8Tensor<OutF32>::IB == 4 &&
+                  KFp4<OutF32>::IB == 4 && KFp8Tensor<OutF32>::CH == 2 * stk::kWordsFp8,
+              "chunk geometry, fp32 outputs");
 
 // ------------------------------------------------------------------------- loads
 
@@ -567,7 +582,7 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = K::template fast<O>(c, in, e, e, w) & vec;
+        ok[j] = K::fast(c, in, e, e, w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
@@ -595,7 +610,7 @@ __device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cn
         F::load(base, ci, raw);
         F::align(raw, sh, in);
         const uint64_t e = e0 + uint64_t(ci) * K::CE;
-        if (c.vec && K::template fast<O>(c, in, e, e, w)) store_chunk<K, O>(ob, ci, w);
+        if (c.vec && K::fast(c, in, e, e, w)) store_chunk<K, O>(ob, ci, w);
         else run_exact<K::KIND, O>(c, out, e, K::CE);
     }
 #pragma unroll 1
@@ -631,7 +646,7 @@ __device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, ui
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = K::template fast<O>(c, in, e, xs[j], w) & vec;
+        ok[j] = K::fast(c, in, e, xs[j], w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
@@ -661,7 +676,7 @@ __device__ __forceinline__ void unit_strided_any(const Ctx& c0, uint64_t e0, uin
         uint32_t raw[F::RW], in[F::N], w[NW];
         F::load(base + K::src_off(x), 0, raw);
         F::align(raw, sh, in);
-        if (c.vec && K::template fast<O>(c, in, e, x, w)) store_chunk<K, O>(ob, ci, w);
+        if (c.vec && K::fast(c, in, e, x, w)) store_chunk<K, O>(ob, ci, w);
         else run_exact<K::KIND, O>(c, out, e, K::CE);
     }
 #pragma unroll 1
@@ -753,26 +768,26 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
             return;
         }
         switch (D.kind) {
-            case ST_KIND_FP8_TENSOR: run_strided<KFp8Tensor, O>(c, e0, cnt, lane); break;
-            case ST_KIND_FP8_BLOCK128: run_strided<KFp8Block, O>(c, e0, cnt, lane); break;
-            case ST_KIND_NVFP4: run_strided<KFp4, O>(c, e0, cnt, lane); break;
-            case ST_KIND_PASS_BF16: run_strided<KPass, O>(c, e0, cnt, lane); break;
-            case ST_KIND_CAST_F16: run_strided<KF16, O>(c, e0, cnt, lane); break;
-            case ST_KIND_MXFP8: run_strided<KMx8, O>(c, e0, cnt, lane); break;
-            case ST_KIND_MXFP4: run_strided<KMx4, O>(c, e0, cnt, lane); break;
-            default: run_strided<KF32, O>(c, e0, cnt, lane); break;
+            case ST_KIND_FP8_TENSOR: run_strided<KFp8Tensor<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_FP8_BLOCK128: run_strided<KFp8Block<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_NVFP4: run_strided<KFp4<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_PASS_BF16: run_strided<KPass<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_CAST_F16: run_strided<KF16<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_MXFP8: run_strided<KMx8<O>, O>(c, e0, cnt, lane); break;
+            case ST_KIND_MXFP4: run_strided<KMx4<O>, O>(c, e0, cnt, lane); break;
+            default: run_strided<KF32<O>, O>(c, e0, cnt, lane); break;
         }
         return;
     }
     switch (D.kind) {
-        case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor, O>(c, e0, cnt, lane); break;
-        case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block, O>(c, e0, cnt, lane); break;
-        case ST_KIND_NVFP4: run_unit<KFp4, O>(c, e0, cnt, lane); break;
-        case ST_KIND_PASS_BF16: run_unit<KPass, O>(c, e0, cnt, lane); break;
-        case ST_KIND_CAST_F16: run_unit<KF16, O>(c, e0, cnt, lane); break;
-        case ST_KIND_MXFP8: run_unit<KMx8, O>(c, e0, cnt, lane); break;
-        case ST_KIND_MXFP4: run_unit<KMx4, O>(c, e0, cnt, lane); break;
-        default: run_unit<KF32, O>(c, e0, cnt, lane); break;
+        case ST_KIND_FP8_TENSOR: run_unit<KFp8Tensor<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_FP8_BLOCK128: run_unit<KFp8Block<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_NVFP4: run_unit<KFp4<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_PASS_BF16: run_unit<KPass<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_CAST_F16: run_unit<KF16<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_MXFP8: run_unit<KMx8<O>, O>(c, e0, cnt, lane); break;
+        case ST_KIND_MXFP4: run_unit<KMx4<O>, O>(c, e0, cnt, lane); break;
+        default: run_unit<KF32<O>, O>(c, e0, cnt, lane); break;
     }
 }
 
