@@ -385,3 +385,35 @@ def test_balanced_checkpoints_keep_file_order():
     h, d, m = _table(raw)
     assert len(d) == 2 and list(d["unit_begin"]) == [0, 3000]
     _check_map(d, m, units, [o.numel for o in ix.outputs()])
+
+
+def test_launch_arguments_are_checked_before_any_gpu_call():
+    """st_materialize_as (and its bf16 forms) and st_stage_file reject bad arguments with ST_E_ARG
+    and a message, before touching the GPU: fake, well-aligned device addresses stand in."""
+    import ctypes as C
+    L = _lib.lib()
+    ok = C.c_void_p(1 << 20)        # 256-byte aligned stand-ins; never dereferenced on these paths
+    cases = [
+        ((None, ok, 5, ok, 0, 0), "null pointer"),
+        ((ok, None, 5, ok, 0, 0), "null pointer"),
+        ((ok, ok, 5, None, 0, 0), "null pointer"),
+        ((C.c_void_p((1 << 20) + 16), ok, 5, ok, 0, 0), "blob is not 256-byte aligned"),
+        ((ok, C.c_void_p((1 << 20) + 32), 5, ok, 0, 0), "work table is not 64-byte aligned"),
+        ((ok, ok, 1 << 32, ok, 0, 0), "at most 2^32 - 1"),
+        ((ok, ok, 5, ok, 3, 0), "unknown output type 3"),
+        ((ok, ok, 5, ok, 0, 2), "unknown flags 0x2"),
+    ]
+    for (blob, descs, n, outs, dt, flags), msg in cases:
+        assert L.st_materialize_as(blob, descs, n, outs, dt, flags, None) == -1, msg
+        assert msg.encode() in L.st_last_error(), (msg, L.st_last_error())
+    # n == 0 is a no-op, whatever the pointers
+    assert L.st_materialize_as(None, None, 0, None, 7, 9, None) == 0
+    assert L.st_materialize(None, None, 0, None, None) == 0
+    assert L.st_materialize(ok, None, 1, ok, None) == -1 and L.st_materialize_slices(None, ok, 1, ok, None) == -1
+    ix = _index(synth.config_bytes(1))
+    assert L.st_stage_file(b"/nonexistent", ix._h, None, ok, 1 << 30, None, None, None) == -1
+    assert b"null pointer" in L.st_last_error()
+    assert L.st_stage_file(b"/nonexistent", ix._h, ok, ok, 1024, None, None, None) == -1
+    assert b"pinned buffer" in L.st_last_error()
+    assert L.st_stage_file(b"/nonexistent", ix._h, C.c_void_p((1 << 20) + 8), ok, 1 << 30, None, None, None) == -1
+    assert b"blob is not" in L.st_last_error()
