@@ -14,31 +14,33 @@
 // element, a handful of VALU operations per element), so there is no matrix-core work; what
 // matters on gfx950 is how the HBM traffic is issued:
 //  * One wavefront per work unit, one-shot.  A unit is 512-2048 elements of one output (about
-//    1-2 KB read, 1-4 KB written).  Each wavefront loads its unit, decodes, stores and exits.
+//    1-2 KB read, 1-4 KB written; measured best against half and double sizes).  Each wavefront loads its unit, decodes, stores and exits.
 //    Measured on MI355X, one-shot wavefronts sustain ~20% more read+write bandwidth than any
 //    persistent loop tried (grid-stride, contiguous ranges, software-pipelined), because a
 //    persistent wavefront's next loads wait behind its own outstanding stores (vmcnt counts both).
-//  * Lane-contiguous chunks.  A chunk is 8 elements: one 16-byte output word for 2-byte output
-//    types, two adjacent words for fp32.  Chunk j*64 + l of a unit belongs to lane l, so a store
-//    instruction of a wavefront covers 1 KB of contiguous output (2 KB as two stores for fp32) and
+//  * Lane-contiguous chunks.  A chunk is one 16-byte output word: 8 elements of a 2-byte output
+//    type, 4 of fp32 (packed fp4 keeps 8, two adjacent fp32 words).  Chunk j*64 + l of a unit
+//    belongs to lane l, so a store instruction of a wavefront covers 1 KB of contiguous output and
 //    a load instruction a contiguous run of the source; lanes read whatever input bytes their
-//    chunk needs (4, 8, 16 or 32 bytes).  Measured on MI355X, lanes that each store four adjacent
-//    words (64-byte stride across a store instruction) reach about 30% less bandwidth.
+//    chunk needs (4, 8 or 16 bytes; 32 for fp32 sources to 2-byte outputs).  Measured on MI355X,
+//    lanes that each store two adjacent words lose about 20%, four adjacent words about 30%.
 //  * XCD-contiguous order.  The hardware hands workgroup b to XCD b mod 8; workgroups are
-//    renumbered so each XCD streams through one contiguous eighth of the work.
+//    renumbered so each XCD streams through one contiguous eighth of the work (the host planner
+//    balances the eighths' bytes when formats of different bytes per unit mix).
 //  * Tiny tensors.  Units are numbered consecutively across outputs and a workgroup's four
 //    wavefronts take four consecutive units, whatever output they belong to, so small tensors are
 //    packed at wavefront granularity.  A per-workgroup map gives the descriptor of the group's
 //    first unit; a wavefront walks forward at most three descriptors.
 //  * Unaligned sources.  A tensor may start at any byte.  A unit whose source is aligned to its
-//    chunk's load word (16 bytes; 8 for FP8, 4 for NVFP4) loads whole words.  Otherwise each lane
+//    chunk's load word (the chunk's source bytes, at most 16) loads whole words.  Otherwise each lane
 //    loads from the 4-byte boundary at or below its bytes (16-byte words at 4-byte alignment and
 //    one load of the remaining dwords, one more dword than the chunk needs), and the byte offset
 //    sh (the same for every lane of a unit) is removed in registers with v_alignbyte.  Measured
 //    on MI355X, this beats loading the two enclosing aligned words and selecting among them.
 //  * Short dependency chain.  Ahead of a wavefront's data loads sit only the table header check,
 //    its map entry and its descriptor; the output pointer and the scalar scale are loaded once the
-//    data loads are in flight (a wait for one scalar load waits for all of them).
+//    data loads are in flight (a wait for one scalar load waits for all of them), and no branch
+//    on those values or on a block scale precedes the decode (see unit_full).
 //  * Decoding uses gfx950's conversion instructions (fp8 and fp4 to fp32, fp32 to bf16 and to
 //    fp16), each checked exhaustively against the exact decoding on the device; one fp32 multiply
 //    per scale.

@@ -10,14 +10,16 @@ static_assert(sizeof(st_desc) == 64, "st_desc must stay 64 bytes");
 // Records a printf-style message for st_last_error() on this thread and returns `code`.
 st_status st_fail(st_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// Work-unit geometry.  Every lane of a wavefront writes whole 16-byte output words (8 bf16
-// elements); output word o*64 + lane of a unit belongs to lane `lane`, so each store instruction
-// of the wavefront covers 1 KB of contiguous output.  kWords = output words per lane per unit:
-//   bf16/fp16 : 2 words -> 1024 elements (2 KB in, 2 KB out)
-//   fp32      : 1 word  ->  512 elements (2 KB in, 1 KB out)
-//   fp8       : 2 words -> 1024 elements (1 KB in, 2 KB out)
-//   nvfp4     : 4 words -> 2048 elements (1 KB + 128 B in, 4 KB out)
-// so every unit reads about 1-2 KB and writes 1-4 KB: one short, fully coalesced burst per wave.
+// Work-unit geometry, in elements per unit, for every output type.  kWords = 16-byte output words
+// per lane per unit for a 2-byte output type (8 elements each); output word o*64 + lane of a unit
+// belongs to lane `lane`, so each store instruction of the wavefront covers 1 KB of contiguous
+// output (fp32 outputs: twice the words, 4 elements each):
+//   bf16/fp16 sources : 2 words -> 1024 elements (2 KB in, 2 KB out)
+//   fp32 sources      : 1 word  ->  512 elements (2 KB in, 1 KB out)
+//   fp8 (all scalings): 2 words -> 1024 elements (1 KB in, 2 KB out)
+//   nvfp4 / mxfp4     : 4 words -> 2048 elements (1 KB + 64-128 B in, 4 KB out)
+// so every unit reads about 1-2 KB and writes 1-4 KB (2-8 KB for fp32 outputs): one short, fully
+// coalesced burst per wave.
 namespace stk {
 constexpr uint32_t kWave = 64;
 constexpr uint32_t kWordElems = 8;
