@@ -1,4 +1,4 @@
-"""stmat: materialise safetensors checkpoint weights as bf16 tensors on an MI355X.
+"""stmat: materialise safetensors checkpoint weights as bf16 (or fp16 / fp32) tensors on an MI355X.
 
 Python binding of libstmat.so (include/stmat.h).  It only marshals arguments: the header index,
 the descriptor plan, staging and the decode all run in the library; torch provides device
@@ -396,7 +396,8 @@ def _quantized(index: SafeTensorIndex, blob, k: int, at, copy: bool) -> Quantize
 
 
 class DeviceCheckpoint:
-    """A checkpoint staged on one GPU: the blob, the descriptor table and a bf16 output arena in
+    """A checkpoint staged on one GPU: the blob, the descriptor table and an output arena (of the
+    index's output type) in
     which every output starts on a 256-byte boundary."""
 
     def __init__(self, index: SafeTensorIndex, path: str | None = None, device="cuda", pinned_mb: int = 256,
@@ -489,7 +490,7 @@ class DeviceCheckpoint:
         return {n: _quantized(self.index, self.blob, pos[n], lambda i: ents[i].begin, copy) for n in want}
 
     def materialize_slices(self, slices, stream=None, strided_kernel: bool | None = None) -> list:
-        """bf16 tensors [rows, cols] for slices of outputs (see SafeTensorIndex.table_slices),
+        """Tensors [rows, cols] of the output type for slices of outputs (see SafeTensorIndex.table_slices),
         decoded in one launch from the staged blob.  ``strided_kernel`` (default: whether any
         slice cuts columns) picks st_materialize_slices; with False, the whole-output kernel's
         exact path decodes column slices element by element."""

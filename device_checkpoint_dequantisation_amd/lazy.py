@@ -205,7 +205,8 @@ class RamCache:
 
 
 class StreamStateDict(Mapping):
-    """Mapping from output name to a bf16 tensor on ``device``, over one safetensors file.
+    """Mapping from output name to a tensor on ``device`` (bf16, or ``out_dtype`` f16 / f32), over
+    one safetensors file.
 
     ``keys()``, ``len()``, ``in`` and :meth:`meta` read nothing but the header.  Indexing decodes one
     tensor on the GPU; :meth:`load` decodes several with one read and one upload.  With
@@ -254,8 +255,8 @@ class StreamStateDict(Mapping):
 
     # ---- loading
     def load(self, names, stream=None) -> dict:
-        """Decode the outputs ``names`` into fresh bf16 tensors, enqueued on ``stream`` (default: the
-        current stream); returns ``{name: tensor}``."""
+        """Decode the outputs ``names`` into fresh tensors of the output type, enqueued on ``stream``
+        (default: the current stream); returns ``{name: tensor}``."""
         torch = _torch()
         names = list(dict.fromkeys(names))
         metas = [self._meta[n] for n in names]  # KeyError for an unknown name
