@@ -396,9 +396,8 @@ def _quantized(index: SafeTensorIndex, blob, k: int, at, copy: bool) -> Quantize
 
 
 class DeviceCheckpoint:
-    """A checkpoint staged on one GPU: the blob, the descriptor table and an output arena (of the
-    index's output type) in
-    which every output starts on a 256-byte boundary."""
+    """A checkpoint staged on one GPU: the blob, the descriptor table and an output arena of the
+    index's output type, in which every output starts on a 256-byte boundary."""
 
     def __init__(self, index: SafeTensorIndex, path: str | None = None, device="cuda", pinned_mb: int = 256,
                  check_vram: bool = True):
