@@ -214,7 +214,7 @@ class StreamStateDict(Mapping):
     memory (LRU) and later loads of them skip the file."""
 
     def __init__(self, path: str, device="cuda", ram_cache_bytes: int = 0, index: SafeTensorIndex | None = None,
-                 out_dtype: str = "bf16"):
+                 out_dtype: str = "bf16", steps_per_load: int = 8):
         self.path = path
         self.index = index if index is not None else SafeTensorIndex.open(path, out_dtype=out_dtype)
         self.device = _torch().device(device)
@@ -231,6 +231,7 @@ class StreamStateDict(Mapping):
         self._side = None   # its copy stream
         self._stage = None  # pinned buffer for small uploads
         self._stage_done = None
+        self.steps_per_load = max(1, int(steps_per_load))  # staging steps of a direct load
 
     # ---- metadata only
     def __iter__(self):
@@ -295,7 +296,7 @@ class StreamStateDict(Mapping):
         torch = _torch()
         ks = [m.index for m in metas]
         total = sum(m.source_bytes for m in metas)
-        chunk = min(64 << 20, max(1 << 20, _round_up(total // 4 + 1, 1 << 20)))
+        chunk = min(64 << 20, max(1 << 20, _round_up(total // self.steps_per_load + 1, 1 << 20)))
         plan = StreamPlan(self.index, chunk, select=ks, pack=True)
         need = 4 * plan.chunk_bytes
         if self._ring is None or self._ring.numel() < need:
