@@ -590,7 +590,7 @@ st_desc make_desc(const st_index& ix, const Output& o, uint32_t out_slot, uint64
     d.scale = o.scale >= 0 ? where(size_t(o.scale)) : 0;
     d.scale2 = o.scale2 >= 0 ? where(size_t(o.scale2)) : 0;
     d.out = out_slot;
-    const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
+    const uint32_t unit_shift = stk::step_shift(o.kind, ix.out_dtype) + ix.unit_log2_scale;
     uint32_t div_shift = 0;
     if (o.kind == ST_KIND_FP8_BLOCK128) {
         uint32_t n = uint32_t(o.shape[1]);
@@ -823,7 +823,7 @@ st_desc make_slice_desc(const st_index& ix, const Output& o, const Slice& g, uin
         if (!whole_chunks || !aligned_rows) d.flags = ST_DESC_EXACT;
     }
     const uint64_t numel = g.rows() * g.cols();
-    const uint32_t unit_shift = stk::step_shift(o.kind) + ix.unit_log2_scale;
+    const uint32_t unit_shift = stk::step_shift(o.kind, ix.out_dtype) + ix.unit_log2_scale;
     d.meta = uint32_t(o.kind) | unit_shift << 8 | div_shift << 16;
     *units = (numel + (uint64_t(1) << unit_shift) - 1) >> unit_shift;
     d.unit_begin = uint32_t(unit_begin);

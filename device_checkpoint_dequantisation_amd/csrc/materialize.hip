@@ -282,8 +282,16 @@ __device__ __forceinline__ void store_elem(uint8_t* out, uint64_t e, uint32_t bi
 // ------------------------------------------------------------------------- per-kind chunks
 //
 // A Kind decodes one chunk of CE elements from IB input bytes, fetched as naturally aligned
-// LG-byte words, into CE * O::BYTES / 4 output words.  `fast` returns false when the chunk must
+// LG-byte words, into CE * O::BYTES / 4 output words.  `sc` loads the chunk's scale word (a scale
+// code, or an fp32 scale's bits; 0 for kinds without a per-chunk scale) from the chunk's output
+// element e and source element xs; `fast` decodes with it and returns false when the chunk must
 // take the exact path.  CH = chunks per lane per unit; chunk c of a unit belongs to lane c % 64.
+// Kinds with a per-chunk scale (SC_LOAD) load it either together with the data, before the first
+// store (EARLY_SC), or just before the chunk's decode, behind a scheduling barrier so that the load
+// is issued before the decode waits for the chunk's data.  Measured on MI355X: loading early gains
+// about 1% for block FP8 into 2-byte outputs and loses 0.5-1.5% for the others (single-byte scale
+// codes that mostly hit in cache); letting the compiler place the late load after the data wait
+// cost MXFP8 3%.
 
 // Per-unit context.  `s` and `vec` are filled in by finish_ctx, after the data loads are issued;
 // whether the scale folds into the fast path is decided in the decode.
@@ -309,7 +317,12 @@ struct Geom {
     static constexpr bool FP4 = KIND_ == ST_KIND_NVFP4 || KIND_ == ST_KIND_MXFP4;
     static constexpr uint32_t KIND = KIND_, CE = (O::BYTES == 4 && !FP4) ? 4 : 8,
                               IB = CE * stk::source_bits(KIND_) / 8, LG = IB < 16 ? IB : 16, N = IB / 4,
-                              CH = stk::words_per_lane(KIND_) * stk::kWordElems / CE;
+                              CH = stk::words_per_lane(KIND_, O::CODE) * stk::kWordElems / CE;
+    // whole units of packed fp4 into fp32 take unit_full_paired
+    static constexpr bool PAIRED = FP4 && O::BYTES == 4;
+    static constexpr bool SC_LOAD = KIND_ == ST_KIND_FP8_BLOCK128 || KIND_ == ST_KIND_NVFP4 || KIND_ == ST_KIND_MXFP8 ||
+                                    KIND_ == ST_KIND_MXFP4;
+    static constexpr bool EARLY_SC = false;
     static_assert(O::BYTES == 4 || (CE == stk::chunk_elems(KIND_) && LG == stk::load_word_bytes(KIND_)),
                   "2-byte outputs use the host planner's geometry");
 };
@@ -319,7 +332,8 @@ struct KPass : Geom<ST_KIND_PASS_BF16, O> {
     using G = Geom<ST_KIND_PASS_BF16, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
+    static __device__ __forceinline__ uint32_t sc(const Ctx&, uint64_t, uint64_t) { return 0; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint32_t, uint32_t* w) {
         if constexpr (O::CODE == ST_OUT_BF16) {  // the bits themselves
 #pragma unroll
             for (uint32_t k = 0; k < G::N; ++k) w[k] = in[k];
@@ -341,7 +355,8 @@ struct KF16 : Geom<ST_KIND_CAST_F16, O> {
     using G = Geom<ST_KIND_CAST_F16, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 2; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
+    static __device__ __forceinline__ uint32_t sc(const Ctx&, uint64_t, uint64_t) { return 0; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint32_t, uint32_t* w) {
         bool nan = false;
 #pragma unroll
         for (uint32_t k = 0; k < G::N; ++k) nan |= (in[k] & 0x7FFFu) > 0x7C00u || (in[k] & 0x7FFF0000u) > 0x7C000000u;
@@ -359,7 +374,8 @@ struct KF32 : Geom<ST_KIND_CAST_F32, O> {
     using G = Geom<ST_KIND_CAST_F32, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e * 4; }
-    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
+    static __device__ __forceinline__ uint32_t sc(const Ctx&, uint64_t, uint64_t) { return 0; }
+    static __device__ __forceinline__ bool fast(const Ctx&, const uint32_t* in, uint32_t, uint32_t* w) {
         bool nan = false;
 #pragma unroll
         for (uint32_t k = 0; k < G::N; ++k) nan |= (in[k] & 0x7FFFFFFFu) > 0x7F800000u;
@@ -390,7 +406,8 @@ struct KFp8Tensor : Geom<ST_KIND_FP8_TENSOR, O> {
     using G = Geom<ST_KIND_FP8_TENSOR, O>;
     static constexpr int SCALE = 1;  // D.scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t, uint32_t* w) {
+    static __device__ __forceinline__ uint32_t sc(const Ctx&, uint64_t, uint64_t) { return 0; }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint32_t, uint32_t* w) {
         return fp8_chunk<O, G::N>(in, c.s, w);
     }
 };
@@ -399,16 +416,19 @@ template <class O>
 struct KFp8Block : Geom<ST_KIND_FP8_BLOCK128, O> {
     using G = Geom<ST_KIND_FP8_BLOCK128, O>;
     static constexpr int SCALE = 0;  // no scalar scale
+    static constexpr bool EARLY_SC = O::BYTES == 2;
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
     // e: first output element of the chunk (a multiple of CE); with cols % CE == 0 the chunk lies
     // in one row and one 128-column block, otherwise it takes the exact path.
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t e, uint64_t, uint32_t* w) {
-        if ((c.D.cols & (G::CE - 1)) != 0) return false;
+    static __device__ __forceinline__ uint32_t sc(const Ctx& c, uint64_t e, uint64_t) {
+        if ((c.D.cols & (G::CE - 1)) != 0) return 0;
         const uint32_t e32 = uint32_t(e);
         const uint32_t row = stk::div_apply(e32, c.D.div_magic, c.D.div_shift);
         const uint32_t col = e32 - row * c.D.cols;
-        const float S = ld_f32(c.blob + c.D.scale + 4ull * ((row >> 7) * c.D.grid_cols + (col >> 7)), c.scale_al);
-        return fp8_chunk<O, G::N>(in, S, w);
+        return as_u32(ld_f32(c.blob + c.D.scale + 4ull * ((row >> 7) * c.D.grid_cols + (col >> 7)), c.scale_al));
+    }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint32_t sc, uint32_t* w) {
+        return ((c.D.cols & (G::CE - 1)) == 0) & fp8_chunk<O, G::N>(in, as_f32(sc), w);
     }
 };
 
@@ -418,8 +438,11 @@ struct KFp4 : Geom<ST_KIND_NVFP4, O> {
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
     // 8 elements from source element xs: (e2m1 * block scale) is exact in fp32, then one RNE
     // multiply by g
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
-        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 4));  // block scale of these 8 elements
+    // the e4m3 block scale of the chunk's 16-element block
+    static __device__ __forceinline__ uint32_t sc(const Ctx& c, uint64_t, uint64_t xs) {
+        return ld_u8(c.blob + c.D.scale + (xs >> 4));
+    }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint32_t code, uint32_t* w) {
         const float bs = fp8x2<false>(code).x;
         const float g = c.s;
         const uint32_t x = in[0];
@@ -429,6 +452,16 @@ struct KFp4 : Geom<ST_KIND_NVFP4, O> {
         put2<O>(w, 2, (p2.x * bs) * g, (p2.y * bs) * g);
         put2<O>(w, 3, (p3.x * bs) * g, (p3.y * bs) * g);
         return finite(g) & ((code & 0x7Fu) != 0x7Fu);  // decided last: see unit_full
+    }
+    // 4 elements from bytes B and B + 1 of x, with their block's scale code (unit_full_paired)
+    template <int B>
+    static __device__ __forceinline__ bool quad(const Ctx& c, uint32_t x, uint32_t code, uint32_t* w) {
+        const float bs = fp8x2<false>(code).x;
+        const float g = c.s;
+        const f32x2 p0 = fp4x2<B>(x), p1 = fp4x2<B + 1>(x);
+        put2<O>(w, 0, (p0.x * bs) * g, (p0.y * bs) * g);
+        put2<O>(w, 1, (p1.x * bs) * g, (p1.y * bs) * g);
+        return finite(g) & ((code & 0x7Fu) != 0x7Fu);
     }
 };
 
@@ -440,8 +473,10 @@ struct KMx8 : Geom<ST_KIND_MXFP8, O> {
     using G = Geom<ST_KIND_MXFP8, O>;
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e; }
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
-        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
+    static __device__ __forceinline__ uint32_t sc(const Ctx& c, uint64_t, uint64_t xs) {
+        return ld_u8(c.blob + c.D.scale + (xs >> 5));
+    }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint32_t code, uint32_t* w) {
         return fp8_chunk<O, G::N>(in, e8m0_exact(code), w);  // a NaN scale code fails its finite check
     }
 };
@@ -450,8 +485,10 @@ template <class O>
 struct KMx4 : Geom<ST_KIND_MXFP4, O> {
     static constexpr int SCALE = 0;  // no scalar scale
     static __device__ __forceinline__ uint64_t src_off(uint64_t e) { return e >> 1; }
-    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint64_t, uint64_t xs, uint32_t* w) {
-        const uint32_t code = ld_u8(c.blob + c.D.scale + (xs >> 5));
+    static __device__ __forceinline__ uint32_t sc(const Ctx& c, uint64_t, uint64_t xs) {
+        return ld_u8(c.blob + c.D.scale + (xs >> 5));
+    }
+    static __device__ __forceinline__ bool fast(const Ctx& c, const uint32_t* in, uint32_t code, uint32_t* w) {
         const float S = e8m0_exact(code);
         const uint32_t x = in[0];
         const f32x2 p0 = fp4x2<0>(x), p1 = fp4x2<1>(x), p2 = fp4x2<2>(x), p3 = fp4x2<3>(x);
@@ -460,6 +497,15 @@ struct KMx4 : Geom<ST_KIND_MXFP4, O> {
         put2<O>(w, 2, p2.x * S, p2.y * S);
         put2<O>(w, 3, p3.x * S, p3.y * S);
         return code != 0xFFu;  // decided last: see unit_full
+    }
+    // 4 elements from bytes B and B + 1 of x, with their block's scale code (unit_full_paired)
+    template <int B>
+    static __device__ __forceinline__ bool quad(const Ctx&, uint32_t x, uint32_t code, uint32_t* w) {
+        const float S = e8m0_exact(code);
+        const f32x2 p0 = fp4x2<B>(x), p1 = fp4x2<B + 1>(x);
+        put2<O>(w, 0, p0.x * S, p0.y * S);
+        put2<O>(w, 1, p1.x * S, p1.y * S);
+        return code != 0xFFu;
     }
 };
 
@@ -524,6 +570,15 @@ struct Fetch {
     }
 };
 
+// The scale word of a chunk decoded in the loop (not EARLY_SC), issued ahead of the decode.
+template <class K>
+__device__ __forceinline__ uint32_t late_sc(const Ctx& c, uint64_t e, uint64_t xs) {
+    if constexpr (!K::SC_LOAD) return 0;
+    const uint32_t s = K::sc(c, e, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    return s;
+}
+
 // The output pointer and the kind's scalar scale, loaded after the unit's data loads are issued.
 // False: the output address is not aligned to the output type, and nothing is written.
 template <class K, class O>
@@ -564,9 +619,16 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
     using F = Fetch<K, ALIGNED>;
     constexpr uint32_t NW = K::CE * O::BYTES / 4;
     const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
-    uint32_t raw[K::CH][F::RW];
+    uint32_t raw[K::CH][F::RW], sc[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
+    if constexpr (K::EARLY_SC) {
+#pragma unroll
+        for (uint32_t j = 0; j < K::CH; ++j) {
+            const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+            sc[j] = K::sc(c0, e, e);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     Ctx c = c0;
     uint8_t* out;
@@ -581,10 +643,11 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
     bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        const uint32_t s = K::EARLY_SC ? sc[j] : late_sc<K>(c, e, e);
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
-        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = K::fast(c, in, e, e, w) & vec;
+        ok[j] = K::fast(c, in, s, w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
@@ -594,6 +657,62 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j)
         if (!ok[j]) run_exact<K::KIND, O>(c, out, e0 + uint64_t(j * stk::kWave + lane) * K::CE, K::CE);
+}
+
+// A whole unit of packed fp4 into fp32.  A lane's 4-byte load holds 8 elements, 32 bytes of
+// output; stored as two adjacent 16-byte words per lane, every store instruction of the wave would
+// leave a 16-byte gap after each lane's word.  Instead, for the 512 elements of load step j, lanes
+// 2i and 2i + 1 load the words of chunks i and 32 + i and swap 16-bit halves with a DPP quad
+// permutation, so that lane l holds elements 4l..4l+3 and 256+4l..256+4l+3: each of the two store
+// instructions then covers 1024 contiguous bytes.  The same chunks are loaded as in unit_full.
+template <class K, class O, bool ALIGNED>
+__device__ __forceinline__ void unit_full_paired(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, ALIGNED>;
+    static_assert(K::CE == 8 && F::N == 1 && O::BYTES == 4, "8 packed fp4 elements per 4-byte word");
+    constexpr uint32_t GE = K::CE * stk::kWave;  // elements per load step
+    const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
+    const bool odd = (lane & 1u) != 0;
+    const uint32_t mine = (lane >> 1) + (odd ? stk::kWave / 2 : 0u);  // the chunk this lane loads
+    uint32_t raw[K::CH][F::RW];
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + mine, raw[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    Ctx c = c0;
+    uint8_t* out;
+    const bool valid = finish_ctx<K, O>(c, out);  // as in unit_full: no branch before the decode
+    const bool vec = valid & c.vec;
+    uint8_t* const ob = out + e0 * O::BYTES;
+    bool ok[K::CH];
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        const uint64_t ea = e0 + j * GE + 4 * lane, eb = ea + GE / 2;
+        const uint32_t sa = K::sc(c, ea, ea), sb = late_sc<K>(c, eb, eb);
+        uint32_t in[1];
+        F::align(raw[j], sh, in);
+        // quad_perm(1, 0, 3, 2): the value of lane l ^ 1
+        const uint32_t mate = uint32_t(__builtin_amdgcn_mov_dpp(int(in[0]), 0xB1, 0xF, 0xF, false));
+        // even lane: its own low half, then its mate's; odd lane: its mate's high half, then its own
+        const uint32_t x = odd ? __builtin_amdgcn_perm(in[0], mate, 0x07060302u)
+                               : __builtin_amdgcn_perm(mate, in[0], 0x05040100u);
+        uint32_t wa[4], wb[4];
+        ok[j] = K::template quad<0>(c, x, sa, wa) & K::template quad<2>(c, x, sb, wb) & vec;
+        if (ok[j]) {
+            uint8_t* p = ob + (j * GE + 4 * lane) * O::BYTES;
+            *reinterpret_cast<u32x4*>(p) = u32x4{wa[0], wa[1], wa[2], wa[3]};
+            *reinterpret_cast<u32x4*>(p + GE / 2 * O::BYTES) = u32x4{wb[0], wb[1], wb[2], wb[3]};
+        }
+    }
+    bool all = true;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+    if (__builtin_amdgcn_ballot_w64(!all) == 0 || !valid) return;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j)
+        if (!ok[j]) {
+            const uint64_t ea = e0 + j * GE + 4 * lane;
+            run_exact<K::KIND, O>(c, out, ea, 4);
+            run_exact<K::KIND, O>(c, out, ea + GE / 2, 4);
+        }
 }
 
 // Any unit: cnt elements (a larger unit size, or an output's final unit).
@@ -612,7 +731,7 @@ __device__ __forceinline__ void unit_any(const Ctx& c0, uint64_t e0, uint32_t cn
         F::load(base, ci, raw);
         F::align(raw, sh, in);
         const uint64_t e = e0 + uint64_t(ci) * K::CE;
-        if (c.vec && K::fast(c, in, e, e, w)) store_chunk<K, O>(ob, ci, w);
+        if (c.vec && K::fast(c, in, K::sc(c, e, e), w)) store_chunk<K, O>(ob, ci, w);
         else run_exact<K::KIND, O>(c, out, e, K::CE);
     }
 #pragma unroll 1
@@ -629,12 +748,14 @@ __device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, ui
     using F = Fetch<K, ALIGNED>;
     constexpr uint32_t NW = K::CE * O::BYTES / 4;
     const uint8_t* base = c0.blob + c0.D.src - sh;
-    uint32_t raw[K::CH][F::RW];
+    uint32_t raw[K::CH][F::RW], sc[K::CH];
     uint64_t xs[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
-        xs[j] = src_elem(c0.D, e0 + uint64_t(j * stk::kWave + lane) * K::CE);
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        xs[j] = src_elem(c0.D, e);
         F::load(base + K::src_off(xs[j]), 0, raw[j]);
+        if constexpr (K::EARLY_SC) sc[j] = K::sc(c0, e, xs[j]);
     }
     __builtin_amdgcn_sched_barrier(0);
     Ctx c = c0;
@@ -645,10 +766,11 @@ __device__ __forceinline__ void unit_strided_full(const Ctx& c0, uint64_t e0, ui
     bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        const uint32_t s = K::EARLY_SC ? sc[j] : late_sc<K>(c, e, xs[j]);
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
-        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        ok[j] = K::fast(c, in, e, xs[j], w) & vec;
+        ok[j] = K::fast(c, in, s, w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
     }
     bool all = true;
@@ -678,7 +800,7 @@ __device__ __forceinline__ void unit_strided_any(const Ctx& c0, uint64_t e0, uin
         uint32_t raw[F::RW], in[F::N], w[NW];
         F::load(base + K::src_off(x), 0, raw);
         F::align(raw, sh, in);
-        if (c.vec && K::fast(c, in, e, x, w)) store_chunk<K, O>(ob, ci, w);
+        if (c.vec && K::fast(c, in, K::sc(c, e, x), w)) store_chunk<K, O>(ob, ci, w);
         else run_exact<K::KIND, O>(c, out, e, K::CE);
     }
 #pragma unroll 1
@@ -712,7 +834,10 @@ template <class K, class O>
 __device__ __forceinline__ void run_unit(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
     const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src + K::src_off(e0)));
     if (cnt != K::CE * K::CH * stk::kWave) unit_any<K, O, false>(c, e0, cnt, a & 3u, lane);
-    else if ((a & (K::LG - 1)) == 0) unit_full<K, O, true>(c, e0, 0, lane);
+    else if constexpr (K::PAIRED) {
+        if ((a & (K::LG - 1)) == 0) unit_full_paired<K, O, true>(c, e0, 0, lane);
+        else unit_full_paired<K, O, false>(c, e0, a & 3u, lane);
+    } else if ((a & (K::LG - 1)) == 0) unit_full<K, O, true>(c, e0, 0, lane);
     else unit_full<K, O, false>(c, e0, a & 3u, lane);
 }
 

@@ -10,16 +10,18 @@ static_assert(sizeof(st_desc) == 64, "st_desc must stay 64 bytes");
 // Records a printf-style message for st_last_error() on this thread and returns `code`.
 st_status st_fail(st_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// Work-unit geometry, in elements per unit, for every output type.  kWords = 16-byte output words
-// per lane per unit for a 2-byte output type (8 elements each); output word o*64 + lane of a unit
-// belongs to lane `lane`, so each store instruction of the wavefront covers 1 KB of contiguous
-// output (fp32 outputs: twice the words, 4 elements each):
+// Work-unit geometry, in elements per unit.  kWords = 16-byte output words per lane per unit
+// counted for a 2-byte output type (8 elements each); output word o*64 + lane of a unit belongs to
+// lane `lane`, so each store instruction of the wavefront covers 1 KB of contiguous output (fp32
+// outputs: twice the words, 4 elements each):
 //   bf16/fp16 sources : 2 words -> 1024 elements (2 KB in, 2 KB out)
 //   fp32 sources      : 1 word  ->  512 elements (2 KB in, 1 KB out)
 //   fp8 (all scalings): 2 words -> 1024 elements (1 KB in, 2 KB out)
-//   nvfp4 / mxfp4     : 4 words -> 2048 elements (1 KB + 64-128 B in, 4 KB out)
-// so every unit reads about 1-2 KB and writes 1-4 KB (2-8 KB for fp32 outputs): one short, fully
-// coalesced burst per wave.
+//   nvfp4 / mxfp4     : 4 words -> 2048 elements (1 KB + 64-128 B in, 4 KB out); into fp32
+//                       outputs 2 words -> 1024 elements (512 B + 32-64 B in, 4 KB out)
+// so every unit reads about 0.5-2 KB and writes 1-4 KB: one short, fully coalesced burst per
+// wave.  (Packed fp4 into fp32 with 2048-element units, 8 KB written per wave, ran 10-14% slower
+// on MI355X than with 1024.)
 namespace stk {
 constexpr uint32_t kWave = 64;
 constexpr uint32_t kWordElems = 8;
@@ -35,15 +37,18 @@ constexpr uint32_t kWordElems = 8;
 #ifndef STK_WORDS_FP4
 #define STK_WORDS_FP4 4
 #endif
+#ifndef STK_WORDS_FP4_F32
+#define STK_WORDS_FP4_F32 2
+#endif
 constexpr uint32_t kWordsPass = STK_WORDS_PASS, kWordsF32 = STK_WORDS_F32, kWordsFp8 = STK_WORDS_FP8,
-                   kWordsFp4 = STK_WORDS_FP4;
+                   kWordsFp4 = STK_WORDS_FP4, kWordsFp4F32 = STK_WORDS_FP4_F32;
 
 constexpr uint32_t ilog2(uint32_t x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 
-constexpr uint32_t words_per_lane(uint32_t kind) {
+constexpr uint32_t words_per_lane(uint32_t kind, uint32_t out_dtype) {
     return kind == ST_KIND_PASS_BF16 || kind == ST_KIND_CAST_F16 ? kWordsPass
          : kind == ST_KIND_CAST_F32                              ? kWordsF32
-         : kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4        ? kWordsFp4
+         : kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4        ? (out_dtype == ST_OUT_F32 ? kWordsFp4F32 : kWordsFp4)
                                                                  : kWordsFp8;
 }
 // The kernel's chunk geometry per kind: output elements per chunk (8 for every kind: one 16-byte
@@ -67,8 +72,10 @@ constexpr uint32_t source_bits(uint32_t kind) {
 // Where the descriptors start in a work table of `groups` map entries.
 constexpr uint64_t table_desc_offset(uint64_t groups) { return 64 + (groups * 4 + 63) / 64 * 64; }
 
-// log2 of the default unit size (elements) of a kind
-constexpr uint32_t step_shift(uint32_t kind) { return ilog2(kWave * kWordElems * words_per_lane(kind)); }
+// log2 of the default unit size (elements) of a kind decoded into an output type
+constexpr uint32_t step_shift(uint32_t kind, uint32_t out_dtype) {
+    return ilog2(kWave * kWordElems * words_per_lane(kind, out_dtype));
+}
 
 // Exact unsigned 32-bit division by an invariant divisor d >= 1 (Granlund & Montgomery,
 // "Division by Invariant Integers using Multiplication", 1994, the round-up method with an

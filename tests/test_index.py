@@ -59,7 +59,15 @@ def test_tiny_traffic_is_the_documented_figure():
     assert ix.data_size == 718_856 and ix.traffic_bytes == 718_856 + 913_408
 
 
-STEP_SHIFT = {"PASS_BF16": 10, "CAST_F16": 10, "CAST_F32": 9, "FP8_TENSOR": 10, "FP8_BLOCK128": 10, "NVFP4": 11}
+STEP_SHIFT = {"PASS_BF16": 10, "CAST_F16": 10, "CAST_F32": 9, "FP8_TENSOR": 10, "FP8_BLOCK128": 10, "NVFP4": 11,
+              "MXFP8": 10, "MXFP4": 11}
+
+
+def step_shift(kind, out_dtype):
+    """Default unit size (log2 elements): packed fp4 into fp32 outputs uses 1024-element units."""
+    if kind in ("NVFP4", "MXFP4") and out_dtype == "f32":
+        return 10
+    return STEP_SHIFT[kind]
 
 DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("pitch", "<u4"), ("flags", "<u4"),
                  ("unit_begin", "<u4"),
@@ -117,10 +125,12 @@ def _check_map(d, m, units, numels):
     assert ends.max(initial=0) == units
 
 
+@pytest.mark.parametrize("k,out_dtype", [(3, "bf16"), (4, "bf16"), (7, "f16"), (4, "f32"), (7, "f32"), (2, "f32")])
 @pytest.mark.parametrize("scale", [0, 2])
-def test_table_invariants(scale):
-    buf = synth.config_bytes(3, small=True)
-    ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=scale)
+def test_table_invariants(scale, k, out_dtype):
+    buf = synth.config_bytes(k, small=True)
+    ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=scale, out_dtype=out_dtype)
+    esize = 4 if out_dtype == "f32" else 2
     raw, units = ix.table()
     h, d, m = _table(raw)
     outs = ix.outputs()
@@ -134,7 +144,7 @@ def test_table_invariants(scale):
             assert row["scale"] == ents[o.scale].begin
         if o.scale2 >= 0:
             assert row["scale2"] == ents[o.scale2].begin
-        assert row["unit_shift"] == STEP_SHIFT[o.kind] + scale
+        assert row["unit_shift"] == step_shift(o.kind, out_dtype) + scale
         assert row["unit_begin"] == pos
         pos += -(-o.numel // (1 << int(row["unit_shift"])))
         if o.kind == "FP8_BLOCK128":
@@ -144,8 +154,8 @@ def test_table_invariants(scale):
     # arena: 256-byte aligned, disjoint, in order
     offs = [o.offset for o in outs]
     assert all(x % 256 == 0 for x in offs)
-    assert all(offs[i] + 2 * outs[i].numel <= offs[i + 1] for i in range(len(offs) - 1))
-    assert ix.arena_bytes >= offs[-1] + 2 * outs[-1].numel
+    assert all(offs[i] + esize * outs[i].numel <= offs[i + 1] for i in range(len(offs) - 1))
+    assert ix.arena_bytes >= offs[-1] + esize * outs[-1].numel
     assert ix.blob_bytes % 256 == 0 and ix.blob_bytes >= ix.data_size
     assert ix.device_bytes >= ix.blob_bytes + ix.arena_bytes + len(raw)
 
