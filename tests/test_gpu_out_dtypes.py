@@ -100,9 +100,11 @@ def test_mx_every_code(kind, shift, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", TYPES)
-def test_outputs_not_aligned_to_16_bytes(out_dtype):
-    """Every output shifted by one element: the exact path writes them one at a time."""
-    buf = synth.config_bytes(2, small=True)
+@pytest.mark.parametrize("k", [2, 4, 7])
+def test_outputs_not_aligned_to_16_bytes(k, out_dtype):
+    """Every output shifted by one element: the exact path writes them one at a time (for packed
+    fp4 into fp32, from the paired-lane unit too)."""
+    buf = synth.config_bytes(k, small=True)
     ix, ck = _staged(buf, out_dtype)
     esize = 4 if out_dtype == "f32" else 2
     arena = torch.empty(ix.arena_bytes // esize + 8, dtype=ix.torch_dtype, device=DEV)
