@@ -6,6 +6,8 @@ configuration bench.py times (one st_materialize over the whole staged blob).
 * A spread of the quantised outputs is also checked whole against an independent GPU computation of
   the same definition with torch (float8_e4m3fn decode, fp32 products in the pages' order, RNE cast
   to bfloat16). The generated checkpoints hold no NaN code, where torch's NaN bits would differ.
+* The fp16 and fp32 kernel instances at full size (scaled FP8, block FP8, NVFP4, MXFP4): sampled
+  elements against the oracle's rounding to that type, whole quantised outputs against torch.
 * Maximum sizes (index built from the header alone, blob filled on the GPU): a bf16 tensor of more
   than 2^32 elements, a 128-block FP8 tensor just under the 2^32-element limit, and a per-tensor
   FP8 tensor whose source starts unaligned and ends past 2^31 bytes.
@@ -54,30 +56,35 @@ def _expand_grid(S, m, n):
     return S.repeat_interleave(128, 0)[:m].repeat_interleave(128, 1)[:, :n]
 
 
-def _torch_reference(kind, shape, blob, src, scale, scale2):
-    """bf16 value of one quantised output, computed whole with torch ops on the GPU."""
+def _torch_reference(kind, shape, blob, src, scale, scale2, out=torch.bfloat16):
+    """Value of one quantised output in the output type ``out``, computed whole with torch ops on
+    the GPU (the fp32 result, then torch's round-to-nearest-even cast)."""
+    return _torch_f32(kind, shape, blob, src, scale, scale2).to(out)
+
+
+def _torch_f32(kind, shape, blob, src, scale, scale2):
     numel = int(np.prod(shape))
     if kind == "FP8_TENSOR":
-        return (_e4m3(blob[src: src + numel]) * _f32(blob, scale, 1)).to(torch.bfloat16)
+        return _e4m3(blob[src: src + numel]) * _f32(blob, scale, 1)
     if kind == "FP8_BLOCK128":
         m, n = shape
         gm, gn = -(-m // 128), -(-n // 128)
         S = _expand_grid(_f32(blob, scale, gm * gn).view(gm, gn), m, n)
-        return (_e4m3(blob[src: src + numel]).view(m, n) * S).to(torch.bfloat16).view(-1)
+        return (_e4m3(blob[src: src + numel]).view(m, n) * S).view(-1)
     if kind == "NVFP4":
         packed = blob[src: src + numel // 2]
         nib = torch.stack([packed & 15, packed >> 4], dim=1).view(-1).long()
         table = torch.tensor(E2M1, dtype=torch.float32, device=blob.device)
         bs = _e4m3(blob[scale: scale + numel // 16]).repeat_interleave(16)
-        return ((table[nib] * bs) * _f32(blob, scale2, 1)).to(torch.bfloat16)
+        return (table[nib] * bs) * _f32(blob, scale2, 1)
     if kind in ("MXFP8", "MXFP4"):   # E8M0 scale per 32 elements, decoded by torch on the CPU
         S = blob[scale: scale + numel // 32].cpu().view(torch.float8_e8m0fnu).float().to(blob.device)
         S = S.repeat_interleave(32)
         if kind == "MXFP8":
-            return (_e4m3(blob[src: src + numel]) * S).to(torch.bfloat16)
+            return _e4m3(blob[src: src + numel]) * S
         packed = blob[src: src + numel // 2]
         nib = torch.stack([packed & 15, packed >> 4], dim=1).view(-1).long()
-        return (torch.tensor(E2M1, dtype=torch.float32, device=blob.device)[nib] * S).to(torch.bfloat16)
+        return torch.tensor(E2M1, dtype=torch.float32, device=blob.device)[nib] * S
     raise ValueError(kind)
 
 
@@ -123,6 +130,54 @@ def test_full_size_checkpoint(k, tmp_path):
                 e = ents[co.tensor]
                 assert torch.equal(got_t.view(torch.uint8), ck.blob[e.begin: e.end]), f"{o.name}: passthrough"
         print(f"config {k}: {len(outs)} outputs sampled; checked whole: {whole}", flush=True)
+        del ck
+    finally:
+        os.remove(path)
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k,out_dtype", [(2, "f32"), (4, "f32"), (7, "f32"), (4, "f16"), (3, "f32")])
+def test_full_size_output_types(k, out_dtype, tmp_path):
+    """The fp16 and fp32 kernel instances at full size, in the bench's launch configuration: sampled
+    elements of every output against the oracle, and whole quantised outputs against torch."""
+    path = str(tmp_path / f"c{k}.safetensors")
+    print(f"full-size config {k} into {out_dtype}: writing", flush=True)
+    synth.write_config(k, path)
+    tdt, ibits = {"f16": (torch.float16, torch.int16), "f32": (torch.float32, torch.int32)}[out_dtype]
+    try:
+        ix = st.SafeTensorIndex.open(path, out_dtype=out_dtype)
+        ck = st.DeviceCheckpoint(ix, path, DEV)
+        ck.arena.view(torch.int16).fill_(0x5A5A)
+        ck.materialize()
+        torch.cuda.synchronize()
+        mm = np.memmap(path, dtype=np.uint8, mode="r")
+        h, outs = oracle.plan(mm)
+        data = mm[h.data_offset:]
+        rng = np.random.default_rng(100 + k)
+        ents = ix.tensors()
+        couts = ix.outputs()
+        esize = 4 if out_dtype == "f32" else 2
+        where, want = [], []
+        for o, co in zip(outs, couts):
+            if o.numel:
+                idx = _sample_idx(o.shape, o.numel, rng)
+                where.append(co.offset // esize + idx)
+                want.append(oracle.decode(o, data, idx, out_dtype))
+        where = torch.from_numpy(np.concatenate(where)).to(DEV)
+        got = ck.arena.view(ibits)[where].cpu().numpy()
+        want = np.concatenate(want)
+        bad = np.flatnonzero(got.view(want.dtype) != want)
+        assert bad.size == 0, f"{bad.size} sampled elements differ from the oracle"
+        whole = {kind: 0 for kind in QUANT}
+        for o, co in zip(outs, couts):
+            if o.kind in QUANT and whole[o.kind] < 4:
+                ref = _torch_reference(o.kind, o.shape, ck.blob, ents[co.tensor].begin,
+                                       ents[co.scale].begin, ents[co.scale2].begin if co.scale2 >= 0 else 0, tdt)
+                got_t = ck.tensors[o.name].reshape(-1)
+                assert got_t.dtype == tdt
+                assert torch.equal(got_t.view(ibits), ref.view(ibits)), f"{o.name}: whole tensor differs"
+                whole[o.kind] += 1
+        print(f"config {k} into {out_dtype}: {len(outs)} outputs sampled; checked whole: {whole}", flush=True)
         del ck
     finally:
         os.remove(path)
