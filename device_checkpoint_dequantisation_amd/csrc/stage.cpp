@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cerrno>
 #include <chrono>
 #include <condition_variable>
 #include <mutex>
@@ -90,6 +91,7 @@ class ReaderPool {
             size_t b = 0;
             while (b < p.len) {
                 const ssize_t r = pread(fd_, p.dst + b, p.len - b, off_t(p.off + b));
+                if (r < 0 && errno == EINTR) continue;  // interrupted before any byte was read
                 if (r <= 0) {
                     ok_.store(false);
                     break;
@@ -242,6 +244,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     std::vector<Piece> batch;
     hipStream_t side = static_cast<hipStream_t>(side_stream), compute = static_cast<hipStream_t>(compute_stream);
     st_stream_stats st{};
+    int last_slot = -1;  // ring slot of the last step that copied bytes
     const size_t nsteps = st_stream_plan_num_steps(plan);
     for (size_t s = 0; status == ST_OK && s < nsteps; ++s) {
         st_stream_step step;
@@ -286,9 +289,13 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
             }
             st.bytes_read += pos;
             ++st.steps;
+            last_slot = slot_id;
         }
         if (step.units) {
-            if (step.bytes && hipStreamWaitEvent(compute, ring.ev[slot_id], 0) != hipSuccess) {
+            // The side stream runs its copies in order, so the event of the last step that copied
+            // anything covers every byte this step's outputs read (a plan attaches an output to a
+            // step that copies its last byte, so that is normally this step's own event).
+            if (last_slot >= 0 && hipStreamWaitEvent(compute, ring.ev[last_slot], 0) != hipSuccess) {
                 status = st_fail(ST_E_HIP, "st_stream_file: hipStreamWaitEvent failed");
                 break;
             }
