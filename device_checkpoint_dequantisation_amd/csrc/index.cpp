@@ -698,7 +698,7 @@ std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* 
     for (size_t j = 0; j < k; ++j) {
         whole[j] = make_desc(ix, ix.outputs[sel[j]], uint32_t(j), 0, &nu[j], at);
         total += nu[j];
-        if (total >= (uint64_t(1) << 32)) throw std::length_error("too many work units");
+        if (total >= (uint64_t(1) << 32)) throw std::length_error("2^32 or more work units");
     }
     const bool cut = eighth_imbalance(ix, sel, k, nu, total) > kImbalance;
     uint64_t small = 0;  // units of the outputs that are not cut
@@ -849,8 +849,8 @@ st_status plan(st_index& ix) {
     for (size_t k = 0; k < all.size(); ++k) all[k] = uint32_t(k);
     try {
         ix.table = sti::build_table(ix, all.data(), all.size(), &ix.total_units);
-    } catch (const std::length_error&) {
-        return st_fail(ST_E_SHAPE, "checkpoint needs 2^32 or more work units");
+    } catch (const std::length_error& e) {
+        return st_fail(ST_E_SHAPE, "checkpoint too large for one work table: %s", e.what());
     }
     return ST_OK;
 }
@@ -1037,8 +1037,8 @@ extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* 
         t = sti::build_table(*idx, sel, k, &u);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
-    } catch (const std::length_error&) {
-        return st_fail(ST_E_SHAPE, "st_index_table_subset: 2^32 or more work units");
+    } catch (const std::length_error& e) {
+        return st_fail(ST_E_SHAPE, "st_index_table_subset: %s", e.what());
     }
     if (bytes) *bytes = t.size();
     if (units) *units = u;
@@ -1080,6 +1080,8 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
         t = assemble(descs, pos, idx->out_dtype);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
+    } catch (const std::length_error& e) {
+        return st_fail(ST_E_SHAPE, "st_index_table_slices: %s", e.what());
     }
     if (bytes) *bytes = t.size();
     if (units) *units = pos;

@@ -214,9 +214,9 @@ st_status make_plan(const st_index* idx, const uint32_t* sel, size_t k, bool all
     } catch (const std::bad_alloc&) {
         delete p;
         return st_fail(ST_E_NOMEM, "out of host memory");
-    } catch (const std::length_error&) {
+    } catch (const std::length_error& e) {
         delete p;
-        return st_fail(ST_E_SHAPE, "st_stream_plan: a step needs 2^32 or more work units, or too many steps");
+        return st_fail(ST_E_SHAPE, "st_stream_plan: %s", e.what());
     }
     *out = p;
     return ST_OK;
