@@ -418,8 +418,8 @@ def lazy_loads(path, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the materialise path is "
-              f"per-GPU independent and is not sharded in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each GPU decodes its own "
+              f"outputs independently, and this library does not shard a checkpoint across GPUs)", file=sys.stderr)
         sys.exit(2)
     rng = np.random.default_rng(0)
     d = args.tmpdir or tempfile.mkdtemp(prefix="stmat_bench_")
