@@ -427,3 +427,25 @@ def test_launch_arguments_are_checked_before_any_gpu_call():
     assert b"pinned buffer" in L.st_last_error()
     assert L.st_stage_file(b"/nonexistent", ix._h, C.c_void_p((1 << 20) + 8), ok, 1 << 30, None, None, None) == -1
     assert b"blob is not" in L.st_last_error()
+
+
+@pytest.mark.parametrize("delta", [-1, 1])
+def test_staging_refuses_a_file_of_the_wrong_size_before_any_gpu_call(delta, tmp_path):
+    """st_stage_file and st_stream_file open the file and compare its size with the index before
+    any GPU call; a file one byte shorter or longer fails with ST_E_IO and both sizes named.  A
+    missing file fails the same way."""
+    import ctypes as C
+    L = _lib.lib()
+    ok = C.c_void_p(1 << 20)        # aligned stand-ins; these paths stop before using them
+    buf = synth.config_bytes(1)
+    ix = _index(buf)
+    p = tmp_path / "c1.safetensors"
+    p.write_bytes(buf[:-1] if delta < 0 else buf + b"\0")
+    want = f"the index expects {len(buf)}".encode()
+    assert L.st_stage_file(str(p).encode(), ix._h, ok, ok, 1 << 30, None, None, None) == -2
+    assert want in L.st_last_error() and f"{len(buf) + delta} bytes".encode() in L.st_last_error()
+    plan = st.StreamPlan(ix, 1 << 20)
+    assert L.st_stream_file(str(p).encode(), ix._h, plan._h, ok, ok, ok, ok, 64 << 20, None, None, None, None) == -2
+    assert want in L.st_last_error()
+    assert L.st_stage_file(str(tmp_path / "missing").encode(), ix._h, ok, ok, 1 << 30, None, None, None) == -2
+    assert b"cannot open" in L.st_last_error()
