@@ -135,3 +135,38 @@ E8 = np.full(4, 127, np.uint8)
 def test_mx_malformed_is_rejected(tensors, match):
     with pytest.raises(OracleError, match=match):
         oracle.plan(make_file(tensors))
+
+
+def test_mxfp4_matches_an_independent_library_decoder():
+    """transformers' MXFP4 dequantiser (written for checkpoints that store 32 e2m1 values as 16
+    uint8 bytes per block with one E8M0 byte per block) is an implementation of the packed layout
+    independent of the oracle.  Its fp32 output pins the nibble order (element 2k in the low
+    nibble of byte k) and the block-scale mapping.  The file is built from the packed bytes
+    themselves, so the test does not assume the order it checks."""
+    pytest.importorskip("transformers")
+    from transformers.integrations.mxfp4 import convert_moe_packed_tensors
+    rng = np.random.default_rng(11)
+    m, k = 24, 96
+    packed = rng.integers(0, 256, m * k // 2, dtype=np.uint64).astype(np.uint8)
+    scales = rng.integers(100, 150, m * (k // 32), dtype=np.uint64).astype(np.uint8)
+    buf = make_file([("w.weight", "U8", (m, k // 2), packed), ("w.weight_scale", "F8_E8M0", (m, k // 32), scales)])
+    got = oracle.materialize(buf, "f32")["w.weight"]
+    blocks = torch.from_numpy(packed.copy()).view(1, m, k // 32, 16)
+    sc = torch.from_numpy(scales.copy()).view(1, m, k // 32)
+    ref = convert_moe_packed_tensors(blocks, sc, dtype=torch.float32)   # [1, k, m]: rows last
+    ref = ref[0].transpose(0, 1).contiguous().numpy()
+    assert ref.shape == (m, k)
+    assert np.array_equal(got, ref.view(np.uint32))
+
+
+def test_nvfp4_nibble_order_is_the_pinned_mxfp4_order():
+    """The oracle's NVFP4 branch unpacks nibbles on its own; with every block scale 1.0 (e4m3 0x38)
+    and a global scale of 1.0 it must equal the MXFP4 branch (pinned above) at scale 2^0."""
+    rng = np.random.default_rng(12)
+    m, k = 16, 64
+    packed = rng.integers(0, 256, m * k // 2, dtype=np.uint64).astype(np.uint8)
+    nv = make_file([("w.weight", "U8", (m, k // 2), packed), ("w.weight_scale", "F8_E4M3", (m, k // 16),
+                    np.full(m * k // 16, 0x38, np.uint8)), ("w.weight_scale_2", "F32", (), f32_bytes(1.0))])
+    mx = make_file([("w.weight", "U8", (m, k // 2), packed),
+                    ("w.weight_scale", "F8_E8M0", (m, k // 32), np.full(m * k // 32, 127, np.uint8))])
+    assert np.array_equal(oracle.materialize(nv, "f32")["w.weight"], oracle.materialize(mx, "f32")["w.weight"])
