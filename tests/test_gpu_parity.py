@@ -259,3 +259,31 @@ def test_large_outputs_cut_into_pieces():
     ck = assert_parity(pieces_file())
     h = np.frombuffer(ck.table.cpu().numpy().tobytes()[:64], dtype=np.uint32)
     assert ck.units > 7000 and h[1] > len(ck.tensors)   # n_desc: the large outputs were cut
+
+
+def test_concurrent_decodes_on_separate_streams():
+    """The library keeps no device state between launches, so decodes of different checkpoints
+    (and output types) enqueued on separate streams may run at the same time: each must still
+    equal the oracle.  Each stream decodes its checkpoint three times in a row."""
+    cases = [(2, "bf16"), (4, "f32"), (7, "f16"), (3, "bf16")]
+    cks, wants, streams = [], [], []
+    for k, dt in cases:
+        buf = synth.config_bytes(k, small=True)
+        ix = st.SafeTensorIndex.from_bytes(buf, out_dtype=dt)
+        ck = st.DeviceCheckpoint(ix, None, DEV)
+        ck.load_bytes(buf[ix.data_offset:])
+        ck.arena.view(torch.int16).fill_(0x5A5A)
+        cks.append(ck)
+        wants.append(oracle.materialize(buf, dt))
+        streams.append(torch.cuda.Stream(DEV))
+    torch.cuda.synchronize()
+    print(f"concurrent decodes: {cases}", flush=True)
+    for _ in range(3):
+        for ck, s in zip(cks, streams):
+            ck.materialize(s)
+    torch.cuda.synchronize()
+    for (k, dt), ck, want in zip(cases, cks, wants):
+        for name, w in want.items():
+            t = ck.tensors[name].contiguous()
+            g = (t.view(torch.int32) if dt == "f32" else t.view(torch.int16)).cpu().numpy().view(w.dtype)
+            assert np.array_equal(g.reshape(w.shape), w), (k, dt, name)
