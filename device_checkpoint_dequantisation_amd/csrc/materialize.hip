@@ -14,14 +14,16 @@
 // element, a handful of VALU operations per element), so there is no matrix-core work; what
 // matters on gfx950 is how the HBM traffic is issued:
 //  * One wavefront per work unit, one-shot.  A unit is 512-2048 elements of one output (about
-//    1-2 KB read, 1-4 KB written; measured best against half and double sizes).  Each wavefront loads its unit, decodes, stores and exits.
+//    0.5-2 KB read, 1-4 KB written; measured best against half and double sizes).  Each
+//    wavefront loads its unit, decodes, stores and exits.
 //    Measured on MI355X, one-shot wavefronts sustain ~20% more read+write bandwidth than any
 //    persistent loop tried (grid-stride, contiguous ranges, software-pipelined), because a
 //    persistent wavefront's next loads wait behind its own outstanding stores (vmcnt counts both).
 //  * Lane-contiguous chunks.  A chunk is one 16-byte output word: 8 elements of a 2-byte output
-//    type, 4 of fp32 (packed fp4 keeps 8, two adjacent fp32 words).  Chunk j*64 + l of a unit
-//    belongs to lane l, so a store instruction of a wavefront covers 1 KB of contiguous output and
-//    a load instruction a contiguous run of the source; lanes read whatever input bytes their
+//    type, 4 of fp32 (packed fp4 keeps 8-element chunks and pairs lanes instead: see
+//    unit_full_paired).  Chunk j*64 + l of a unit belongs to lane l, so a store instruction of a
+//    wavefront covers 1 KB of contiguous output and a load instruction a contiguous run of the
+//    source; lanes read whatever input bytes their
 //    chunk needs (4, 8 or 16 bytes; 32 for fp32 sources to 2-byte outputs).  Measured on MI355X,
 //    lanes that each store two adjacent words lose about 20%, four adjacent words about 30%.
 //  * XCD-contiguous order.  The hardware hands workgroup b to XCD b mod 8; workgroups are
@@ -30,7 +32,8 @@
 //  * Tiny tensors.  Units are numbered consecutively across outputs and a workgroup's four
 //    wavefronts take four consecutive units, whatever output they belong to, so small tensors are
 //    packed at wavefront granularity.  A per-workgroup map gives the descriptor of the group's
-//    first unit; a wavefront walks forward at most three descriptors.
+//    first unit; a wavefront walks forward from it (at most three descriptors, plus any outputs
+//    with no units in between).
 //  * Unaligned sources.  A tensor may start at any byte.  A unit whose source is aligned to its
 //    chunk's load word (the chunk's source bytes, at most 16) loads whole words.  Otherwise each lane
 //    loads from the 4-byte boundary at or below its bytes (16-byte words at 4-byte alignment and
@@ -871,7 +874,7 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     uint32_t d = ld_uniform<uint32_t>(table + sizeof(st_table_header) + 4 * size_t(grp));
     const st_desc* descs = reinterpret_cast<const st_desc*>(table + desc_off);
     Desc D = load_desc(descs + d);
-    while (unit >= D.unit_end) D = load_desc(descs + (++d));  // at most 3 steps, past empty outputs
+    while (unit >= D.unit_end) D = load_desc(descs + (++d));  // up to 3 steps, plus empty outputs
 
     const uint64_t e0 = uint64_t(unit - D.unit_begin) << D.unit_shift;
     const uint32_t cnt = unit + 1 == D.unit_end ? D.tail : 1u << D.unit_shift;
