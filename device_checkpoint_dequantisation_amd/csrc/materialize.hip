@@ -23,9 +23,9 @@
 //    type, 4 of fp32 (packed fp4 keeps 8-element chunks and pairs lanes instead: see
 //    unit_full_paired).  Chunk j*64 + l of a unit belongs to lane l, so a store instruction of a
 //    wavefront covers 1 KB of contiguous output and a load instruction a contiguous run of the
-//    source; lanes read whatever input bytes their
-//    chunk needs (4, 8 or 16 bytes; 32 for fp32 sources to 2-byte outputs).  Measured on MI355X,
-//    lanes that each store two adjacent words lose about 20%, four adjacent words about 30%.
+//    source; lanes read whatever input bytes their chunk needs (4, 8 or 16 bytes; 32 for fp32
+//    sources to 2-byte outputs).  Measured on MI355X, lanes that each store two adjacent words
+//    lose about 20%, four adjacent words about 30%.
 //  * XCD-contiguous order.  The hardware hands workgroup b to XCD b mod 8; workgroups are
 //    renumbered so each XCD streams through one contiguous eighth of the work (the host planner
 //    balances the eighths' bytes when formats of different bytes per unit mix).
