@@ -900,7 +900,7 @@ extern "C" st_status st_index_build(const void* header_bytes, uint64_t header_le
     ix->header_len = n;
     ix->data_size = file_size - hb;
     ix->unit_log2_scale = opts ? opts->unit_log2_scale : 0;
-    ix->out_dtype = opts ? (opts->flags & 3u) : ST_OUT_BF16;
+    ix->out_dtype = opts ? (opts->flags & 3u) : uint32_t(ST_OUT_BF16);
     try {
         JVal root;
         if (st_status r = JsonReader(text, n).parse(root)) return r;
@@ -1092,4 +1092,4 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
     return ST_OK;
 }
 
-extern "C" uint32_t st_index_out_dtype(const st_index* idx) { return idx ? idx->out_dtype : ST_OUT_BF16; }
+extern "C" uint32_t st_index_out_dtype(const st_index* idx) { return idx ? idx->out_dtype : uint32_t(ST_OUT_BF16); }
