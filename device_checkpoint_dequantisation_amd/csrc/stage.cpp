@@ -22,6 +22,7 @@
 #include <cerrno>
 #include <chrono>
 #include <condition_variable>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -44,12 +45,14 @@ struct Piece {
     size_t len;
 };
 
-// Reader threads for one staging call.  read() splits a batch of ranges into pieces and reads
-// them with pread on the pool's threads and the calling thread; every thread takes part in every
-// batch, so a batch is over once all of them have checked in.
+// Reader threads.  read() splits a batch of ranges of one file into pieces and reads them with
+// pread on the pool's threads and the calling thread; every thread takes part in every batch, so
+// a batch is over once all of them have checked in.  One pool serves the whole process (see
+// Readers below): starting eight threads per call cost a 113 MB per-layer load about 0.1 ms
+// (measured on the GPU machine's host, 2.72-2.82 ms per layer against 2.66).
 class ReaderPool {
   public:
-    explicit ReaderPool(int fd) : fd_(fd) {
+    ReaderPool() {
         for (int i = 0; i < kReaders; ++i) threads_.emplace_back([this] { worker(); });
     }
     ~ReaderPool() {
@@ -61,7 +64,7 @@ class ReaderPool {
         for (auto& t : threads_) t.join();
     }
     // False if a read failed or hit the end of the file.
-    bool read(const std::vector<Piece>& ranges) {
+    bool read(int fd, const std::vector<Piece>& ranges) {
         size_t total = 0;
         for (const Piece& r : ranges) total += r.len;
         const size_t piece = std::max<size_t>(size_t(1) << 20, (total / (2 * (kReaders + 1)) + 4095) & ~size_t(4095));
@@ -71,6 +74,7 @@ class ReaderPool {
                 pieces.push_back(Piece{r.dst + b, r.off + b, std::min(piece, r.len - b)});
         {
             std::lock_guard<std::mutex> lk(m_);
+            fd_ = fd;
             pieces_.swap(pieces);
             next_.store(0);
             ok_.store(true);
@@ -114,7 +118,7 @@ class ReaderPool {
         }
     }
 
-    int fd_;
+    int fd_ = -1;                 // the batch's file; written only while every thread is idle
     std::vector<std::thread> threads_;
     std::mutex m_;
     std::condition_variable cv_, done_cv_;
@@ -124,6 +128,40 @@ class ReaderPool {
     size_t checked_in_ = 0;
     uint64_t gen_ = 0;
     bool stop_ = false;
+};
+
+// The process's reader pool, taken for the length of one call.  A call that finds it in use (a
+// concurrent call from another thread) gets a pool of its own for that call.  The shared pool is
+// never destroyed (its threads wait on a condition variable until the process ends), and a child
+// process created by fork() starts a pool of its own, since the parent's threads do not exist in it.
+class Readers {
+  public:
+    Readers() {
+        std::unique_lock<std::mutex> lk(shared_mutex(), std::try_to_lock);
+        if (lk.owns_lock()) {
+            static ReaderPool* pool = nullptr;
+            static pid_t owner = 0;
+            if (!pool || owner != getpid()) {
+                pool = new ReaderPool();  // any pool left from before a fork is abandoned
+                owner = getpid();
+            }
+            lock_ = std::move(lk);
+            pool_ = pool;
+        } else {
+            own_.reset(new ReaderPool());
+            pool_ = own_.get();
+        }
+    }
+    bool read(int fd, const std::vector<Piece>& ranges) { return pool_->read(fd, ranges); }
+
+  private:
+    static std::mutex& shared_mutex() {
+        static std::mutex m;
+        return m;
+    }
+    std::unique_lock<std::mutex> lock_;
+    std::unique_ptr<ReaderPool> own_;
+    ReaderPool* pool_ = nullptr;
 };
 
 // An open file descriptor, closed on scope exit.
@@ -180,7 +218,7 @@ extern "C" st_status st_stage_file(const char* path, const st_index* idx, void* 
     if (status != ST_OK) return status;
     RingEvents ring;
     if ((status = ring.create()) != ST_OK) return status;
-    ReaderPool pool(file.fd);
+    Readers pool;
     hipStream_t stream = static_cast<hipStream_t>(side_stream);
     const size_t chunk = (pinned_bytes / kSlots) & ~size_t(4095);
     double t_read = 0;
@@ -194,7 +232,7 @@ extern "C" st_status st_stage_file(const char* path, const st_index* idx, void* 
             break;
         }
         auto t0 = std::chrono::steady_clock::now();
-        const bool ok = pool.read({Piece{slot, off0 + done, len}});
+        const bool ok = pool.read(file.fd, {Piece{slot, off0 + done, len}});
         t_read += seconds_since(t0);
         if (!ok) {
             status = st_fail(ST_E_IO, "read of %s failed at byte %llu", path, (unsigned long long)(off0 + done));
@@ -240,7 +278,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     if (status != ST_OK) return status;
     RingEvents ring;
     if ((status = ring.create()) != ST_OK) return status;
-    ReaderPool pool(file.fd);
+    Readers pool;
     std::vector<Piece> batch;
     hipStream_t side = static_cast<hipStream_t>(side_stream), compute = static_cast<hipStream_t>(compute_stream);
     st_stream_stats st{};
@@ -268,7 +306,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
                 pos += len;
             }
             auto t0 = std::chrono::steady_clock::now();
-            if (!pool.read(batch))
+            if (!pool.read(file.fd, batch))
                 status = st_fail(ST_E_IO, "read of %s failed in step %zu", path, s);
             st.seconds_read += seconds_since(t0);
             if (status != ST_OK) break;
@@ -337,8 +375,8 @@ extern "C" st_status st_read_plans(const char* path, const st_index* idx, const 
     if (status != ST_OK) return status;
     auto t0 = std::chrono::steady_clock::now();
     {
-        ReaderPool pool(file.fd);
-        if (!pool.read(batch)) status = st_fail(ST_E_IO, "read of %s failed", path);
+        Readers pool;
+        if (!pool.read(file.fd, batch)) status = st_fail(ST_E_IO, "read of %s failed", path);
     }
     if (seconds_read) *seconds_read = seconds_since(t0);
     return status;

@@ -288,3 +288,52 @@ def test_read_plans_several_and_errors(tmp_path):
     (tmp_path / "short.safetensors").write_bytes(buf[:-1])
     with pytest.raises(st.StError, match="ST_E_IO"):
         st.read_plans(str(tmp_path / "short.safetensors"), ix, plans[:1], hosts[:1])
+
+
+def test_read_plans_from_several_threads_and_files(tmp_path):
+    """The reader pool is shared by the process: repeated calls reuse it, calls on different files
+    and calls from several threads at once (one takes the shared pool, the others a pool of their
+    own) all land their bytes exactly."""
+    import threading
+    import torch
+    files = []
+    for k in (2, 4, 6):
+        buf = synth.config_bytes(k, small=True)
+        path = tmp_path / f"c{k}.safetensors"
+        path.write_bytes(buf)
+        ix = st.SafeTensorIndex.open(str(path))
+        plan = st.StreamPlan(ix, 64 << 10, select=list(range(ix.num_outputs)), pack=True)
+        files.append((str(path), ix, plan, np.frombuffer(buf, np.uint8)[ix.data_offset:]))
+
+    def check(path, ix, plan, data, host):
+        for k in range(ix.num_outputs):
+            co = ix.output(k)
+            for i in (co.tensor, co.scale, co.scale2):
+                if i >= 0:
+                    e = ix.tensors()[i]
+                    d = plan.tensor_offset(e.begin)
+                    assert np.array_equal(host.numpy()[d: d + e.end - e.begin], data[e.begin:e.end])
+
+    for _ in range(3):                       # sequential calls, alternating files
+        for path, ix, plan, data in files:
+            host = torch.zeros(plan.blob_bytes, dtype=torch.uint8)
+            st.read_plans(path, ix, [plan], [host])
+            check(path, ix, plan, data, host)
+    errors = []
+
+    def worker(j):
+        try:
+            path, ix, plan, data = files[j % len(files)]
+            for _ in range(5):
+                host = torch.zeros(plan.blob_bytes, dtype=torch.uint8)
+                st.read_plans(path, ix, [plan], [host])
+                check(path, ix, plan, data, host)
+        except Exception as e:   # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
