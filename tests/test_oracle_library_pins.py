@@ -50,3 +50,22 @@ def test_mxfp8_equals_the_library_dequantiser():
         got = oracle.materialize(buf, out_dtype)["w.weight"]
         ref = _dequantize(q, s, tdt).contiguous().view(idt).numpy().view(got.dtype)
         assert np.array_equal(got, ref), out_dtype
+
+
+def test_nvfp4_with_unit_global_scale_equals_the_library_dequantiser():
+    """The library also dequantises packed e2m1 weights (int8 storage, two nibbles per byte) against
+    a scale grid; with e4m3 block scales over [M, K/16] it computes NVFP4's first product.  With a
+    global scale of 1.0 the oracle's NVFP4 output must equal it: this pins the [M, K/16] block-scale
+    layout and the e4m3 scale decode of the NVFP4 branch against an independent implementation."""
+    rng = np.random.default_rng(21)
+    m, k = 32, 128
+    packed = rng.integers(0, 256, m * k // 2, dtype=np.uint64).astype(np.uint8)
+    bs = _codes(rng, m * k // 16)
+    buf = make_file([("w.weight", "U8", (m, k // 2), packed), ("w.weight_scale", "F8_E4M3", (m, k // 16), bs),
+                     ("w.weight_scale_2", "F32", (), np.array([1.0], np.float32).tobytes())])
+    q = torch.from_numpy(packed.copy()).view(torch.int8).view(m, k // 2)
+    s = torch.from_numpy(bs.copy()).view(torch.float8_e4m3fn).view(m, k // 16)
+    for out_dtype, tdt, idt in (("f32", torch.float32, torch.int32), ("bf16", torch.bfloat16, torch.int16)):
+        got = oracle.materialize(buf, out_dtype)["w.weight"]
+        ref = _dequantize(q, s, tdt).contiguous().view(idt).numpy().view(got.dtype)
+        assert np.array_equal(got, ref), out_dtype
