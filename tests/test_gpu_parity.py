@@ -72,7 +72,7 @@ def fp8_every_code_file(shift):
     return make_file(tensors)
 
 
-def nvfp4_every_code_file(shift):
+def nvfp4_every_code_file(shift, storage="U8"):
     """Rows of K = 48 (K % 32 == 16): every e2m1 code against every e4m3 block-scale code,
     including NaN codes and subnormals, under several global scales."""
     sc = np.arange(256, dtype=np.uint8)
@@ -82,7 +82,8 @@ def nvfp4_every_code_file(shift):
     bs = np.repeat(sc, 6)[: M * K // 16]
     tensors = list(_pad(shift))
     for i, g in enumerate([0x3B2D27D2, 0x3F800000, 0x00000001, 0x7F7FFFFF, 0x7F800000, 0x7FC00000, 0x00000000]):
-        tensors += [(f"n{i}.weight", "U8", (M, K // 2), packed), (f"n{i}.weight_scale", "F8_E4M3", (M, K // 16), np.roll(bs, i)),
+        wshape = (M, K // 2) if storage == "U8" else (M, K)   # F4: the shape counts unpacked elements
+        tensors += [(f"n{i}.weight", storage, wshape, packed), (f"n{i}.weight_scale", "F8_E4M3", (M, K // 16), np.roll(bs, i)),
                     (f"n{i}.weight_scale_2", "F32", (), np.array([g], np.uint32).tobytes())]
     return make_file(tensors)
 
@@ -138,9 +139,10 @@ def test_fp8_tensor_every_code_every_alignment(shift):
     assert_parity(fp8_every_code_file(shift))
 
 
+@pytest.mark.parametrize("storage", ["U8", "F4"])
 @pytest.mark.parametrize("shift", [0, 1, 3, 6])
-def test_nvfp4_every_nibble_every_block_scale(shift):
-    assert_parity(nvfp4_every_code_file(shift))
+def test_nvfp4_every_nibble_every_block_scale(shift, storage):
+    assert_parity(nvfp4_every_code_file(shift, storage))
 
 
 @pytest.mark.parametrize("M,N", [(300, 200), (5, 1), (130, 7), (257, 129), (128, 4096), (1, 16), (129, 48)])
