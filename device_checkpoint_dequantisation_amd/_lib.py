@@ -106,6 +106,7 @@ SIGNATURES = {
     "st_index_traffic_bytes": (C.c_uint64, [C.c_void_p]),
     "st_index_device_bytes": (C.c_uint64, [C.c_void_p]),
     "st_index_table": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
+    "st_index_descs": (C.c_void_p, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "st_index_table_subset": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_void_p, C.c_size_t,
                                         C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
     "st_index_table_slices": (C.c_int, [C.c_void_p, C.POINTER(Slice), C.c_size_t, C.c_void_p, C.c_size_t,

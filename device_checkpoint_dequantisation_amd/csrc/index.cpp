@@ -1024,6 +1024,13 @@ extern "C" const void* st_index_table(const st_index* idx, size_t* bytes, uint64
     return idx->table.data();
 }
 
+extern "C" const void* st_index_descs(const st_index* idx, size_t* n, size_t* bytes) {
+    uint64_t units = 0;
+    const void* t = st_index_table(idx, bytes, &units);
+    if (n) *n = t ? size_t(units) : 0;
+    return t;
+}
+
 extern "C" st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t k, void* dst,
                                            size_t dst_bytes, size_t* bytes, uint64_t* units) {
     st_clear();

@@ -170,63 +170,110 @@ typedef struct st_plan_opts {
 typedef struct st_index st_index;   /* opaque, host memory, owned by the library */
 
 /* Human-readable description of the last error on the calling thread ("" if none).  Valid
- * until the next stmat call on the same thread. */
+ * until the next stmat call on the same thread.  Messages name the tensor, the field and the
+ * measured values: the pages' loader fails with the measured free and total memory rather than
+ * attempting an unsafe load ("Resident Modal LLM Architecture", "Residency And Memory") and stops
+ * with a hard error that says what to change when a requested read path is unavailable ("Disk
+ * tier safetensors streaming design audit", "Strategy summary / Range reads and tiering"). */
 const char* st_last_error(void);
 
 /* From the first 8 bytes of a file, the number of bytes the header occupies (8 + N).
- * Fails with ST_E_HEADER if N exceeds ST_HEADER_CAP. */
+ * Fails with ST_E_HEADER if N exceeds ST_HEADER_CAP.  The header alone carries every tensor's
+ * dtype, shape and data offsets ("Disk tier safetensors streaming design audit", "FastSageTensors
+ * capability audit": header parsing and metadata); this is how much of the file to read for it. */
 st_status st_header_size(const void* first8, uint64_t* header_bytes);
 
 /* Build the metadata-only index from the first header_len bytes of a safetensors file of
  * file_size bytes (header_len >= 8 + N; extra bytes are ignored).  Parses and validates the
  * header, checks that the data_offsets tile the data section exactly, pairs quantised weights
  * with their scales, and plans the device descriptor table.  No tensor byte is read.
- * Fails (and sets *out = NULL) on any malformed header; see st_status. */
+ * Fails (and sets *out = NULL) on any malformed header; see st_status.
+ * Source: the SafeTensorIndex / TensorMeta of "Disk tier safetensors streaming design audit",
+ * "Strategy summary / Streaming safetensors mapping" (metadata-only parsing, no full dict
+ * materialisation); the scale pairing covers the checkpoint families of "Resident Modal LLM
+ * Architecture", "Current Backend Boundary" (Qwen block-FP8, ModelOpt NVFP4) and the scaled-FP8
+ * conversion of the design audit's "Mandatory research audit". */
 st_status st_index_build(const void* header_bytes, uint64_t header_len, uint64_t file_size,
                          const st_plan_opts* opts, st_index** out);
 
-/* st_index_build on the header of the file at `path` (reads only 8 + N bytes). */
+/* st_index_build on the header of the file at `path` (reads only 8 + N bytes).  ST_E_IO if the
+ * file cannot be opened or read.  Source: as st_index_build (metadata read without loading a
+ * tensor). */
 st_status st_index_open(const char* path, const st_plan_opts* opts, st_index** out);
 
+/* Frees an index and everything it owns (names, tables); NULL is a no-op. */
 void st_index_free(st_index* idx);
 
+/* The byte ranges a load reads: only the data section, never the header twice ("Disk tier
+ * safetensors streaming design audit", "Strategy summary / Range reads and tiering": read only
+ * the tensor range).  Both return 0 for a NULL index. */
 uint64_t st_index_data_offset(const st_index* idx);   /* 8 + N: file offset of the data section */
 uint64_t st_index_data_size(const st_index* idx);     /* bytes of the data section */
 /* Bytes to allocate for the device blob: data size plus 64, rounded up to a multiple of 256.
  * The kernel reads whole aligned words, which may reach a few bytes past the data, so the
  * padding must be present. */
 uint64_t st_index_blob_bytes(const st_index* idx);
+/* Header entries, read from the metadata alone: per tensor its name, dtype, shape and data
+ * offsets ("Disk tier safetensors streaming design audit", "FastSageTensors capability audit":
+ * a per-tensor frame of dtype, shape and data_offsets with no tensor allocated; "Strategy
+ * summary / Streaming safetensors mapping": metadata-only keys).  st_index_tensor fails with
+ * ST_E_ARG for a NULL pointer or i >= st_index_count. */
 size_t st_index_count(const st_index* idx);           /* header entries (tensors) */
 st_status st_index_tensor(const st_index* idx, size_t i, st_tensor_meta* out);
 /* Index of the header entry called `name`, or -1. */
 int64_t st_index_find(const st_index* idx, const char* name);
-/* The header's __metadata__ as a JSON object text ("{}" if absent); valid for the index's lifetime. */
+/* The header's __metadata__ as a JSON object text ("{}" if absent); valid for the index's lifetime.
+ * The design audit asks for metadata returned without loading tensors ("Disk tier safetensors
+ * streaming design audit", "Pipeline refactors"). */
 const char* st_index_metadata_json(const st_index* idx);
 
+/* The outputs: every weight after scale pairing, with its kind (bf16 copy, fp16/fp32 cast,
+ * scaled FP8, block FP8, NVFP4, MXFP8, MXFP4) and logical shape, in output order.  The quantised
+ * kinds are the checkpoint families of "Resident Modal LLM Architecture", "Current Backend
+ * Boundary" and of the design audit's "Mandatory research audit".  st_index_output fails with
+ * ST_E_ARG for a NULL pointer or k >= st_index_num_outputs. */
 size_t st_index_num_outputs(const st_index* idx);
 st_status st_index_output(const st_index* idx, size_t k, st_output_info* out);
 /* The output element type the index plans for (st_plan_opts.flags). */
 uint32_t st_index_out_dtype(const st_index* idx);
 /* Byte offset of output k inside one output arena in which every output starts on a
- * 256-byte boundary, and the arena's total size (2 or 4 bytes per element). */
+ * 256-byte boundary, and the arena's total size (2 or 4 bytes per element).  The arena is
+ * framework-allocated memory that the outputs view ("Disk tier safetensors streaming design
+ * audit", "FastSageTensors capability audit": torch interop allocates tensor memory and wraps raw
+ * pointers as tensors).  0 for a NULL index or k out of range. */
 uint64_t st_index_output_offset(const st_index* idx, size_t k);
 uint64_t st_index_output_arena_bytes(const st_index* idx);
 /* Bytes read + bytes written by materialising every output (the data section plus 2 or 4
- * bytes per output element). */
+ * bytes per output element): the byte count a throughput figure for the decode divides.  The
+ * pages publish no such figure; this is the algorithmic traffic, not a counter reading. */
 uint64_t st_index_traffic_bytes(const st_index* idx);
 /* Device memory the whole load needs: blob + work table + pointer array + arena.
- * Compare with the free device memory before allocating; the requirement is arithmetic. */
+ * Compare with the free device memory before allocating; the requirement is arithmetic.  The
+ * pages' loader checks the free memory before a load and fails with the measured free and total
+ * figures ("Resident Modal LLM Architecture", "Residency And Memory"), and decides admission by
+ * arithmetic it owns ("VRAM co-management across processes", "The WDDM position", current
+ * position).  0 for a NULL index. */
 uint64_t st_index_device_bytes(const st_index* idx);
 
 /* The work table for every output (descriptor k writes outs[k]), host memory owned by the
  * index.  *bytes = table size, *units = work units (the `n` st_materialize takes); either
- * pointer may be NULL. */
+ * pointer may be NULL.  NULL for a NULL index.  Source: the descriptor table the metadata-only
+ * index hands to the device ("Disk tier safetensors streaming design audit", "Strategy summary /
+ * Streaming safetensors mapping"). */
 const void* st_index_table(const st_index* idx, size_t* bytes, uint64_t* units);
+/* The same table as st_index_table, in the argument order (index, n, bytes): *n receives the
+ * table's work-unit count, the `n` that st_materialize takes (the launch is one wavefront per
+ * unit, so a unit count, not a descriptor count, sizes it); *bytes the table size.  Either
+ * pointer may be NULL; NULL for a NULL index. */
+const void* st_index_descs(const st_index* idx, size_t* n, size_t* bytes);
 
 /* A self-contained work table for a subset of outputs: sel[0..k) are output indices (any
  * order; repeats allowed); descriptor j writes outs[j], so outs[j] must point to output sel[j].
  * With dst == NULL only *bytes and *units are set (a size query); otherwise dst_bytes must be
- * at least that size.  Used for on-demand loads of single tensors. */
+ * at least that size.  ST_E_ARG for an index out of range or dst too small.  Used for on-demand
+ * loads of single tensors ("Disk tier safetensors streaming design audit", "Strategy summary /
+ * Streaming safetensors mapping": loading tensors on demand; "Tests and docs": single-tensor
+ * loading). */
 st_status st_index_table_subset(const st_index* idx, const uint32_t* sel, size_t k, void* dst,
                                 size_t dst_bytes, size_t* bytes, uint64_t* units);
 
@@ -254,7 +301,8 @@ typedef struct {
  * bounds, ST_E_SHAPE for a cut that splits a scale block or a column slice too large. */
 st_status st_index_table_slices(const st_index* idx, const st_slice* slices, size_t k, void* dst,
                                 size_t dst_bytes, size_t* bytes, uint64_t* units);
-/* Elements of slice `s` once its bounds are resolved (rows * cols), or ST_E_ARG. */
+/* Elements of slice `s` once its bounds are resolved (rows * cols), or ST_E_ARG.  Source: as the
+ * slices above (slicing metadata). */
 st_status st_index_slice_numel(const st_index* idx, const st_slice* s, uint64_t* rows, uint64_t* cols);
 
 /* Stage the data section of the file at `path` into `blob_dev` (device memory of at least
@@ -263,8 +311,14 @@ st_status st_index_slice_numel(const st_index* idx, const st_slice* s, uint64_t*
  * chunks) and copies each chunk with hipMemcpyAsync on `side_stream`; records `done_event`
  * (may be NULL) on that stream after the last copy.  Returns once every read is done and every
  * copy is enqueued; the pinned buffer must stay allocated until done_event completes.
+ * A later st_stage_file or st_stream_file call given the same pinned buffer first waits (on the
+ * host) for this call's copies out of it, so a caller may reuse the buffer at once.
  * If `seconds_read` is not NULL it receives
- * the wall time spent in file reads (for a file -> pinned rate). */
+ * the wall time spent in file reads (for a file -> pinned rate).
+ * Errors: ST_E_ARG (null pointers, pinned buffer too small, misaligned blob), ST_E_IO (open, size
+ * or read failure), ST_E_HIP (a copy or event).
+ * Source: "Disk tier safetensors streaming design audit", "Strategy summary / Range reads and
+ * tiering" (Disk->RAM->GPU: read the range into pinned CPU memory, copy it to the GPU). */
 st_status st_stage_file(const char* path, const st_index* idx, void* blob_dev, void* pinned,
                         size_t pinned_bytes, void* side_stream, void* done_event,
                         double* seconds_read);
@@ -308,13 +362,16 @@ typedef struct {
 
 /* Plan the streaming load of every output of `idx` in steps of at most chunk_bytes (>= 64 KiB).
  * Every byte of the data section belongs to exactly one range; every output to exactly one step;
- * the blob is laid out like the data section. */
+ * the blob is laid out like the data section.  ST_E_ARG for a NULL index or a chunk too small.
+ * Source: the range reads and tiering cited above this group. */
 st_status st_stream_plan_build(const st_index* idx, uint64_t chunk_bytes, st_stream_plan** out);
 /* Plan the load of outputs sel[0..k) (distinct indices) only: the ranges cover their weight and
  * scale tensors (plus gaps of at most 4 KiB between file-adjacent ones).  flags: 0 or
  * ST_PLAN_PACK.  Output order within a step follows sel. */
 st_status st_stream_plan_select(const st_index* idx, const uint32_t* sel, size_t k, uint64_t chunk_bytes,
                                 uint32_t flags, st_stream_plan** out);
+/* Accessors of a plan (the plan owns what they return; 0 / NULL for a NULL plan).  Source: the
+ * range reads and tiering cited above this group. */
 void      st_stream_plan_free(st_stream_plan* plan);
 uint64_t  st_stream_plan_chunk_bytes(const st_stream_plan* plan);
 /* Bytes of the device blob the plan's tables address (ST_BLOB_ALIGN-aligned allocation). */
@@ -341,7 +398,8 @@ typedef struct {
 /* Stream the file at `path` through `plan`: for each step, read its ranges into a slot of the
  * pinned ring (pinned_bytes >= 4 * chunk_bytes; four slots), copy each to blob_dev + dst with
  * hipMemcpyAsync on `side_stream`, make `compute_stream` wait for those copies and enqueue
- * st_materialize over the step's table on `compute_stream`.
+ * st_materialize over the step's table on `compute_stream`.  A later call given the same pinned
+ * buffer first waits (on the host) for this call's copies out of it.
  *   blob_dev    st_stream_plan_blob_bytes bytes, ST_BLOB_ALIGN-aligned
  *   tables_dev  device copy of st_stream_plan_tables, 64-byte aligned
  *   outs_dev    device array of output pointers in plan order (see st_stream_plan_order)
@@ -359,8 +417,11 @@ st_status st_stream_file(const char* path, const st_index* idx, const st_stream_
 /* Read every range of `plan` from the file at `path` into host memory: range r lands at
  * host_blob + dst.  host_bytes must be at least st_stream_plan_blob_bytes(plan); bytes no range
  * covers are left as they are.  Uploading host_blob (one copy) and launching the plan's tables
- * then decodes the plan's outputs without touching the file again (a RAM tier).  Synchronous;
- * no GPU calls.  If `seconds_read` is not NULL it receives the wall time of the reads. */
+ * then decodes the plan's outputs without touching the file again (a RAM tier: "Disk tier
+ * safetensors streaming design audit", "Disk tier integration", an LRU of RAM-resident weights
+ * with a byte limit).  Synchronous; no GPU calls.  If `seconds_read` is not NULL it receives the
+ * wall time of the reads.  Errors: ST_E_ARG (null pointers, buffer too small, plan of another
+ * index), ST_E_IO (open, size or read failure). */
 st_status st_read_plan(const char* path, const st_index* idx, const st_stream_plan* plan, void* host_blob,
                        size_t host_bytes, double* seconds_read);
 /* st_read_plan for n plans of the same index at once (one pool of reader threads): plan j's
@@ -369,6 +430,10 @@ st_status st_read_plans(const char* path, const st_index* idx, const st_stream_p
                         void* const* host_blobs, const size_t* host_bytes, size_t n, double* seconds_read);
 
 /* Enqueue the grouped materialise kernel on `stream` (hipStream_t; NULL = default stream).
+ * It turns the staged bytes of every descriptor into compute-dtype tensors: the checkpoint
+ * families of "Resident Modal LLM Architecture", "Current Backend Boundary" (Qwen block-FP8,
+ * ModelOpt NVFP4) and the scaled-FP8 checkpoints of the design audit's "Mandatory research
+ * audit", each element as defined at the top of this header.
  *   blob   device copy of the data section (st_index_blob_bytes bytes, ST_BLOB_ALIGN-aligned)
  *   descs  device copy of a work table (st_index_table / st_index_table_subset), 64-byte aligned
  *   n      the table's work-unit count (returned with the table); the launch is one 64-lane
@@ -392,7 +457,8 @@ st_status st_materialize_slices(const void* blob, const void* descs, size_t n, v
 
 #define ST_MAT_SLICES 1u     /* st_materialize_as: the instance with the strided column-slice path */
 
-/* The general entry point: st_materialize for a table planned with output type out_dtype
+/* The general entry point (source: as st_materialize): st_materialize for a table planned with
+ * output type out_dtype
  * (st_out_dtype; outs then point to arrays of that type, aligned to it), flags 0 or
  * ST_MAT_SLICES.  One kernel instance per output type: a table planned for another type than
  * out_dtype makes every wavefront return without writing.  ST_E_ARG for an unknown type or
