@@ -18,8 +18,8 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, Desc, OutputInfo, PlanOpts, Slice,  # noqa: F401
-                   StError, StreamStats, StreamStep, TensorMeta, check, lib)
+from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, TABLE_MAGIC, Desc, OutputInfo,  # noqa: F401
+                   PlanOpts, Slice, StError, StreamStats, StreamStep, TableHeader, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
            "stage_file", "stream_file", "read_plans", "StError", "KINDS", "QUANTIZED_KINDS"]
@@ -287,6 +287,20 @@ def _torch():
     return torch
 
 
+def check_table(raw: bytes, units: int, out_dtype: str):
+    """Raise ValueError unless the host copy ``raw`` of a work table records ``units`` work units
+    and the output type ``out_dtype``: the kernel would leave every output unwritten otherwise."""
+    if len(raw) < 64:
+        raise ValueError(f"work table of {len(raw)} bytes has no header")
+    h = TableHeader.from_buffer_copy(bytes(raw[:64]))
+    if h.magic != TABLE_MAGIC:
+        raise ValueError(f"not a work table (magic 0x{h.magic:08x})")
+    if h.units != units:
+        raise ValueError(f"work table holds {h.units} units, the launch was given {units}")
+    if h.out_dtype >= len(OUT_DTYPES) or OUT_DTYPES[h.out_dtype] != out_dtype:
+        raise ValueError(f"work table was planned for output type code {h.out_dtype}, the launch asks for {out_dtype}")
+
+
 def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> float:
     """Copy the file's data section into ``blob`` (device uint8 tensor of index.blob_bytes) through
     the pinned uint8 host tensor ``pinned`` on ``side_stream``; returns seconds spent reading."""
@@ -413,6 +427,7 @@ class DeviceCheckpoint:
                 raise MemoryError(f"checkpoint needs {need} bytes of device memory; {free} of {total} are free")
         self.blob = torch.empty(index.blob_bytes, dtype=torch.uint8, device=self.device)
         table, units = index.table()
+        check_table(table, units, index.out_dtype)
         self.units = units
         self.table = torch.frombuffer(bytearray(table), dtype=torch.uint8).to(self.device)
         dt = index.torch_dtype
@@ -430,9 +445,13 @@ class DeviceCheckpoint:
             self.stage(path, pinned_mb)
 
     def stage(self, path: str, pinned_mb: int = 256):
+        """Copy the file's data section into the blob (returns once the copy is complete).  Work
+        already enqueued on the current stream (an earlier decode reading the blob) runs first."""
         torch = _torch()
+        self.synchronize()
         pinned = torch.empty(max(2, pinned_mb) << 20, dtype=torch.uint8, pin_memory=True)
         side = torch.cuda.Stream(self.device)
+        side.wait_stream(torch.cuda.current_stream(self.device))
         self.stage_seconds_read = stage_file(path, self.index, self.blob, pinned, side)
         side.synchronize()
         del pinned
@@ -443,6 +462,7 @@ class DeviceCheckpoint:
         Returns the pipeline's statistics once everything is enqueued; the outputs are ready when
         ``stream`` reaches this point (the pinned ring is held until then, see ``synchronize``)."""
         torch = _torch()
+        self.synchronize()  # an earlier streamed load's copies may still read the pinned ring
         plan = plan or StreamPlan(self.index, chunk_mb << 20)
         compute = stream if stream is not None else torch.cuda.current_stream(self.device)
         need = 4 * plan.chunk_bytes
@@ -498,17 +518,32 @@ class DeviceCheckpoint:
         shapes = [self.index.slice_shape(*((sl + (None, None))[:3] if isinstance(sl, tuple) else (sl,))) for sl in slices]
         outs = [torch.empty(shp, dtype=self.index.torch_dtype, device=self.device) for shp in shapes]
         raw, units = self.index.table_slices(slices)
+        check_table(raw, units, self.index.out_dtype)
         if strided_kernel is None:
             strided_kernel = self.index.has_column_slices(slices)
         table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
         ptrs = torch.tensor([o.data_ptr() for o in outs] or [0], dtype=torch.int64).to(self.device)
         if units:
-            materialize(self.blob, table, units, ptrs, stream, slices=strided_kernel, out_dtype=self.index.out_dtype)
+            s = self._launch_stream(stream)
+            for t in [table, ptrs] + outs:  # allocated on the current stream, used on s
+                t.record_stream(s)
+            materialize(self.blob, table, units, ptrs, s, slices=strided_kernel, out_dtype=self.index.out_dtype)
         return outs
+
+    def _launch_stream(self, stream):
+        """The stream a decode runs on: ``stream``, ordered after the work already enqueued on the
+        current stream (uploads, staging), or the current stream itself."""
+        torch = _torch()
+        cur = torch.cuda.current_stream(self.device)
+        if stream is None or stream == cur:
+            return cur
+        stream.wait_stream(cur)
+        return stream
 
     def materialize(self, stream=None):
         if self.units:
-            materialize(self.blob, self.table, self.units, self.outs, stream, out_dtype=self.index.out_dtype)
+            materialize(self.blob, self.table, self.units, self.outs, self._launch_stream(stream),
+                        out_dtype=self.index.out_dtype)
         return self.tensors
 
 

@@ -5,7 +5,8 @@
 // to the GPU and release the host buffer.  Byte ranges are read by a few threads into a ring
 // carved from the caller's pinned buffer, and each slot is copied with hipMemcpyAsync on a side
 // stream while the next one is being read.  An event per ring slot keeps a slot from being
-// overwritten before its copy has finished.
+// overwritten before its copy has finished, and an event per caller buffer keeps the next call
+// from reading into a ring that the previous call's copies are still reading.
 //  * st_stage_file: the whole data section, in slot-sized chunks.
 //  * st_stream_file: the steps of a stream plan; after each step's copies the compute stream waits
 //    for them and decodes the outputs the step completes, so decoding overlaps later reads and
@@ -198,6 +199,84 @@ struct RingEvents {
     }
 };
 
+// Copies still reading a caller's pinned buffer when a call returns.  st_stage_file and
+// st_stream_file return once their copies are enqueued, so the side stream may still be reading
+// the ring; a later call handed the same buffer must not read the file into it before then.  Each
+// call records an event on its side stream after its last copy and files it under the buffer's
+// address range; the next call whose buffer overlaps that range waits for the event on the host
+// before its first read.  Entries are few (one per ring a process uses); past kMaxEntries the
+// oldest is waited for and dropped.
+class PinnedInFlight {
+  public:
+    static PinnedInFlight& get() {
+        static PinnedInFlight* p = new PinnedInFlight();  // never destroyed: events outlive static teardown
+        return *p;
+    }
+    // Waits for every recorded copy out of [base, base + bytes).
+    st_status wait(const void* base, size_t bytes, const char* who) {
+        std::vector<hipEvent_t> evs;
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            for (size_t i = 0; i < v_.size();) {
+                if (overlaps(v_[i], base, bytes)) {
+                    evs.push_back(v_[i].ev);
+                    v_.erase(v_.begin() + long(i));
+                } else {
+                    ++i;
+                }
+            }
+        }
+        st_status r = ST_OK;
+        for (hipEvent_t e : evs) {
+            if (hipEventSynchronize(e) != hipSuccess && r == ST_OK)
+                r = st_fail(ST_E_HIP, "%s: waiting for an earlier call's copies out of the pinned buffer failed", who);
+            (void)hipEventDestroy(e);
+        }
+        return r;
+    }
+    // Records the point after the last copy out of [base, base + bytes) on `side`; if no event can
+    // be recorded there, waits for the stream instead.
+    void record(const void* base, size_t bytes, hipStream_t side) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            (void)hipStreamSynchronize(side);
+            return;
+        }
+        if (hipEventRecord(e, side) != hipSuccess) {
+            (void)hipEventDestroy(e);
+            (void)hipStreamSynchronize(side);
+            return;
+        }
+        hipEvent_t oldest = nullptr;
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            v_.push_back(Entry{static_cast<const char*>(base), bytes, e});
+            if (v_.size() > kMaxEntries) {
+                oldest = v_.front().ev;
+                v_.erase(v_.begin());
+            }
+        }
+        if (oldest) {
+            (void)hipEventSynchronize(oldest);
+            (void)hipEventDestroy(oldest);
+        }
+    }
+
+  private:
+    struct Entry {
+        const char* base;
+        size_t bytes;
+        hipEvent_t ev;
+    };
+    static bool overlaps(const Entry& x, const void* base, size_t bytes) {
+        const char* b = static_cast<const char*>(base);
+        return x.base < b + bytes && b < x.base + x.bytes;
+    }
+    static constexpr size_t kMaxEntries = 64;
+    std::mutex m_;
+    std::vector<Entry> v_;
+};
+
 double seconds_since(std::chrono::steady_clock::time_point t0) {
     return std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
 }
@@ -216,6 +295,7 @@ extern "C" st_status st_stage_file(const char* path, const st_index* idx, void* 
     FileFd file;
     st_status status = open_checked(path, idx, file);
     if (status != ST_OK) return status;
+    if ((status = PinnedInFlight::get().wait(pinned, pinned_bytes, "st_stage_file")) != ST_OK) return status;
     RingEvents ring;
     if ((status = ring.create()) != ST_OK) return status;
     Readers pool;
@@ -248,6 +328,7 @@ extern "C" st_status st_stage_file(const char* path, const st_index* idx, void* 
     if (status == ST_OK && done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), stream) != hipSuccess)
         status = st_fail(ST_E_HIP, "st_stage_file: hipEventRecord failed");
     if (status != ST_OK) (void)hipStreamSynchronize(stream);  // nothing may still read the ring
+    else PinnedInFlight::get().record(pinned, pinned_bytes, stream);
     if (seconds_read) *seconds_read = t_read;
     return status;
 }
@@ -276,6 +357,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     FileFd file;
     st_status status = open_checked(path, idx, file);
     if (status != ST_OK) return status;
+    if ((status = PinnedInFlight::get().wait(pinned, pinned_bytes, "st_stream_file")) != ST_OK) return status;
     RingEvents ring;
     if ((status = ring.create()) != ST_OK) return status;
     Readers pool;
@@ -347,6 +429,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     if (status == ST_OK && done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), compute) != hipSuccess)
         status = st_fail(ST_E_HIP, "st_stream_file: hipEventRecord failed");
     if (status != ST_OK) (void)hipStreamSynchronize(side);  // nothing may still read the ring
+    else PinnedInFlight::get().record(pinned, pinned_bytes, side);
     if (stats) *stats = st;
     return status;
 }

@@ -228,6 +228,7 @@ class StreamStateDict(Mapping):
         self.ram = RamCache(ram_cache_bytes)
         self.stats = collections.Counter()
         self._ring = None   # pinned staging ring of the direct path
+        self._ring_free = None  # event after the last copy out of the ring
         self._side = None   # its copy stream
         self._stage = None  # pinned buffer for small uploads
         self._stage_done = None
@@ -300,6 +301,8 @@ class StreamStateDict(Mapping):
         plan = StreamPlan(self.index, chunk, select=ks, pack=True)
         need = 4 * plan.chunk_bytes
         if self._ring is None or self._ring.numel() < need:
+            if self._ring_free is not None:  # the old ring's last copies must be done before it is freed
+                self._ring_free.synchronize()
             self._ring = torch.empty(max(need, 4 << 20), dtype=torch.uint8, pin_memory=True)
         if self._side is None:
             self._side = torch.cuda.Stream(self.device)
@@ -316,6 +319,8 @@ class StreamStateDict(Mapping):
         self.stats["file_bytes"] += st["bytes_read"]
         self.stats["launches"] += st["launches"]
         blob.record_stream(self._side)
+        self._ring_free = torch.cuda.Event()
+        self._ring_free.record(self._side)  # after this load's last copy out of the ring
 
     def _load_cached(self, metas, outs, s):
         """Per-output packed entries, read from the file once and then kept in the RAM tier."""
