@@ -1,16 +1,19 @@
-"""GPU parity at the benchmark's full checkpoint sizes and at maximum sizes, in the launch
-configuration bench.py times (one st_materialize over the whole staged blob).
+"""GPU parity at full checkpoint sizes and at maximum sizes, in the launch configuration bench.py
+times (one st_materialize over the whole staged blob).  The five benchmark checkpoints are compared
+with the oracle element by element in full in test_gpu_fullsize_oracle.py; here:
 
-* Every output is checked against the CPU oracle on sampled elements the oracle computes one by
-  one: first, last, row and 128-block boundaries, and random positions.
+* The MXFP8 and MXFP4 checkpoints at full size: every output is checked against the CPU oracle on
+  sampled elements the oracle computes one by one: first, last, row and 128-block boundaries, and
+  random positions.
 * A spread of the quantised outputs is also checked whole against an independent GPU computation of
   the same definition with torch (float8_e4m3fn decode, fp32 products in the pages' order, RNE cast
   to bfloat16). The generated checkpoints hold no NaN code, where torch's NaN bits would differ.
 * The fp16 and fp32 kernel instances at full size (scaled FP8, block FP8, NVFP4, MXFP4): sampled
   elements against the oracle's rounding to that type, whole quantised outputs against torch.
 * Maximum sizes (index built from the header alone, blob filled on the GPU): a bf16 tensor of more
-  than 2^32 elements, a 128-block FP8 tensor just under the 2^32-element limit, and a per-tensor
-  FP8 tensor whose source starts unaligned and ends past 2^31 bytes.
+  than 2^32 elements, a 128-block FP8 tensor just under the 2^32-element limit, a per-tensor
+  FP8 tensor whose source starts unaligned and ends past 2^31 bytes, and a checkpoint of more than
+  2^24 work units, whose launch needs more than 2^22 workgroups and so a second grid row.
 """
 import os
 
@@ -88,7 +91,7 @@ def _torch_f32(kind, shape, blob, src, scale, scale2):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("k", [6, 7])
 def test_full_size_checkpoint(k, tmp_path):
     path = str(tmp_path / f"c{k}.safetensors")
     print(f"full-size config {k}: writing", flush=True)
@@ -269,5 +272,64 @@ def test_scaled_fp8_unaligned_beyond_2_31_bytes():
             end = min(size, start + (1 << 28))
             ref = (_e4m3(ck.blob[b + start: b + end]) * s).to(torch.bfloat16)
             assert torch.equal(out[start:end].view(torch.int16), ref.view(torch.int16)), f"{name} {start}:{end}"
+    del ck
+    torch.cuda.empty_cache()
+
+
+def test_launch_beyond_2_22_workgroups():
+    """Five per-tensor FP8 tensors of 2^32 elements each (the last one 777 elements longer, starting
+    off its 8-byte word): 20,971,521 work units of 1024 elements, 5,242,881 workgroups, so the grid
+    takes a second row (its first holds 2^22 workgroups).  Every element is checked in bands
+    against torch's e4m3 decode times the scale rounded to bf16, and sampled elements of every
+    tensor against the oracle."""
+    n = 1 << 32
+    sizes = [n, n, n, n, n + 777]
+    names = [f"b{i}" for i in range(5)]
+    spec = []
+    for nm, size in zip(names, sizes):
+        spec += [(f"{nm}.weight", "F8_E4M3", (size,)), (f"{nm}.scale_weight", "F32", ())]
+    scales = [0.001 * (i + 1) + 0.0007 for i in range(5)]
+    print(f"grid beyond 2^22 workgroups: 5 scaled-FP8 tensors, {sum(sizes)} elements", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+
+    def fill(blob, offs):
+        for nm, sc in zip(names, scales):
+            _random_bytes(blob[slice(*offs[f"{nm}.weight"])], gen, no_nan_e4m3=True)
+            blob[slice(*offs[f"{nm}.scale_weight"])].copy_(torch.tensor([sc], device=DEV).view(torch.uint8))
+
+    ck, lay = _staged_from_header(spec, fill)
+    assert ck.units > 1 << 24, ck.units
+    assert -(-ck.units // 4) > 1 << 22
+    ck.materialize()
+    torch.cuda.synchronize()
+    band = 1 << 28
+    for nm, size in zip(names, sizes):
+        b, _ = lay.offsets[f"{nm}.weight"]
+        s = _f32(ck.blob, lay.offsets[f"{nm}.scale_weight"][0], 1)
+        out = ck.tensors[f"{nm}.weight"]
+        for start in range(0, size, band):
+            end = min(size, start + band)
+            ref = (_e4m3(ck.blob[b + start: b + end]) * s).to(torch.bfloat16)
+            assert torch.equal(out[start:end].view(torch.int16), ref.view(torch.int16)), f"{nm} {start}:{end}"
+    # sampled elements against the oracle, from the header and the bytes around each sample
+    h = oracle.parse_header(lay.header)
+    outs = {o.name: o for o in oracle.classify(h)}
+    rng = np.random.default_rng(22)
+    checked = 0
+    for nm, size in zip(names, sizes):
+        o = outs[f"{nm}.weight"]
+        idx = np.unique(np.concatenate([[0, size - 1, size - 777, (1 << 32) - 1], rng.integers(0, size, 4096)]))
+        idx = idx[idx < size]
+        lo = o.src.begin
+        codes = ck.blob[lo + torch.from_numpy(idx).to(DEV)].cpu().numpy()
+        data = np.zeros(o.scale.end, dtype=np.uint8)   # the data section, sparse: sampled codes + the scale
+        data[lo + idx] = codes
+        data[o.scale.begin: o.scale.end] = ck.blob[o.scale.begin: o.scale.end].cpu().numpy()
+        want = oracle.decode(o, data, idx)
+        got = ck.tensors[o.name][torch.from_numpy(idx).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), o.name
+        checked += idx.size
+    print(f"grid beyond 2^22 workgroups: {ck.units} units, bands exact, {checked} sampled elements equal the oracle",
+          flush=True)
     del ck
     torch.cuda.empty_cache()
