@@ -175,3 +175,51 @@ def _forward_ref(want, p, x):
                 + lin(h, w("attn.v.weight"), w("attn.v.bias")), w("attn.o.weight"), w("attn.o.bias"))
     h = h * w("norm2.weight")
     return h + lin(torch.relu(lin(h, w("mlp.up.weight"))), w("mlp.down.weight"), w("mlp.down.bias"))
+
+
+def _busy(ms_target=300):
+    """Keep the current stream busy for a while with matrix products (fp32, no transposed views)."""
+    a = torch.randn(4096, 4096, device=DEV)
+    for _ in range(max(1, ms_target // 2)):
+        a = torch.mm(a, a) * 1e-3
+    return a
+
+
+def test_back_to_back_loads_behind_a_busy_stream(tmp_path):
+    """The side stream's copies wait for the compute stream, so with a busy compute stream the first
+    load's copies out of the pinned ring are still queued when it returns; the second load must not
+    read the file into that ring before they have run.  Several keys per load, so every load spans
+    several ring steps; no synchronisation between the loads."""
+    path, buf = _file(tmp_path, 2)
+    want = oracle.materialize(buf)
+    sd = st.StreamStateDict(path, DEV, steps_per_load=8)
+    names = list(sd)
+    half = len(names) // 2
+    first, second = names[:half], names[half:]
+    print(f"back-to-back loads: {len(first)} + {len(second)} keys behind a busy stream", flush=True)
+    busy = _busy()
+    got1 = sd.load(first)
+    got2 = sd.load(second)
+    busy = _busy(100)
+    got3 = sd.load(first[::-1])                   # and once more through a larger ring
+    torch.cuda.synchronize()
+    del busy
+    for got in (got1, got2, got3):
+        for name, t in got.items():
+            assert np.array_equal(_bits(t).reshape(want[name].shape), want[name]), name
+
+
+def test_device_checkpoint_restream_behind_a_busy_stream(tmp_path):
+    """DeviceCheckpoint.stream twice on the same pinned ring and arena, the second call made while the
+    first one's copies wait behind a busy compute stream."""
+    path, buf = _file(tmp_path, 4)
+    want = oracle.materialize(buf)
+    ix = st.SafeTensorIndex.open(path)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    busy = _busy()
+    ck.stream(path, chunk_mb=1)
+    ck.stream(path, chunk_mb=1)
+    ck.synchronize()
+    del busy
+    for name, w in want.items():
+        assert np.array_equal(_bits(ck.tensors[name]).reshape(w.shape), w), name
