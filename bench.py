@@ -3,11 +3,13 @@
 One step = one st_materialize launch over every descriptor of a seeded synthetic checkpoint whose
 blob is already resident in HBM (staging is measured separately).  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--all] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--configs 2,3,4,5] [--all] [--no-cpu]
 
-Default workload: the scaled-FP8 DiT-style checkpoint (57 blocks of e4m3fn weights with per-tensor
-fp32 scales plus bf16 vectors).  ``--all`` adds the other checkpoint families (including the MXFP8
-and MXFP4 ones) to the line under "formats".
+By default every benchmark family is timed in one run: the scaled-FP8 DiT checkpoint (c2), the
+block-FP8 LLM checkpoint (c3), the NVFP4 checkpoint (c4) and the many-small-tensor blob (c5), each
+with its own roofline fraction under "formats".  The headline ``value`` and ``roofline`` are the
+NVFP4 checkpoint's, the largest of them (26.87 GB of traffic per launch).  ``--all`` adds the tiny
+blob and the MXFP8 / MXFP4 checkpoints.
 """
 from __future__ import annotations
 
@@ -70,13 +72,57 @@ def profiled_traffic(k):
     return traffic if sha == h.hexdigest() else None
 
 
+def pinned_to_device(blob, nbytes, piece=1 << 30, reps=3):
+    """Host-to-device copy rate on its own: one pinned buffer (touched beforehand) copied into the
+    blob piece by piece with hipMemcpyAsync on a side stream, timed with events on that stream."""
+    import torch
+    n = min(piece, nbytes)
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    host.fill_(0x3C)
+    side = torch.cuda.Stream(blob.device)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            a.record(side)
+            for off in range(0, nbytes, n):
+                m = min(n, nbytes - off)
+                blob[off: off + m].copy_(host[:m], non_blocking=True)
+            b.record(side)
+        side.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del host
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def drop_page_cache(path):
+    """Ask the kernel to evict the file's pages from the page cache (fsync, then
+    POSIX_FADV_DONTNEED); True if the request was accepted.  The eviction is advisory."""
+    try:
+        fd = os.open(path, os.O_RDONLY)
+        try:
+            os.fsync(fd)
+            os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+        finally:
+            os.close(fd)
+        return True
+    except (OSError, AttributeError):
+        return False
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
-    ap.add_argument("--all", action="store_true", help="also measure the other checkpoint families")
+    ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS),
+                    help="the headline workload (value, roofline, cpu_baseline)")
+    ap.add_argument("--configs", default="2,3,4,5",
+                    help="comma-separated families timed beside the headline (empty: the headline only)")
+    ap.add_argument("--all", action="store_true", help="also measure the tiny blob and the MX families")
+    ap.add_argument("--cold-stage", action=argparse.BooleanOptionalAction, default=True,
+                    help="also stage the headline checkpoint after asking the kernel to drop it from the page cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--unit-scale", type=int, default=0)
@@ -140,28 +186,39 @@ def sampled_parity(path, ix, ck, rng, per_output=64, out_dtype="bf16"):
     return True, checked, None
 
 
-def cpu_baseline(path, budget_s):
-    """The oracle as it stands, single-threaded NumPy, on whole outputs in file order until the
-    time budget is spent; GB/s over the same algorithmic bytes (bytes read + bf16 bytes written)."""
+def cpu_baseline(path, budget_s, piece=1 << 20):
+    """The oracle as it stands (single-threaded NumPy) decoding the checkpoint's outputs in file
+    order, in calls of ``piece`` elements, until the time budget is spent; GB/s over the same
+    algorithmic bytes as the kernel (each element's share of its output's read bytes + 2 bytes
+    written).  Scale tensors count with the output they belong to."""
     import oracle
     mm = np.memmap(path, dtype=np.uint8, mode="r")
     h, outs = oracle.plan(mm)
     data = mm[h.data_offset:]
-    nbytes = 0
+    nbytes = 0.0
+    elems = 0
     done = 0
     t0 = time.perf_counter()
     with np.errstate(invalid="ignore", over="ignore"):
         for o in outs:
-            oracle.decode(o, data)
-            nbytes += (o.src.end - o.src.begin) + (o.scale.end - o.scale.begin if o.scale else 0) + \
-                (o.scale2.end - o.scale2.begin if o.scale2 else 0) + 2 * o.numel
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+            read = (o.src.end - o.src.begin) + (o.scale.end - o.scale.begin if o.scale else 0) + \
+                (o.scale2.end - o.scale2.begin if o.scale2 else 0)
+            for a in range(0, o.numel, piece):
+                b = min(o.numel, a + piece)
+                oracle.decode(o, data, np.arange(a, b, dtype=np.int64))
+                nbytes += read * (b - a) / o.numel + 2 * (b - a)
+                elems += b - a
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            else:
+                done += 1
+                continue
+            break
     dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {len(outs)} outputs in file order ({nbytes / 1e9:.3f} GB of traffic) "
-                      f"decoded by the single-threaded NumPy oracle in {dt:.1f}s"}
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"the first {elems:,} output elements in file order ({done} whole outputs of {len(outs)}, "
+                      f"{nbytes / 1e9:.3f} GB of traffic) decoded by the single-threaded NumPy oracle in "
+                      f"{piece:,}-element calls, {dt:.1f}s, on 1 of the host's {os.cpu_count()} CPUs"}
 
 
 def measure(k, d, args, rng, overrides=None):
@@ -184,6 +241,22 @@ def measure(k, d, args, rng, overrides=None):
     read_s = st.stage_file(path, ix, ck.blob, pinned, side)
     side.synchronize()
     stage_s = time.perf_counter() - t0
+    h2d = pinned_to_device(ck.blob, ix.data_size)   # the copy alone, from pinned pages already touched
+    cold = None
+    if k == args.config and args.cold_stage:
+        if drop_page_cache(path):
+            t0 = time.perf_counter()
+            cold_read_s = st.stage_file(path, ix, ck.blob, pinned, side)
+            side.synchronize()
+            cold_s = time.perf_counter() - t0
+            cold = {"file_to_pinned_GBps": round(ix.data_size / cold_read_s / 1e9, 2) if cold_read_s > 0 else None,
+                    "file_to_device_GBps": round(ix.data_size / cold_s / 1e9, 2),
+                    "page_cache": "dropped first (fsync + POSIX_FADV_DONTNEED, advisory)"}
+            log(f"[bench] config {k}: staging after dropping the page cache {ix.data_size / cold_s / 1e9:.2f} GB/s")
+        else:
+            cold = {"page_cache": "could not be dropped on this host"}
+        st.stage_file(path, ix, ck.blob, pinned, side)   # the blob as staged, for the timed decode
+        side.synchronize()
     del pinned
     traffic = ix.traffic_bytes
     log(f"[bench] config {k}: {ix.num_outputs} outputs, traffic {traffic / 1e9:.3f} GB, index {index_ms:.1f} ms, "
@@ -225,12 +298,15 @@ def measure(k, d, args, rng, overrides=None):
         "k": k, "path": path, "traffic": traffic, "read": ix.data_size, "written": traffic - ix.data_size,
         "outputs": ix.num_outputs, "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": float(kms.mean()),
         "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min()), "index_ms": index_ms,
-        "stage": dict({"file_to_pinned_GBps": ix.data_size / read_s / 1e9 if read_s > 0 else None,
-                       "file_to_device_GBps": ix.data_size / stage_s / 1e9,
-                       "file_to_device_first_GBps": ix.data_size / first_stage_s / 1e9,
+        "stage": dict({"file_to_pinned_GBps": round(ix.data_size / read_s / 1e9, 2) if read_s > 0 else None,
+                       "pinned_to_device_GBps": round(h2d, 2),
+                       "file_to_device_GBps": round(ix.data_size / stage_s / 1e9, 2),
+                       "file_to_device_first_GBps": round(ix.data_size / first_stage_s / 1e9, 2),
                        "page_cache": "warm (file just written)",
-                       "pinned_ring": "512 MiB; 'first' includes touching its freshly pinned pages"},
-                      **(load or {})),
+                       "pinned_ring": "512 MiB; 'first' includes touching its freshly pinned pages",
+                       "pinned_to_device": "1 GiB pinned buffer, touched, copied with hipMemcpyAsync on a side "
+                                           "stream and timed with events there (best of 3)"},
+                      **({"cold": cold} if cold else {}), **(load or {})),
         "gen_s": gen_s, "parity": "sampled-bit-exact" if ok else f"MISMATCH:{bad}", "parity_elements": checked,
         "shards": shards, "out_types": types, "flushed": flushed,
     }
@@ -415,6 +491,25 @@ def lazy_loads(path, dev):
     return res
 
 
+def family_line(k, v):
+    """One family's figures for the "formats" object of the bench line."""
+    tr = profiled_traffic(k)
+    d = {"workload": WORKLOADS[k], "GBps": round(v["GBps"], 2), "hbm_peak_frac": round(v["GBps"] / HBM_PEAK_GBPS, 4),
+         "roofline": {"bound": "hbm", "achieved": round(v["kernel_GBps"], 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(v["kernel_GBps"] / HBM_PEAK_GBPS, 4), "traffic": tr,
+                      "traffic_ratio": round(tr / v["traffic"], 4) if tr else None},
+         "kernel_ms": {"mean": round(v["kernel_ms_mean"], 4), "median": round(v["kernel_ms_median"], 4),
+                       "min": round(v["kernel_ms_min"], 4)},
+         "traffic_bytes": v["traffic"], "read_bytes": v["read"], "written_bytes": v["written"], "outputs": v["outputs"],
+         "parity": v["parity"], "parity_elements": v["parity_elements"], "staging": v["stage"]}
+    if v.get("flushed"):
+        fl = v["flushed"]
+        d["flushed_cache"] = {"kernel_ms_median": round(fl["median"], 4),
+                              "GBps": round(v["traffic"] / (fl["median"] * 1e-3) / 1e9, 2),
+                              "hbm_peak_frac": round(v["traffic"] / (fl["median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return d
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -423,11 +518,17 @@ def main():
         sys.exit(2)
     rng = np.random.default_rng(0)
     d = args.tmpdir or tempfile.mkdtemp(prefix="stmat_bench_")
-    configs = [args.config] + ([k for k in sorted(WORKLOADS) if k != args.config] if args.all else [])
+    configs = [int(x) for x in args.configs.split(",") if x.strip()] if args.configs else []
+    if args.all:
+        configs += [k for k in sorted(WORKLOADS) if k not in configs]
+    configs = [args.config] + [k for k in configs if k != args.config]
     results = {}
     cpu = None
     for k in configs:
         results[k] = measure(k, d, args, rng)
+        r = results[k]
+        log(f"[bench] config {k}: {r['GBps']:.1f} GB/s wall, {r['kernel_GBps']:.1f} GB/s by kernel events "
+            f"({r['kernel_GBps'] / HBM_PEAK_GBPS:.3f} of HBM peak), parity {r['parity']}")
         if k == args.config and args.extras:
             results[k]["lazy"] = lazy_loads(results[k]["path"], "cuda:0")
             log(f"[bench] lazy per-layer loads: {results[k]['lazy']}")
@@ -451,18 +552,19 @@ def main():
         torch.cuda.synchronize()
         del a, b
     r = results[args.config]
+    head = family_line(args.config, r)
     line = {
         "metric": METRIC, "value": round(r["GBps"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "read_bytes": r["read"], "written_bytes": r["written"],
-                   "outputs": r["outputs"], "hbm_peak_frac": round(r["GBps"] / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(r["kernel_GBps"], 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(r["kernel_GBps"] / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config)},
+                   "outputs": r["outputs"], "hbm_peak_frac": round(r["GBps"] / HBM_PEAK_GBPS, 4),
+                   "families_timed": [f"c{k}" for k in configs]},
+        "roofline": {k: v for k, v in head["roofline"].items() if k != "traffic_ratio"},
         "cpu_baseline": cpu,
-        "kernel_ms": {"mean": round(r["kernel_ms_mean"], 4), "median": round(r["kernel_ms_median"], 4),
-                      "min": round(r["kernel_ms_min"], 4)},
+        "kernel_ms": head["kernel_ms"],
         "staging": r["stage"], "index_build_ms": round(r["index_ms"], 2), "parity": r["parity"],
+        "formats": {f"c{k}": family_line(k, v) for k, v in results.items()},
     }
     if "lazy" in r:
         line["lazy_loads"] = r["lazy"]
@@ -474,14 +576,6 @@ def main():
         line["scaled_fp8_all_weights_16B_aligned"] = {"GBps": round(aligned["GBps"], 2),
                                                       "kernel_ms_mean": round(aligned["kernel_ms_mean"], 4),
                                                       "parity": aligned["parity"]}
-    if args.all:
-        line["formats"] = {
-            f"c{k}": dict({"GBps": round(v["GBps"], 2), "hbm_peak_frac": round(v["GBps"] / HBM_PEAK_GBPS, 4),
-                           "kernel_ms_mean": round(v["kernel_ms_mean"], 4), "traffic_bytes": v["traffic"],
-                           "parity": v["parity"], "staging": v["stage"]},
-                          **({"flushed_cache": {"kernel_ms_median": round(v["flushed"]["median"], 4),
-                                                "GBps": round(v["traffic"] / (v["flushed"]["median"] * 1e-3) / 1e9, 2)}}
-                             if v.get("flushed") else {})) for k, v in results.items()}
     print(json.dumps(line), flush=True)
 
 
