@@ -22,7 +22,7 @@ from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, TABLE_MAGIC
                    PlanOpts, Slice, StError, StreamStats, StreamStep, TableHeader, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
-           "stage_file", "stream_file", "read_plans", "StError", "KINDS", "QUANTIZED_KINDS"]
+           "materialize_noalloc", "stage_file", "stream_file", "read_plans", "StError", "KINDS", "QUANTIZED_KINDS"]
 
 
 @dataclass(frozen=True)
@@ -321,6 +321,22 @@ def materialize(blob, table, units: int, outs, stream=None, slices: bool = False
     check(lib().st_materialize_as(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
                                   C.c_void_p(outs.data_ptr()), OUT_DTYPES.index(out_dtype), MAT_SLICES if slices else 0,
                                   C.c_void_p(s.cuda_stream)), "st_materialize_as")
+
+
+def materialize_noalloc(blob, table_raw: bytes, units: int, out_ptrs, stream=None, slices: bool = False,
+                        out_dtype: str = "bf16"):
+    """The allocation-free launch (st_materialize_noalloc): the work table ``table_raw`` (host bytes)
+    and the device output pointers ``out_ptrs`` (ints) are copied into the library's own device
+    array on ``stream`` and decoded from there.  Returns the host buffers handed to the copies; keep
+    them until ``stream`` has passed the launch."""
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(blob.device)
+    table = C.create_string_buffer(bytes(table_raw), len(table_raw))
+    ptrs = (C.c_void_p * max(1, len(out_ptrs)))(*[int(p) for p in out_ptrs])
+    check(lib().st_materialize_noalloc(C.c_void_p(blob.data_ptr()), table, len(table_raw), units, ptrs, len(out_ptrs),
+                                       OUT_DTYPES.index(out_dtype), MAT_SLICES if slices else 0,
+                                       C.c_void_p(s.cuda_stream)), "st_materialize_noalloc")
+    return table, ptrs
 
 
 def read_plans(path: str, index: SafeTensorIndex, plans, hosts) -> float:

@@ -47,6 +47,7 @@ class TableHeader(C.Structure):
 assert C.sizeof(TableHeader) == 64
 TABLE_MAGIC = 0x334D5453
 UNITS_PER_GROUP = 4
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 DESC_EXACT = 1
@@ -118,6 +119,8 @@ SIGNATURES = {
     "st_materialize_slices": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "st_materialize_as": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32, C.c_uint32,
                                     C.c_void_p]),
+    "st_materialize_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_size_t, C.c_void_p, C.c_size_t,
+                                         C.c_uint32, C.c_uint32, C.c_void_p]),
     "st_index_out_dtype": (C.c_uint32, [C.c_void_p]),
     "st_stream_plan_build": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p)]),
     "st_stream_plan_select": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_size_t, C.c_uint64, C.c_uint32,

@@ -52,8 +52,15 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstring>
+#include <mutex>
 
 #include "st_internal.h"
+
+// Device storage of st_materialize_noalloc: the work table and the output-pointer array of the
+// latest call on each GPU (every GPU the library runs on holds its own copy until the process ends).
+// Host code never names it directly: its per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[ST_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -963,6 +970,75 @@ extern "C" st_status st_materialize_as(const void* blob, const void* descs, size
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return st_fail(ST_E_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
     return ST_OK;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The address of `scratch` on device `dev`, looked up once per device with that device current.
+st_status scratch_address(int dev, uint8_t** out) {
+    static std::mutex m;
+    static uint8_t* addr[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices) return st_fail(ST_E_ARG, "st_materialize_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(m);
+    if (!addr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return st_fail(ST_E_HIP, "st_materialize_noalloc: hipGetDevice failed");
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return st_fail(ST_E_HIP, "st_materialize_noalloc: hipSetDevice(%d) failed", dev);
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return st_fail(ST_E_HIP, "st_materialize_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                           dev, hipGetErrorString(e));
+        addr[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = addr[dev];
+    return ST_OK;
+}
+
+}  // namespace
+
+extern "C" st_status st_materialize_noalloc(const void* blob, const void* table_host, size_t table_bytes, size_t n,
+                                            void* const* outs_host, size_t n_outs, uint32_t out_dtype, uint32_t flags,
+                                            void* stream) {
+    const char* who = "st_materialize_noalloc";
+    if (n == 0) return ST_OK;
+    if (!blob || !table_host || (n_outs && !outs_host)) return st_fail(ST_E_ARG, "%s: null pointer", who);
+    const uint64_t outs_off = (uint64_t(table_bytes) + 255) / 256 * 256;
+    const uint64_t need = outs_off + 8 * uint64_t(n_outs);
+    if (table_bytes > ST_NOALLOC_SCRATCH_BYTES || need > ST_NOALLOC_SCRATCH_BYTES)
+        return st_fail(ST_E_ARG, "%s: a %zu-byte work table and %zu output pointers need %llu bytes of scratch, at most %u",
+                       who, table_bytes, n_outs, (unsigned long long)need, unsigned(ST_NOALLOC_SCRATCH_BYTES));
+    if (table_bytes < sizeof(st_table_header)) return st_fail(ST_E_ARG, "%s: %zu-byte work table has no header", who, table_bytes);
+    st_table_header h;
+    memcpy(&h, table_host, sizeof h);
+    const uint64_t groups = (uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
+    if (h.magic != ST_TABLE_MAGIC || h.bytes != table_bytes || h.map_offset != sizeof(st_table_header) ||
+        h.desc_offset != stk::table_desc_offset(groups) || h.desc_offset + 64 * uint64_t(h.n_desc) > table_bytes)
+        return st_fail(ST_E_ARG, "%s: not a work table of %zu bytes and %zu units", who, table_bytes, n);
+    if (h.units != n) return st_fail(ST_E_ARG, "%s: the table holds %llu work units, n is %zu", who, (unsigned long long)h.units, n);
+    if (h.out_dtype != out_dtype)
+        return st_fail(ST_E_ARG, "%s: the table was planned for output type %u, the launch asks for %u", who, h.out_dtype, out_dtype);
+    const uint8_t* descs = static_cast<const uint8_t*>(table_host) + h.desc_offset;
+    for (uint32_t d = 0; d < h.n_desc; ++d) {
+        uint32_t out;
+        memcpy(&out, descs + 64 * size_t(d) + offsetof(st_desc, out), sizeof out);
+        if (out >= n_outs) return st_fail(ST_E_ARG, "%s: descriptor %u writes output %u of %zu", who, d, out, n_outs);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess) return st_fail(ST_E_HIP, "%s: hipStreamGetDevice failed", who);
+    uint8_t* ptr = nullptr;
+    st_status r = scratch_address(dev, &ptr);
+    if (r != ST_OK) return r;
+    // Every byte the kernel reads is written by these two copies; nothing needs clearing.
+    if (hipMemcpyAsync(ptr, table_host, table_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+        (n_outs && hipMemcpyAsync(ptr + outs_off, outs_host, 8 * n_outs, hipMemcpyHostToDevice, s) != hipSuccess))
+        return st_fail(ST_E_HIP, "%s: copy into the scratch array failed", who);
+    return st_materialize_as(blob, ptr, n, reinterpret_cast<void* const*>(ptr + outs_off), out_dtype, flags, stream);
 }
 
 extern "C" st_status st_materialize(const void* blob, const void* descs, size_t n, void* const* outs, void* stream) {

@@ -466,6 +466,33 @@ st_status st_materialize_slices(const void* blob, const void* descs, size_t n, v
 st_status st_materialize_as(const void* blob, const void* descs, size_t n, void* const* outs,
                             uint32_t out_dtype, uint32_t flags, void* stream);
 
+/* ---- A launch that allocates nothing --------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  st_materialize_as takes its work table and output-pointer array
+ * in device memory the caller allocated; this variant takes both in host memory and copies them
+ * (hipMemcpyAsync on `stream`) into a device array the library owns, ST_NOALLOC_SCRATCH_BYTES per
+ * GPU, held from the first call on a GPU until the process ends, then launches the same kernel on
+ * it.  It calls no allocating routine.
+ *   blob        the staged data section, as for st_materialize (device memory)
+ *   table_host  a work table in host memory (st_index_table, st_index_descs, st_index_table_subset or
+ *               st_index_table_slices), table_bytes long, n its work-unit count
+ *   outs_host   host array of n_outs device output pointers (descriptor d writes outs_host[desc.out])
+ *   out_dtype, flags  as st_materialize_as
+ * table_host and outs_host must stay valid and unchanged until `stream` has passed the launch (the
+ * copies are asynchronous).  Limit: round_up(table_bytes, 256) + 8 * n_outs <= ST_NOALLOC_SCRATCH_BYTES
+ * (the table takes 64 bytes per output plus 1 byte per work unit: about 32 G fp8 elements in one
+ * call); larger loads split into subset tables.  Every call on one GPU shares that GPU's array:
+ * calls on one stream are ordered, but calls that can overlap (other streams, other threads) race
+ * and must be ordered by the caller.  The array keeps the last call's contents; nothing in it needs
+ * clearing, since each call writes every byte its launch reads.
+ * Errors: ST_E_ARG for null pointers, sizes past the limit, a table whose header disagrees with n,
+ * table_bytes or out_dtype, or a descriptor naming an output pointer past n_outs (all checked on the
+ * host before anything is enqueued); ST_E_HIP if the device lookup, a copy or the launch fails. */
+#define ST_NOALLOC_SCRATCH_BYTES (32u << 20)
+st_status st_materialize_noalloc(const void* blob, const void* table_host, size_t table_bytes, size_t n,
+                                 void* const* outs_host, size_t n_outs, uint32_t out_dtype, uint32_t flags,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif
