@@ -72,14 +72,17 @@ def profiled_traffic(k):
     return traffic if sha == h.hexdigest() else None
 
 
-def pinned_to_device(blob, nbytes, piece=1 << 30, reps=3):
-    """Host-to-device copy rate on its own: one pinned buffer (touched beforehand) copied into the
-    blob piece by piece with hipMemcpyAsync on a side stream, timed with events on that stream."""
+def pinned_to_device(device, nbytes, piece=1 << 30, reps=3):
+    """Host-to-device copy rate on its own: ``nbytes`` copied from one pinned buffer (touched
+    beforehand) into one device buffer of the same size, piece by piece, with hipMemcpyAsync on a
+    side stream, timed with events on that stream.  The staged blob is left alone."""
     import torch
     n = min(piece, nbytes)
     host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
     host.fill_(0x3C)
-    side = torch.cuda.Stream(blob.device)
+    dst = torch.empty(n, dtype=torch.uint8, device=device)
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
     best = None
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -87,12 +90,12 @@ def pinned_to_device(blob, nbytes, piece=1 << 30, reps=3):
             a.record(side)
             for off in range(0, nbytes, n):
                 m = min(n, nbytes - off)
-                blob[off: off + m].copy_(host[:m], non_blocking=True)
+                dst[:m].copy_(host[:m], non_blocking=True)
             b.record(side)
         side.synchronize()
         ms = a.elapsed_time(b)
         best = ms if best is None else min(best, ms)
-    del host
+    del host, dst
     return nbytes / (best * 1e-3) / 1e9
 
 
@@ -241,7 +244,7 @@ def measure(k, d, args, rng, overrides=None):
     read_s = st.stage_file(path, ix, ck.blob, pinned, side)
     side.synchronize()
     stage_s = time.perf_counter() - t0
-    h2d = pinned_to_device(ck.blob, ix.data_size)   # the copy alone, from pinned pages already touched
+    h2d = pinned_to_device(dev, ix.data_size)   # the copy alone, from pinned pages already touched
     cold = None
     if k == args.config and args.cold_stage:
         if drop_page_cache(path):
