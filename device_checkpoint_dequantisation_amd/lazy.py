@@ -16,6 +16,7 @@ from __future__ import annotations
 import collections
 import fnmatch
 import re
+import threading
 import time
 from collections.abc import Mapping
 from dataclasses import dataclass
@@ -27,6 +28,21 @@ _ONE_STEP = 1 << 60  # chunk size that keeps a whole selection in one staging st
 
 def _round_up(x: int, a: int) -> int:
     return (x + a - 1) // a * a
+
+
+def _batches(sizes, n):
+    """Indices 0..len(sizes)-1 in order, cut into at most n runs of about equal total size."""
+    total = sum(sizes)
+    out, cur, acc = [], [], 0
+    for i, sz in enumerate(sizes):
+        cur.append(i)
+        acc += sz
+        if acc * n >= total * (len(out) + 1) and len(out) < n - 1:
+            out.append(cur)
+            cur = []
+    if cur:
+        out.append(cur)
+    return out
 
 
 @dataclass(frozen=True)
@@ -57,19 +73,86 @@ class OutputMeta:
 class PinnedArena:
     """Pinned host memory carved from slabs (first fit, coalescing frees), so that the RAM tier
     does not pin a fresh allocation for every entry.  Slabs are ``slab_bytes`` (or one entry's
-    size, if larger) and are allocated on demand, never more than ``max_bytes`` in total."""
+    size, if larger) and are allocated on demand, never more than ``max_bytes`` in total.
 
-    def __init__(self, max_bytes: int, slab_bytes: int = 256 << 20, allocate=None):
+    With ``prefetch`` (the default for real pinned memory), a background thread keeps one spare
+    slab allocated and touched ahead of need: the first write to a freshly pinned page maps it, and
+    done inside a file read that mapping made filling the tier several times slower than reading
+    into pages already touched (measured on MI355X hosts: about 12 against 70 GB/s)."""
+
+    def __init__(self, max_bytes: int, slab_bytes: int = 256 << 20, allocate=None, prefetch: bool | None = None):
         self.max_bytes = int(max_bytes)
         self.slab_bytes = max(256, min(int(slab_bytes), self.max_bytes))
         self.allocate = allocate or (lambda n: _torch().empty(n, dtype=_torch().uint8, pin_memory=True))
         self.slabs = []      # pinned uint8 tensors
         self.free = []       # per slab: sorted list of [offset, size] holes
         self.allocated = 0
+        self.prefetch = (allocate is None) if prefetch is None else bool(prefetch)
+        self._spare = None         # a touched slab of slab_bytes, not yet in use
+        self._spare_thread = None
+        self._spare_error = None
+        if self.prefetch:
+            self._start_spare()
 
     @property
     def capacity(self) -> int:
-        return sum(t.numel() for t in self.slabs)
+        """Bytes of the slabs in use, plus a spare slab being prepared or ready."""
+        spare = self.slab_bytes if (self._spare_thread is not None or self._spare is not None) else 0
+        return sum(t.numel() for t in self.slabs) + spare
+
+    def _start_spare(self):
+        """Allocate and touch the next slab in a background thread, if one more slab fits."""
+        if not self.prefetch or self._spare_thread is not None or self._spare is not None:
+            return
+        if sum(t.numel() for t in self.slabs) + 2 * self.slab_bytes > self.max_bytes:
+            return   # keep room for a slab of one large entry
+
+        def work(size=self.slab_bytes):
+            try:
+                t = self.allocate(size)
+                t.fill_(0)   # first touch of every page, off the read path
+                self._spare = t
+            except BaseException as e:  # reported when the slab is wanted
+                self._spare_error = e
+
+        self._spare_thread = threading.Thread(target=work, name="pinned-arena-prefetch", daemon=True)
+        self._spare_thread.start()
+
+    def reserve_slabs(self, nbytes: int) -> int:
+        """Allocate and touch slabs now until they hold ``nbytes`` (within ``max_bytes``), so that
+        later entries land in memory that is already pinned and mapped; returns the bytes of slabs
+        held.  Creating pinned memory is the slow part of filling the tier (measured on MI355X
+        hosts: about 12 GB/s, and other HIP calls of the process wait meanwhile)."""
+        if self._spare_thread is not None:
+            self._spare_thread.join()
+            self._spare_thread = None
+        if self._spare is not None:      # a spare already prepared becomes a slab first
+            t, self._spare = self._spare, None
+            self.slabs.append(t)
+            self.free.append([[0, t.numel()]])
+        while sum(t.numel() for t in self.slabs) < nbytes:
+            size = self.slab_bytes
+            if self.capacity + size > self.max_bytes:
+                break
+            t = self.allocate(size)
+            t.fill_(0)
+            self.slabs.append(t)
+            self.free.append([[0, size]])
+        return self.capacity
+
+    def _take_spare(self, n: int):
+        """The spare slab if it holds n bytes (waiting for it if it is still being prepared)."""
+        if self._spare_thread is not None:
+            self._spare_thread.join()
+            self._spare_thread = None
+        if self._spare_error is not None:
+            e, self._spare_error = self._spare_error, None
+            raise e
+        t = self._spare
+        if t is None or t.numel() < n:
+            return None
+        self._spare = None
+        return t
 
     def alloc(self, n: int):
         """(slab, offset) of n free bytes (256-byte aligned), or None if none is free and no new
@@ -85,12 +168,21 @@ class PinnedArena:
                         holes.remove(h)
                     self.allocated += n
                     return si, off
-        size = max(self.slab_bytes, n)
-        if self.capacity + size > self.max_bytes:
-            return None
-        self.slabs.append(self.allocate(size))
+        slab = self._take_spare(n)
+        if slab is None:
+            size = max(self.slab_bytes, n)
+            if self.capacity + size > self.max_bytes:
+                if self._spare is None:
+                    return None
+                self._spare = None   # a slab of one large entry takes the spare's place
+                if self.capacity + size > self.max_bytes:
+                    return None
+            slab = self.allocate(size)
+        size = slab.numel()
+        self.slabs.append(slab)
         self.free.append([[n, size - n]] if size > n else [])
         self.allocated += n
+        self._start_spare()
         return len(self.slabs) - 1, 0
 
     def release(self, si: int, off: int, n: int):
@@ -211,10 +303,11 @@ class StreamStateDict(Mapping):
     ``keys()``, ``len()``, ``in`` and :meth:`meta` read nothing but the header.  Indexing decodes one
     tensor on the GPU; :meth:`load` decodes several with one read and one upload.  With
     ``ram_cache_bytes`` > 0 the checkpoint bytes of recently loaded outputs stay in pinned host
-    memory (LRU) and later loads of them skip the file."""
+    memory (LRU) and later loads of them skip the file; ``ram_preallocate`` pins that memory (up to
+    the checkpoint's size) when the mapping is created instead of while loads fill the tier."""
 
     def __init__(self, path: str, device="cuda", ram_cache_bytes: int = 0, index: SafeTensorIndex | None = None,
-                 out_dtype: str = "bf16", steps_per_load: int = 8):
+                 out_dtype: str = "bf16", steps_per_load: int = 8, ram_preallocate: bool = False):
         self.path = path
         self.index = index if index is not None else SafeTensorIndex.open(path, out_dtype=out_dtype)
         self.device = _torch().device(device)
@@ -233,6 +326,15 @@ class StreamStateDict(Mapping):
         self._stage = None  # pinned buffer for small uploads
         self._stage_done = None
         self.steps_per_load = max(1, int(steps_per_load))  # staging steps of a direct load
+        self.fill_batches = 4   # file reads per load that fills the RAM tier (overlapping the uploads)
+        self.ram_preallocate_seconds = 0.0
+        if ram_preallocate and self.ram.arena is not None:
+            # pinned slabs for the whole checkpoint (each entry is its weight and scale bytes, runs
+            # aligned to 256 bytes), or for the tier's bound if that is smaller
+            need = sum(m.source_bytes + 1024 for m in self._meta.values())
+            t0 = time.perf_counter()
+            self.ram.arena.reserve_slabs(min(need, self.ram.max_bytes))
+            self.ram_preallocate_seconds = time.perf_counter() - t0
 
     # ---- metadata only
     def __iter__(self):
@@ -323,9 +425,13 @@ class StreamStateDict(Mapping):
         self._ring_free.record(self._side)  # after this load's last copy out of the ring
 
     def _load_cached(self, metas, outs, s):
-        """Per-output packed entries, read from the file once and then kept in the RAM tier."""
+        """Per-output packed entries, read from the file once and then kept in the RAM tier.  Misses
+        are read in a few batches of about equal bytes, and each batch's uploads and decodes are
+        enqueued before the next batch is read, so that file reads overlap the host-to-device copies."""
         torch = _torch()
         entries, miss = {}, []
+        plans, wheres, hosts = [], [], []
+        entered = 0   # misses whose reserved memory now belongs to an entry
         try:
             for m in metas:
                 e = self.ram.get(m.index)
@@ -338,7 +444,6 @@ class StreamStateDict(Mapping):
                     self.stats["ram_hits"] += 1
             if miss:
                 plans = [StreamPlan(self.index, _ONE_STEP, select=[m.index], pack=True) for m in miss]
-                wheres, hosts = [], []
                 for p in plans:  # arena memory when the entry can be kept, a transient buffer otherwise
                     w = self.ram.reserve(p.blob_bytes)
                     wheres.append(w)
@@ -346,43 +451,23 @@ class StreamStateDict(Mapping):
                                  else torch.empty(p.blob_bytes, dtype=torch.uint8, pin_memory=True))
                     if w is not None:  # held until the entry is in the cache, then protected
                         self.ram.bytes += p.blob_bytes
-                t0 = time.perf_counter()
-                try:
-                    read_plans(self.path, self.index, plans, hosts)
-                except BaseException:
-                    for p, w in zip(plans, wheres):  # give the reserved memory back
-                        if w is not None:
-                            self.ram.bytes -= p.blob_bytes
-                            self.ram.arena.release(w[0], w[1], p.blob_bytes)
-                    raise
-                self.stats["read_seconds"] += time.perf_counter() - t0
-                self.stats["file_bytes"] += sum(e - b for p in plans for b, e in p.ranges)
-                # the tables of all new entries and the output pointers in one upload
-                *tables, ptrs = self._upload_parts([p.tables for p in plans] +
-                                                   [self._pointer_bytes([outs[m.name] for m in metas])])
-                uploaded = torch.cuda.Event()
-                uploaded.record(s)
-                for m, p, h, tab, w in zip(miss, plans, hosts, tables, wheres):
-                    e = _Entry(p, h, w)
-                    e.table_dev = tab
-                    e.table_ready = uploaded
-                    entries[m.index] = e
-                    if w is not None:
-                        self.ram.bytes -= p.blob_bytes
-                        self.ram.protected.add(m.index)
-                        self.ram.put(m.index, e)
-                    self.stats["ram_misses"] += 1
-            # one device blob with a 256-byte aligned segment per output, one launch per output
-            segs, total = [], 0
-            for m in metas:
-                segs.append(total)
-                total += _round_up(entries[m.index].nbytes, 256)
-            blob = torch.empty(max(total, 256), dtype=torch.uint8, device=self.device)
-            if not miss:
-                ptrs = self._upload(self._pointer_bytes([outs[m.name] for m in metas]))
+            # the tables of all new entries and the output pointers in one upload
+            *tables, ptrs = self._upload_parts([p.tables for p in plans] +
+                                               [self._pointer_bytes([outs[m.name] for m in metas])])
+            uploaded = torch.cuda.Event()
+            uploaded.record(s)
             ptrs = ptrs[: 8 * len(metas)].view(torch.int64)
-            for j, (m, off) in enumerate(zip(metas, segs)):
-                e = entries[m.index]
+            # one device blob with a 256-byte aligned segment per output, one launch per output
+            nbytes = {m.index: e.nbytes for m, e in ((m, entries.get(m.index)) for m in metas) if e is not None}
+            nbytes.update({m.index: p.blob_bytes for m, p in zip(miss, plans)})
+            segs, total = {}, 0
+            for j, m in enumerate(metas):
+                segs[m.index] = (j, total)
+                total += _round_up(nbytes[m.index], 256)
+            blob = torch.empty(max(total, 256), dtype=torch.uint8, device=self.device)
+
+            def decode(m, e):
+                j, off = segs[m.index]
                 blob[off: off + e.nbytes].copy_(e.host, non_blocking=True)
                 ev = torch.cuda.Event()
                 ev.record(s)
@@ -392,6 +477,34 @@ class StreamStateDict(Mapping):
                         materialize(blob[off:], e.table_dev[step.table_offset:], step.units, ptrs[j:], s,
                                     out_dtype=self.index.out_dtype)
                         self.stats["launches"] += 1
+
+            for m in metas:
+                if m.index in entries:
+                    decode(m, entries[m.index])
+            for batch in _batches([p.blob_bytes for p in plans], self.fill_batches):
+                t0 = time.perf_counter()
+                read_plans(self.path, self.index, [plans[i] for i in batch], [hosts[i] for i in batch])
+                self.stats["read_seconds"] += time.perf_counter() - t0
+                self.stats["file_bytes"] += sum(e - b for i in batch for b, e in plans[i].ranges)
+                for i in batch:
+                    m, p, w = miss[i], plans[i], wheres[i]
+                    e = _Entry(p, hosts[i], w)
+                    e.table_dev = tables[i]
+                    e.table_ready = uploaded
+                    entries[m.index] = e
+                    if w is not None:
+                        self.ram.bytes -= p.blob_bytes
+                        self.ram.protected.add(m.index)
+                        self.ram.put(m.index, e)
+                    entered = i + 1
+                    self.stats["ram_misses"] += 1
+                    decode(m, e)
+        except BaseException:
+            for p, w in list(zip(plans, wheres))[entered:]:  # give back memory no entry took
+                if w is not None:
+                    self.ram.bytes -= p.blob_bytes
+                    self.ram.arena.release(w[0], w[1], p.blob_bytes)
+            raise
         finally:
             self.ram.protected.clear()
 

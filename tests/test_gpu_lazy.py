@@ -223,3 +223,21 @@ def test_device_checkpoint_restream_behind_a_busy_stream(tmp_path):
     del busy
     for name, w in want.items():
         assert np.array_equal(_bits(ck.tensors[name]).reshape(w.shape), w), name
+
+
+def test_preallocated_ram_tier(tmp_path):
+    """A tier whose pinned memory is created up front: loads fill it without new slabs, and later
+    loads hit it; every tensor equals the oracle."""
+    path, buf = _file(tmp_path, 2)
+    want = oracle.materialize(buf)
+    sd = st.StreamStateDict(path, DEV, ram_cache_bytes=1 << 30, ram_preallocate=True)
+    slabs = len(sd.ram.arena.slabs)
+    assert slabs >= 1 and sd.ram.arena.capacity >= sum(sd.meta(k).source_bytes for k in sd)
+    names = list(sd)
+    for rnd in range(2):
+        got = sd.load(names)
+        torch.cuda.synchronize()
+        for name, t in got.items():
+            assert np.array_equal(_bits(t).reshape(want[name].shape), want[name]), name
+    assert len(sd.ram.arena.slabs) == slabs        # no slab was added while filling
+    assert sd.stats["ram_hits"] == len(names)

@@ -164,3 +164,47 @@ def test_arena_slab_never_exceeds_the_bound():
     a = st.lazy.PinnedArena(1000, slab_bytes=256 << 20, allocate=lambda n: torch.empty(n, dtype=torch.uint8))
     assert a.slab_bytes == 1000
     assert a.alloc(300) == (0, 0) and a.capacity == 1000
+
+
+def test_arena_prefetches_a_touched_spare_slab_within_the_bound():
+    made = []
+
+    def alloc(n):
+        t = torch.full((n,), 7, dtype=torch.uint8)   # not zero: the spare must come back touched (zeroed)
+        made.append(n)
+        return t
+
+    a = st.lazy.PinnedArena(8192, slab_bytes=2048, allocate=alloc, prefetch=True)
+    assert a.capacity == 2048                 # the first spare, prepared in the background
+    x = a.alloc(1000)
+    assert x == (0, 0) and int(a.slabs[0].sum()) == 0
+    for _ in range(4):                         # fill slabs; spares stop once another slab would not fit
+        a.alloc(2000)
+    assert sum(t.numel() for t in a.slabs) <= 8192 and a.capacity <= 8192
+    assert a.alloc(2000) is None               # the bound is full
+    big = st.lazy.PinnedArena(8192, slab_bytes=2048, allocate=alloc, prefetch=True)
+    assert big.alloc(5000) == (0, 0)           # an entry larger than a slab gets a slab of its own
+    assert big.slabs[0].numel() == 5120 and big.capacity <= 8192   # rounded to 256
+
+
+def test_arena_reserve_slabs_up_front():
+    a = st.lazy.PinnedArena(8192, slab_bytes=2048, allocate=lambda n: torch.full((n,), 9, dtype=torch.uint8),
+                            prefetch=False)
+    assert a.reserve_slabs(5000) == 6144            # three slabs, touched (zeroed)
+    assert all(int(t.sum()) == 0 for t in a.slabs)
+    assert a.alloc(2000) == (0, 0) and a.alloc(2000) == (1, 0)   # entries land in the reserved slabs
+    assert a.reserve_slabs(1 << 20) == 8192         # never past the bound
+
+
+def test_arena_reserve_takes_the_prepared_spare():
+    a = st.lazy.PinnedArena(8192, slab_bytes=2048, allocate=lambda n: torch.zeros(n, dtype=torch.uint8), prefetch=True)
+    assert a.reserve_slabs(1000) == 2048 and len(a.slabs) == 1   # the spare, now a slab
+    assert a.alloc(1000) == (0, 0) and len(a.slabs) == 1
+
+
+def test_fill_batches_cover_every_miss_in_order():
+    from device_checkpoint_dequantisation_amd.lazy import _batches
+    assert _batches([], 4) == []
+    assert _batches([5], 4) == [[0]]
+    assert _batches([10] * 13, 4) == [[0, 1, 2, 3], [4, 5, 6], [7, 8, 9], [10, 11, 12]]
+    assert _batches([100, 1, 1, 1], 2) == [[0], [1, 2, 3]]
