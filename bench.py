@@ -415,14 +415,40 @@ def end_to_end_loads(path, ix, ck, side, stream, args, rng):
             "stream_launches": sstats["launches"], "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}"}
 
 
+SOURCE_BYTES = {"PASS_BF16": 2, "CAST_F16": 2, "CAST_F32": 4, "FP8_TENSOR": 1, "FP8_BLOCK128": 1,
+                "NVFP4": 0.5 + 1 / 16, "MXFP8": 1 + 1 / 32, "MXFP4": 0.5 + 1 / 32}
+
+
+def slice_traffic(ix, slices, out_bytes=2):
+    """Algorithmic bytes of decoding `slices`: each element's source bytes (with its share of the
+    NVFP4 / MX block scales) plus the output bytes; per-tensor and block-FP8 grid scales are
+    counted per slice (4 bytes per scale the slice uses)."""
+    outs = ix.outputs()
+    total = 0.0
+    for sl in slices:
+        k = sl[0]
+        r, c = ix.slice_shape(*sl)
+        o = outs[k]
+        total += r * c * (SOURCE_BYTES[o.kind] + out_bytes)
+        if o.kind == "FP8_TENSOR":
+            total += 4
+        elif o.kind == "FP8_BLOCK128":
+            total += 4 * -(-r // 128) * -(-c // 128)
+        elif o.kind == "NVFP4":
+            total += 4
+    return int(total)
+
+
 def tp_shards(ix, ck, steps, n=8):
     """Decode the whole checkpoint as n-way tensor-parallel shards of every 2-d output (row shards,
     then column shards; cuts on scale-block boundaries), one launch per layout, and check every
-    shard against the unsharded decode on the GPU."""
+    shard against the unsharded decode on the GPU.  "col_shard_one" decodes one rank's column shard
+    of every 2-d output (and every other output whole), as one GPU of an n-way tensor-parallel
+    group would; its GB/s counts that table's own algorithmic bytes."""
     import torch
     outs = ix.outputs()
     res = {}
-    for label, axis in (("row_shards", 0), ("col_shards", 1)):
+    for label, axis in (("row_shards", 0), ("col_shards", 1), ("col_shard_one", 1)):
         slices = []
         for k, o in enumerate(outs):
             if len(o.shape) != 2:
@@ -435,6 +461,8 @@ def tp_shards(ix, ck, steps, n=8):
             for b in range(0, dim, step):
                 part = (b, min(dim, b + step))
                 slices.append((k, part, None) if axis == 0 else (k, None, part))
+                if label == "col_shard_one":
+                    break
         shapes = [ix.slice_shape(*sl) for sl in slices]
         offs, total = [], 0
         for r, c in shapes:
@@ -465,9 +493,10 @@ def tp_shards(ix, ck, steps, n=8):
             b.record(stream)
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        traffic = ix.traffic_bytes if label != "col_shard_one" else slice_traffic(ix, slices)
         res[label] = {"shards_per_output": n, "slices": len(slices), "kernel_ms_mean": round(ms, 4),
                       "kernel": "st_materialize_slices" if strided else "st_materialize",
-                      "GBps": round(ix.traffic_bytes / (ms * 1e-3) / 1e9, 2),
+                      "traffic_bytes": traffic, "GBps": round(traffic / (ms * 1e-3) / 1e9, 2),
                       "parity": "bit-exact vs whole decode" if ok else "MISMATCH"}
         del arena
     return res

@@ -123,3 +123,50 @@ def test_tensor_parallel_shards_reassemble(k):
             torch.cuda.synchronize()
             whole = np.concatenate([_bits(t).reshape(t.shape) for t in got], axis=axis)
             assert np.array_equal(whole, want[o.name]), (o.name, axis)
+
+
+@pytest.mark.parametrize("kind", ["NVFP4", "MXFP4"])
+def test_interleaved_fp4_column_shards_match_the_whole_decode(kind):
+    """8-way column shards of packed fp4 weights large enough that the planner interleaves them in
+    many bands (index from the header alone, random bytes filled on the GPU, codes and scales free of
+    NaN): every shard equals its block of the whole decode, which equals the oracle on sampled
+    elements."""
+    from synth.st_writer import Group, TensorSpec, layout
+    m, k = 1536, 5120
+    spec = [("w.weight", "U8", (m, k // 2))]
+    if kind == "NVFP4":
+        spec += [("w.weight_scale", "F8_E4M3", (m, k // 16)), ("w.weight_scale_2", "F32", ())]
+    else:
+        spec += [("w.weight_scale", "F8_E8M0", (m, k // 32))]
+    lay = layout([Group([TensorSpec(n, d, s)], None) for n, d, s in spec])
+    ix = st.SafeTensorIndex.from_bytes(lay.header, file_size=len(lay.header) + lay.data_size)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(17)
+    blob = ck.blob
+    b, e = lay.offsets["w.weight"]
+    blob[b:e] = torch.randint(0, 256, (e - b,), device=DEV, dtype=torch.uint8, generator=gen)
+    sb, se = lay.offsets["w.weight_scale"]
+    lo, hi = (0x08, 0x68) if kind == "NVFP4" else (115, 130)
+    blob[sb:se] = torch.randint(lo, hi, (se - sb,), device=DEV, dtype=torch.uint8, generator=gen)
+    if kind == "NVFP4":
+        gb, ge = lay.offsets["w.weight_scale_2"]
+        blob[gb:ge] = torch.tensor([0.0123], device=DEV).view(torch.uint8)
+    ck.arena.view(torch.int16).fill_(0x5A5A)
+    ck.materialize()
+    slices = [(0, None, (c, c + k // 8)) for c in range(0, k, k // 8)]
+    raw, units = ix.table_slices(slices)
+    n_desc = int(np.frombuffer(raw[:8], "<u4")[1])
+    assert n_desc > 8, "the shards were not split into bands"
+    got = ck.materialize_slices(slices)
+    torch.cuda.synchronize()
+    whole = ck.tensors["w.weight"]
+    for (o, _, (c0, c1)), t in zip(slices, got):
+        assert torch.equal(t.view(torch.int16), whole[:, c0:c1].view(torch.int16)), (c0, c1)
+    # the whole decode against the oracle on sampled elements
+    h = oracle.parse_header(lay.header)
+    out = oracle.classify(h)[0]
+    data = blob[: lay.data_size].cpu().numpy()
+    idx = np.random.default_rng(3).integers(0, m * k, 4096)
+    want = oracle.decode(out, data, idx)
+    g = whole.reshape(-1)[torch.from_numpy(idx).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(g, want)

@@ -114,3 +114,47 @@ def test_refused_cuts(ix3):
     with pytest.raises(st.StError, match="ST_E_ARG"):
         ix3.table_slices([(10 ** 6, None, None)])
     ix3.table_slices([(q, (128, 128), None)])   # empty slices are fine
+
+
+def _header_index(spec):
+    """An index built from a header alone (no data bytes needed for planning)."""
+    from synth.st_writer import Group, TensorSpec, layout
+    lay = layout([Group([TensorSpec(n, d, sh)], None) for n, d, sh in spec])
+    return st.SafeTensorIndex.from_bytes(lay.header, file_size=len(lay.header) + lay.data_size)
+
+
+SIBLING_CASES = {
+    "nvfp4": [("w.weight", "U8", (4096, 2560)), ("w.weight_scale", "F8_E4M3", (4096, 320)), ("w.weight_scale_2", "F32", ()),
+              ("b.weight", "BF16", (100,))],
+    "mxfp4": [("w.weight", "U8", (2048, 4096)), ("w.weight_scale", "F8_E8M0", (2048, 256)), ("b.weight", "BF16", (100,))],
+    "fp8": [("w.weight", "F8_E4M3", (4096, 3072)), ("w.scale_weight", "F32", ()), ("b.weight", "BF16", (100,))],
+    "mxfp8": [("w.weight", "F8_E4M3", (2048, 4096)), ("w.weight_scale", "F8_E8M0", (2048, 128)), ("b.weight", "BF16", (100,))],
+}
+
+
+@pytest.mark.parametrize("case", sorted(SIBLING_CASES))
+def test_sibling_column_slices_interleave_in_bands(case):
+    """8-way column shards of a weight (plus a row slice and a lone column slice): sibling column
+    slices of packed fp4 weights are placed band by band, other kinds keep the request order; each
+    slice's descriptors cover its units exactly once with the right element offsets, and the map
+    stays valid."""
+    from tests.test_index import _check_map
+    ix = _header_index(SIBLING_CASES[case])
+    o = ix.output(0)
+    kind, cols = o.kind, o.shape[1]
+    q = 16 if kind == "NVFP4" else 32 if kind in ("MXFP8", "MXFP4") else 8
+    step = cols // 8
+    slices = [(0, None, (c, c + step)) for c in range(0, cols, step)]
+    slices += [(0, (0, 3), None), (0, (1, 5), (0, q)), (1, None, None)]
+    raw, units = ix.table_slices(slices)
+    h, d, m = _table(raw)
+    numels = [ix.slice_shape(*sl)[0] * ix.slice_shape(*sl)[1] for sl in slices]
+    _check_map(d, m, units, numels)
+    outs = [int(r["out"]) for r in d]
+    if kind in ("NVFP4", "MXFP4"):
+        assert outs[:16] == list(range(8)) * 2          # band 0 of every shard, then band 1, ...
+        shard_units = -(-numels[0] // (1 << int(d[0]["unit_shift"])))
+        assert len(d) == 8 * -(-shard_units // 16) + 3       # bands of 16 units, plus the 3 others
+        assert outs[-3:] == [8, 9, 10]                    # the other slices, whole, in request order
+    else:
+        assert outs == list(range(len(slices)))
