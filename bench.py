@@ -412,7 +412,11 @@ def end_to_end_loads(path, ix, ck, side, stream, args, rng):
             "streamed_load_GBps": round(ix.data_size / min(stream_s) / 1e9, 2),
             "streamed_load_s": round(min(stream_s), 4), "serial_load_s": round(min(serial_s), 4),
             "stream_chunk_MiB": args.stream_chunk_mb, "stream_steps": len(plan.steps),
-            "stream_launches": sstats["launches"], "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}"}
+            "stream_launches": sstats["launches"], "streamed_parity": "sampled-bit-exact" if sok else f"MISMATCH:{sbad}",
+            "streamed_first_decode_enqueued_ms": round(1e3 * sstats["seconds_first_launch"], 3),
+            "first_outputs": "streamed: the first step's outputs are decoded as soon as its bytes land, "
+                             "streamed_first_decode_enqueued_ms after the call starts; serial: no output "
+                             "before the whole data section is staged (serial_load_s)"}
 
 
 SOURCE_BYTES = {"PASS_BF16": 2, "CAST_F16": 2, "CAST_F32": 4, "FP8_TENSOR": 1, "FP8_BLOCK128": 1,

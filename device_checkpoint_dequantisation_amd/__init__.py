@@ -362,6 +362,7 @@ def stream_file(path: str, index: SafeTensorIndex, plan: StreamPlan, blob, table
                                C.c_void_p(side_stream.cuda_stream), C.c_void_p(stream.cuda_stream), None,
                                C.byref(st)), "st_stream_file")
     return {"seconds_read": st.seconds_read, "seconds_wait": st.seconds_wait, "bytes_read": st.bytes_read,
+            "seconds_first_launch": st.seconds_first_launch,
             "steps": st.steps, "launches": st.launches}
 
 

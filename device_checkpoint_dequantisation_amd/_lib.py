@@ -80,10 +80,10 @@ class StreamStep(C.Structure):
 
 class StreamStats(C.Structure):
     _fields_ = [("seconds_read", C.c_double), ("seconds_wait", C.c_double), ("bytes_read", C.c_uint64),
-                ("steps", C.c_uint32), ("launches", C.c_uint32)]
+                ("steps", C.c_uint32), ("launches", C.c_uint32), ("seconds_first_launch", C.c_double)]
 
 
-assert C.sizeof(StreamRange) == 32 and C.sizeof(StreamStep) == 40 and C.sizeof(StreamStats) == 32
+assert C.sizeof(StreamRange) == 32 and C.sizeof(StreamStep) == 40 and C.sizeof(StreamStats) == 40
 
 
 # name -> (restype, argtypes); the full list of exported symbols the header declares.

@@ -364,6 +364,8 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     std::vector<Piece> batch;
     hipStream_t side = static_cast<hipStream_t>(side_stream), compute = static_cast<hipStream_t>(compute_stream);
     st_stream_stats st{};
+    st.seconds_first_launch = -1;
+    const auto t_call = std::chrono::steady_clock::now();
     int last_slot = -1;  // ring slot of the last step that copied bytes
     const size_t nsteps = st_stream_plan_num_steps(plan);
     for (size_t s = 0; status == ST_OK && s < nsteps; ++s) {
@@ -423,7 +425,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
                                        size_t(step.units), outs_dev + step.first_out, st_index_out_dtype(idx), 0,
                                        compute_stream);
             if (status != ST_OK) break;
-            ++st.launches;
+            if (st.launches++ == 0) st.seconds_first_launch = seconds_since(t_call);
         }
     }
     if (status == ST_OK && done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), compute) != hipSuccess)

@@ -393,6 +393,9 @@ typedef struct {
     uint64_t bytes_read;
     uint32_t steps;         /* steps staged */
     uint32_t launches;      /* st_materialize launches enqueued */
+    double seconds_first_launch;  /* wall time from the call's start until the first decode was
+                                     enqueued (its step's bytes read and their copy queued); -1 if
+                                     there was none */
 } st_stream_stats;
 
 /* Stream the file at `path` through `plan`: for each step, read its ranges into a slot of the

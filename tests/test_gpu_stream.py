@@ -41,6 +41,7 @@ def test_stream_small_matches_oracle(variant, chunk, tmp_path):
     print(f"stream {variant} chunk {chunk}", flush=True)
     ck, stats = _stream(path, chunk_bytes=chunk)
     assert stats["bytes_read"] == ck.index.data_size
+    assert stats["launches"] >= 1 and 0 <= stats["seconds_first_launch"] <= stats["seconds_read"] + 1.0
     want = oracle.materialize(buf)
     for name, w in want.items():
         got = ck.tensors[name].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
