@@ -51,6 +51,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 DESC_EXACT = 1
+DESC_SPLIT = 2
 
 
 class Slice(C.Structure):

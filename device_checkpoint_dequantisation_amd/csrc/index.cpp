@@ -853,17 +853,72 @@ st_desc make_slice_desc(const st_index& ix, const Output& o, const Slice& g, uin
 #ifndef ST_SLICE_BAND_KINDS
 #define ST_SLICE_BAND_KINDS ((1u << ST_KIND_NVFP4) | (1u << ST_KIND_MXFP4))
 #endif
+#ifndef ST_SLICE_SPLIT
+#define ST_SLICE_SPLIT 1
+#endif
 constexpr uint64_t kBandUnits = ST_SLICE_BAND_UNITS;
+constexpr bool kSplit = ST_SLICE_SPLIT != 0;
 constexpr uint32_t kBandKinds = ST_SLICE_BAND_KINDS;
 
-std::vector<st_desc> interleave_column_slices(const std::vector<st_desc>& descs, const std::vector<uint64_t>& nu,
-                                              const std::vector<Slice>& gs, const st_slice* slices, uint64_t* total) {
+// A split descriptor for the slices j, j + 1, ..., j + S - 1 of the request if they are every column
+// shard of their rows: one output, the same rows, equal widths W in column order covering [0, C) with
+// S = C / W a power of two from 2 to 64, W a whole number of chunks, rows * C below 2^32, none
+// exact-only, each shard below 2^32 bytes, and a kind planned that way (stk::split_kind).  *count = S.
+bool split_desc(const st_index& ix, size_t j, const std::vector<Slice>& gs, const std::vector<st_desc>& descs,
+                const st_slice* slices, size_t k, st_desc* d, uint64_t* units, size_t* count) {
+    if (!kSplit) return false;
+    const Slice& g0 = gs[j];
+    const Output& o = ix.outputs[slices[j].output];
+    if (!g0.strided() || g0.c0 != 0 || !stk::split_kind(o.kind)) return false;
+    const uint64_t W = g0.cols(), C = g0.C;
+    if (W == 0 || C % W) return false;
+    const uint64_t S = C / W;
+    if (S < 2 || S > 64 || (S & (S - 1)) || j + S > k) return false;
+    if (W % stk::chunk_elems(o.kind) || W % 4 || g0.rows() * C >= (uint64_t(1) << 32) ||
+        g0.rows() * W * sti::out_bytes(ix) >= (uint64_t(1) << 32))  // a shard's byte offsets are 32-bit
+        return false;
+    for (size_t i = 0; i < S; ++i) {
+        const Slice& g = gs[j + i];
+        if (slices[j + i].output != slices[j].output || g.r0 != g0.r0 || g.r1 != g0.r1 || g.c0 != i * W ||
+            g.cols() != W || (descs[j + i].flags & ST_DESC_EXACT))
+            return false;
+    }
+    Slice whole = g0;   // the same rows, every column: a contiguous source
+    whole.c0 = 0;
+    whole.c1 = C;
+    *d = make_slice_desc(ix, o, whole, uint32_t(j), 0, units);
+    d->flags = ST_DESC_SPLIT;
+    d->pitch = uint32_t(C);
+    d->cols = uint32_t(W);
+    d->grid_cols = stk::ilog2(uint32_t(S));
+    d->div_magic = stk::div_magic(uint32_t(W));
+    d->meta = (d->meta & 0xFF00FFFFu) | stk::div_shift(uint32_t(W)) << 16;
+    *count = size_t(S);
+    return true;
+}
+
+std::vector<st_desc> interleave_column_slices(const st_index& ix, const std::vector<st_desc>& descs,
+                                              const std::vector<uint64_t>& nu, const std::vector<Slice>& gs,
+                                              const st_slice* slices, uint64_t* total) {
     const size_t k = descs.size();
+    // complete shard sets first: split descriptors, placed where their first shard is
+    std::vector<st_desc> split(k);
+    std::vector<uint64_t> split_units(k, 0);
+    std::vector<size_t> split_count(k, 0);
+    std::vector<bool> in_split(k, false);
+    for (size_t j = 0; j < k; ++j) {
+        size_t S = 0;
+        if (!in_split[j] && split_desc(ix, j, gs, descs, slices, k, &split[j], &split_units[j], &S)) {
+            split_count[j] = S;
+            for (size_t i = j; i < j + S; ++i) in_split[i] = true;
+        }
+    }
+    // sibling groups of the remaining packed-fp4 column slices
     std::vector<int64_t> group(k, -1);   // first member of the slice's sibling group
     std::map<std::tuple<uint32_t, uint64_t, uint64_t>, size_t> first;
     std::vector<size_t> members(k, 0);
     for (size_t j = 0; j < k; ++j) {
-        if (!gs[j].strided() || (descs[j].flags & ST_DESC_EXACT) || nu[j] == 0) continue;
+        if (in_split[j] || !gs[j].strided() || (descs[j].flags & ST_DESC_EXACT) || nu[j] == 0) continue;
         if (!((kBandKinds >> (descs[j].meta & 0xFFu)) & 1u)) continue;
         auto key = std::make_tuple(slices[j].output, gs[j].r0, gs[j].r1);
         auto it = first.emplace(key, j).first;
@@ -885,6 +940,15 @@ std::vector<st_desc> interleave_column_slices(const std::vector<st_desc>& descs,
     std::vector<bool> done(k, false);
     for (size_t j = 0; j < k; ++j) {
         if (done[j]) continue;
+        if (split_count[j]) {
+            st_desc d = split[j];
+            d.unit_begin = uint32_t(pos);
+            d.unit_end = uint32_t(pos + split_units[j]);
+            out.push_back(d);
+            pos += split_units[j];
+            for (size_t i = j; i < j + split_count[j]; ++i) done[i] = true;
+            continue;
+        }
         if (group[j] < 0 || members[size_t(group[j])] < 2) {
             place(j, 0, nu[j]);
             done[j] = true;
@@ -892,7 +956,7 @@ std::vector<st_desc> interleave_column_slices(const std::vector<st_desc>& descs,
         }
         std::vector<size_t> sib;
         for (size_t i = j; i < k; ++i)
-            if (group[i] == group[j]) sib.push_back(i);
+            if (group[i] == group[j] && !done[i]) sib.push_back(i);
         uint64_t most = 0;
         for (size_t i : sib) most = std::max(most, nu[i]);
         for (uint64_t a = 0; a < most; a += kBandUnits)
@@ -1156,7 +1220,7 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
             pos += nu[j];
             if (pos >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "st_index_table_slices: 2^32 or more work units");
         }
-        descs = interleave_column_slices(descs, nu, gs, slices, &pos);
+        descs = interleave_column_slices(*idx, descs, nu, gs, slices, &pos);
         t = assemble(descs, pos, idx->out_dtype);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");

@@ -234,11 +234,22 @@ __device__ __forceinline__ Desc load_desc(const st_desc* d) {
 static_assert(offsetof(st_desc, meta) == 15 * 4, "descriptor layout");
 
 // Source element of output element e: e itself, or for a column slice (pitch != 0) the element
-// row * pitch + col of the slice's source rows, with row = e / cols and col = e % cols.
+// row * pitch + col of the slice's source rows, with row = e / cols and col = e % cols.  A split
+// descriptor reads its rows whole (e is the source element; its destination is split_dst).
 __device__ __forceinline__ uint64_t src_elem(const Desc& D, uint64_t e) {
-    if (D.pitch == 0) return e;
+    if (D.pitch == 0 || (D.flags & ST_DESC_SPLIT)) return e;
     const uint32_t row = stk::div_apply(uint32_t(e), D.div_magic, D.div_shift);
     return e + uint64_t(row) * (D.pitch - D.cols);
+}
+
+// Destination of source element e of a split descriptor: the rows [pitch] are cut into 2^grid_cols
+// shards of cols elements each; shard s = (e / cols) mod 2^grid_cols is output out + s, a
+// [rows, cols] row-major array, and e lands at (e / pitch) * cols + e mod cols in it.  Returns the
+// element index; *which = s.
+__device__ __forceinline__ uint32_t split_dst(const Desc& D, uint64_t e, uint32_t* which) {
+    const uint32_t q = stk::div_apply(uint32_t(e), D.div_magic, D.div_shift);
+    *which = q & ((1u << D.grid_cols) - 1u);
+    return (q >> D.grid_cols) * D.cols + (uint32_t(e) - q * D.cols);
 }
 
 // The exact fp32 value of element e of a KIND descriptor (before the output rounding), straight
@@ -829,10 +840,126 @@ __device__ __forceinline__ void run_strided(const Ctx& c, uint64_t e0, uint32_t 
 // Every element of a unit through the exact path (descriptors the host marks exact-only).
 template <uint32_t KIND, class O>
 __device__ __forceinline__ void unit_exact(const Ctx& c, uint64_t e0, uint32_t cnt, uint32_t lane) {
+    if (c.D.flags & ST_DESC_SPLIT) {  // each element to its shard
+        if constexpr (KIND == ST_KIND_FP8_BLOCK128) return;  // never planned: its scale grid needs cols
+#pragma unroll 1
+        for (uint32_t t = lane; t < cnt; t += stk::kWave) {
+            uint32_t s;
+            const uint32_t i = split_dst(c.D, e0 + t, &s);
+            uint8_t* out = c.outs[c.D.out + s];
+            if ((reinterpret_cast<uintptr_t>(out) & (O::BYTES - 1)) == 0)
+                store_elem<O>(out, i, kind_exact<KIND, O>(c.blob, c.D, e0 + t));
+        }
+        return;
+    }
     uint8_t* out = ld_uniform<uint8_t*>(c.outs + c.D.out);
     if (reinterpret_cast<uintptr_t>(out) & (O::BYTES - 1)) return;
 #pragma unroll 1
     for (uint32_t t = lane; t < cnt; t += stk::kWave) store_elem<O>(out, e0 + t, kind_exact<KIND, O>(c.blob, c.D, e0 + t));
+}
+
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+
+// Stores one chunk of a split descriptor to its shard (p: the chunk's output address); chunks the fast
+// path cannot take (NaN inputs, non-finite scales, a shard not 16-byte aligned) go element by element.
+template <class K, class O>
+__device__ __forceinline__ void split_store(const Ctx& c, const uint32_t* in, uint32_t s, uint8_t* shard,
+                                            uint32_t idx, uint64_t e) {
+    constexpr uint32_t NW = K::CE * O::BYTES / 4;
+    uint32_t w[NW];
+    uint8_t* p = shard + size_t(idx) * O::BYTES;
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) == 0 && K::fast(c, in, s, w)) {
+        // A pointer taken from another lane is generic to the compiler: without the global address
+        // space the stores are flat ones, which also count against the LDS/scalar wait counter, so
+        // every later wait for a cross-lane read or a scalar load would wait for them.
+        global_u32x4* g = (global_u32x4*)(p);
+#pragma unroll
+        for (uint32_t k = 0; k < NW / 4; ++k) g[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    } else if ((reinterpret_cast<uintptr_t>(shard) & (O::BYTES - 1)) == 0) {
+#pragma unroll 1
+        for (uint32_t k = 0; k < K::CE; ++k) store_elem<O>(shard, idx + k, kind_exact<K::KIND, O>(c.blob, c.D, e + k));
+    }
+}
+
+// A whole unit of a split descriptor (every column shard of some rows in one descriptor; see
+// split_dst): the source is read whole, like a whole output, with the same load order as unit_full,
+// and each chunk is stored to its shard.  A chunk never crosses a shard (cols is a whole number of
+// chunks), so it is still one 16-byte output word, at a per-lane address; its offset in the shard is
+// a multiple of 16 bytes, so the shards' own alignment decides the vector stores, once per unit.
+// Lane l loads shard (l mod 2^grid_cols)'s output pointer once; each chunk takes its shard's from
+// that lane.  Every lane of the wave is active here (the unit test is wave-uniform), as that
+// cross-lane read needs.  As in unit_full, chunks the fast path cannot take go element by element
+// after all the fast stores.
+template <class K, class O, bool ALIGNED>
+__device__ __forceinline__ void unit_split_full(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, ALIGNED>;
+    constexpr uint32_t NW = K::CE * O::BYTES / 4;
+    const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
+    uint32_t raw[K::CH][F::RW];
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
+    const uint64_t mine =
+        reinterpret_cast<uint64_t>(c0.outs[c0.D.out + (lane & ((1u << c0.D.grid_cols) - 1u))]);
+    __builtin_amdgcn_sched_barrier(0);
+    Ctx c = c0;
+    uint8_t* first;
+    (void)finish_ctx<K, O>(c, first);  // the scalar scale; the shards' pointers are checked below
+    bool ok[K::CH], vec = false;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        const uint32_t s = late_sc<K>(c, e, e);
+        // every shard 16-byte aligned; taken after the first scale load is issued, so that one wait
+        // covers the data, the pointers and that scale, as in unit_full
+        if (j == 0) vec = __builtin_amdgcn_ballot_w64((mine & 15u) != 0) == 0;
+        uint32_t which, in[F::N], w[NW];
+        const uint32_t idx = split_dst(c.D, e, &which);
+        const int from = int(which << 2);
+        const uint32_t lo = uint32_t(__builtin_amdgcn_ds_bpermute(from, int(uint32_t(mine))));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_ds_bpermute(from, int(uint32_t(mine >> 32))));
+        F::align(raw[j], sh, in);
+        ok[j] = K::fast(c, in, s, w) & vec;
+        if (ok[j]) {
+            global_u32x4* g = (global_u32x4*)(reinterpret_cast<uint8_t*>(uint64_t(hi) << 32 | lo) + size_t(idx) * O::BYTES);
+#pragma unroll
+            for (uint32_t k = 0; k < NW / 4; ++k) g[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+        }
+    }
+    bool all = true;
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+    if (__builtin_amdgcn_ballot_w64(!all) == 0) return;  // the common case
+#pragma unroll
+    for (uint32_t j = 0; j < K::CH; ++j) {
+        if (ok[j]) continue;
+        const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
+        uint32_t which;
+        const uint32_t idx = split_dst(c.D, e, &which);
+        uint8_t* shard = c.outs[c.D.out + which];
+        if ((reinterpret_cast<uintptr_t>(shard) & (O::BYTES - 1)) != 0) continue;
+#pragma unroll 1
+        for (uint32_t k = 0; k < K::CE; ++k) store_elem<O>(shard, idx + k, kind_exact<K::KIND, O>(c.blob, c.D, e + k));
+    }
+}
+
+// A partial unit of a split descriptor (its last, or any unit of a larger unit size): the lane walks
+// its chunks with unaligned loads, correct at any alignment, each loading its shard's pointer.
+template <class K, class O>
+__device__ __forceinline__ void unit_split_any(const Ctx& c0, uint64_t e0, uint32_t cnt, uint32_t sh, uint32_t lane) {
+    using F = Fetch<K, false>;
+    const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
+    Ctx c = c0;
+    uint8_t* first;
+    (void)finish_ctx<K, O>(c, first);
+    const uint32_t nch = cnt / K::CE;
+    for (uint32_t ci = lane; ci < nch; ci += stk::kWave) {
+        const uint64_t e = e0 + uint64_t(ci) * K::CE;
+        uint32_t raw[F::RW], in[F::N], which;
+        F::load(base, ci, raw);
+        const uint32_t idx = split_dst(c.D, e, &which);
+        F::align(raw, sh, in);
+        split_store<K, O>(c, in, K::sc(c, e, e), c.outs[c.D.out + which], idx, e);
+    }
 }
 
 // A whole unit takes the aligned or unaligned fast path by its source alignment; a partial unit (an
@@ -890,8 +1017,27 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     c.D = D;
     c.outs = outs;
     c.scale_al = (D.scale & 3u) == 0;
-    if ((D.pitch | D.flags) != 0) {  // column slices and exact-only descriptors
-        if (!SLICES || (D.flags & ST_DESC_EXACT)) {
+    if ((D.pitch | D.flags) != 0) {  // column slices, split descriptors and exact-only descriptors
+        if (SLICES && (D.flags & (ST_DESC_SPLIT | ST_DESC_EXACT)) == ST_DESC_SPLIT && (cnt & 7u) == 0 &&
+            stk::split_kind(D.kind)) {
+            const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src)), sh = a & 3u;
+            const bool full = cnt == (1u << D.unit_shift) && D.unit_shift == stk::step_shift(D.kind, O::CODE);
+            switch (D.kind) {
+#define ST_SPLIT_CASE(KIND_, K_)                                                           \
+    case KIND_:                                                                            \
+        if (!full) unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                           \
+        else if ((a & (K_<O>::LG - 1)) == 0) unit_split_full<K_<O>, O, true>(c, e0, 0, lane);  \
+        else unit_split_full<K_<O>, O, false>(c, e0, sh, lane);                              \
+        break;
+                ST_SPLIT_CASE(ST_KIND_FP8_TENSOR, KFp8Tensor)
+                ST_SPLIT_CASE(ST_KIND_NVFP4, KFp4)
+                ST_SPLIT_CASE(ST_KIND_MXFP4, KMx4)
+#undef ST_SPLIT_CASE
+                default: break;  // not a split kind
+            }
+            return;
+        }
+        if (!SLICES || (D.flags & (ST_DESC_EXACT | ST_DESC_SPLIT))) {
             switch (D.kind) {
                 case ST_KIND_FP8_TENSOR: unit_exact<ST_KIND_FP8_TENSOR, O>(c, e0, cnt, lane); break;
                 case ST_KIND_FP8_BLOCK128: unit_exact<ST_KIND_FP8_BLOCK128, O>(c, e0, cnt, lane); break;

@@ -153,7 +153,7 @@ def test_interleaved_fp4_column_shards_match_the_whole_decode(kind):
         blob[gb:ge] = torch.tensor([0.0123], device=DEV).view(torch.uint8)
     ck.arena.view(torch.int16).fill_(0x5A5A)
     ck.materialize()
-    slices = [(0, None, (c, c + k // 8)) for c in range(0, k, k // 8)]
+    slices = [(0, None, (c, c + k // 8)) for c in range(0, k, k // 8)][::-1]   # reversed: bands, not a split
     raw, units = ix.table_slices(slices)
     n_desc = int(np.frombuffer(raw[:8], "<u4")[1])
     assert n_desc > 8, "the shards were not split into bands"
@@ -170,3 +170,119 @@ def test_interleaved_fp4_column_shards_match_the_whole_decode(kind):
     want = oracle.decode(out, data, idx)
     g = whole.reshape(-1)[torch.from_numpy(idx).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(g, want)
+
+
+SPLIT_KINDS = ("FP8_TENSOR", "NVFP4", "MXFP4")   # kinds whose complete shard sets become split descriptors
+
+
+def _split_sets(o):
+    """Complete, in-order column shard sets (2, 4 and 8 shards) an output allows for a split."""
+    if len(o.shape) != 2 or o.kind == "FP8_BLOCK128":
+        return []
+    R, C = o.shape
+    q = 32 if o.kind in ("MXFP8", "MXFP4") else 16 if o.kind == "NVFP4" else 8
+    return [[(c, c + C // n) for c in range(0, C, C // n)] for n in (2, 4, 8) if C % (n * q) == 0]
+
+
+def _split_config(k):
+    """Config k's bytes; the packed fp4 families at widths that split (512 columns: 2, 4 and 8 shards;
+    320 columns: 2 shards), as their small forms have none."""
+    if k in (4, 7):
+        from synth import configs
+        from synth.st_writer import build_bytes
+        groups, meta, pad = (configs.nvfp4 if k == 4 else configs.mxfp4)(seed=k, layers=2, big=512, small=320)
+        return build_bytes(groups, meta, pad)
+    return synth.config_bytes(k, small=k != 1)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("k", [1, 2, 4, 5, 7])
+def test_split_shards_match_the_oracle(k, out_dtype):
+    """Complete shard sets of every 2-d output that allows them (one split descriptor each: the source
+    read whole, each chunk stored to its shard), through the slices instance's fast path and through
+    the plain instance's per-element path, against the oracle's whole output."""
+    buf = _split_config(k)
+    want = oracle.materialize(buf, out_dtype)
+    ix = st.SafeTensorIndex.from_bytes(buf, out_dtype=out_dtype)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    ck.load_bytes(buf[ix.data_offset:])
+    outs = ix.outputs()
+    sets = [(kk, cols) for kk, o in enumerate(outs) for cols in _split_sets(o)][:120]
+    assert sets, "no output allows a split"
+    slices = [(kk, None, c) for kk, cols in sets for c in cols]
+    raw, units = ix.table_slices(slices)
+    n_desc = int(np.frombuffer(raw[:8], "<u4")[1])
+    n_split = sum(outs[kk].kind in SPLIT_KINDS for kk, _ in sets)
+    assert n_split, "no set of a split kind"
+    # one split descriptor per set of a split kind, one descriptor per shard otherwise
+    assert n_desc == sum(1 if outs[kk].kind in SPLIT_KINDS else len(cols) for kk, cols in sets), n_desc
+    bits = {"f32": torch.int32}.get(out_dtype, torch.int16)
+    for strided_kernel in (True, False):
+        print(f"split c{k} {out_dtype}: {len(sets)} sets, {len(slices)} shards, slices instance {strided_kernel}",
+              flush=True)
+        got = ck.materialize_slices(slices, strided_kernel=strided_kernel)
+        torch.cuda.synchronize()
+        for (kk, _, (c0, c1)), t in zip(slices, got):
+            w = want[outs[kk].name].reshape(outs[kk].shape[0], -1)
+            g = t.view(bits).cpu().numpy().view(w.dtype)
+            assert np.array_equal(g, w[:, c0:c1]), (outs[kk].name, c0, c1, strided_kernel)
+
+
+def test_split_shards_with_misaligned_outputs():
+    """A shard whose output is 2 bytes off a 16-byte boundary takes the per-element path; the other
+    shards of the set keep the fast path; all equal the oracle."""
+    buf = _split_config(4)
+    want = oracle.materialize(buf)
+    ix, ck = _staged(buf)
+    outs = ix.outputs()
+    kk = next(j for j, o in enumerate(outs) if _split_sets(o) and len(_split_sets(o)[-1]) == 8)
+    o = outs[kk]
+    cols = _split_sets(o)[-1]
+    slices = [(kk, None, c) for c in cols]
+    R = o.shape[0]
+    sizes = [R * (c1 - c0) for c0, c1 in cols]
+    arena = torch.full((sum(sizes) + 8 * 16,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ptrs, views, pos = [], [], 8
+    for i, n in enumerate(sizes):
+        off = pos + (1 if i == 3 else 0)                     # shard 3 sits 2 bytes off 16
+        ptrs.append(arena.data_ptr() + 2 * off)
+        views.append(arena[off: off + n])
+        pos = off + n + 8 - (off + n) % 8 + 8
+    raw, units = ix.table_slices(slices)
+    table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
+    p = torch.tensor(ptrs, dtype=torch.int64, device=DEV)
+    st.materialize(ck.blob, table, units, p, slices=True)
+    torch.cuda.synchronize()
+    w = want[o.name].reshape(R, -1)
+    for (c0, c1), v in zip(cols, views):
+        assert np.array_equal(_bits(v).reshape(R, c1 - c0), w[:, c0:c1]), (c0, c1)
+
+
+def test_split_fp4_shards_of_a_large_weight():
+    """Complete 8-way shard sets of large NVFP4 and MXFP4 weights (many full units; index from the
+    header, random bytes on the GPU): one split descriptor each, every shard equal to its block of the
+    whole decode."""
+    from synth.st_writer import Group, TensorSpec, layout
+    m, k = 1536, 5120
+    spec = [("a.weight", "U8", (m, k // 2)), ("a.weight_scale", "F8_E4M3", (m, k // 16)), ("a.weight_scale_2", "F32", ()),
+            ("b.weight", "U8", (m, k // 2)), ("b.weight_scale", "F8_E8M0", (m, k // 32))]
+    lay = layout([Group([TensorSpec(n, d, s_)], None) for n, d, s_ in spec])
+    ix = st.SafeTensorIndex.from_bytes(lay.header, file_size=len(lay.header) + lay.data_size)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(23)
+    for name, (lo, hi) in (("a.weight", (0, 256)), ("b.weight", (0, 256)), ("a.weight_scale", (0x08, 0x68)),
+                           ("b.weight_scale", (115, 130))):
+        b, e = lay.offsets[name]
+        ck.blob[b:e] = torch.randint(lo, hi, (e - b,), device=DEV, dtype=torch.uint8, generator=gen)
+    gb, ge = lay.offsets["a.weight_scale_2"]
+    ck.blob[gb:ge] = torch.tensor([0.0171], device=DEV).view(torch.uint8)
+    ck.materialize()
+    outs = ix.outputs()
+    slices = [(j, None, (c, c + k // 8)) for j in range(2) for c in range(0, k, k // 8)]
+    raw, units = ix.table_slices(slices)
+    assert int(np.frombuffer(raw[:8], "<u4")[1]) == 2
+    got = ck.materialize_slices(slices)
+    torch.cuda.synchronize()
+    for (j, _, (c0, c1)), t in zip(slices, got):
+        whole = ck.tensors[outs[j].name]
+        assert torch.equal(t.view(torch.int16), whole[:, c0:c1].view(torch.int16)), (j, c0, c1)

@@ -129,32 +129,82 @@ SIBLING_CASES = {
     "mxfp4": [("w.weight", "U8", (2048, 4096)), ("w.weight_scale", "F8_E8M0", (2048, 256)), ("b.weight", "BF16", (100,))],
     "fp8": [("w.weight", "F8_E4M3", (4096, 3072)), ("w.scale_weight", "F32", ()), ("b.weight", "BF16", (100,))],
     "mxfp8": [("w.weight", "F8_E4M3", (2048, 4096)), ("w.weight_scale", "F8_E8M0", (2048, 128)), ("b.weight", "BF16", (100,))],
+    "bf16": [("w.weight", "BF16", (1024, 2048)), ("b.weight", "BF16", (100,))],
 }
+SPLIT_CASES = ("fp8", "mxfp4", "nvfp4")   # the kinds whose complete shard sets are split
+
+
+def _descs_by_out(d):
+    return [int(r["out"]) for r in d]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_complete_shard_sets_become_split_descriptors(case):
+    """Every column shard of a weight, equal widths, in column order, listed together: one split
+    descriptor (source rows read whole, shard s written to outs[out + s]) covering the shards' units;
+    other slices keep their own descriptors in request order."""
+    ix = _header_index(SIBLING_CASES[case])
+    o = ix.output(0)
+    C = o.shape[1]
+    for n in (2, 4, 8):
+        W = C // n
+        slices = [(1, None, None)] + [(0, None, (c, c + W)) for c in range(0, C, W)] + [(0, (0, 3), None)]
+        raw, units = ix.table_slices(slices)
+        h, d, m = _table(raw)
+        assert len(d) == 3 and _descs_by_out(d) == [0, 1, n + 1]
+        sd = d[1]
+        assert sd["flags"] == _lib.DESC_SPLIT and sd["pitch"] == C and sd["cols"] == W
+        assert sd["grid_cols"] == n.bit_length() - 1
+        R = o.shape[0]
+        shift = int(sd["unit_shift"])
+        assert int(sd["unit_end"]) - int(sd["unit_begin"]) == -(-R * C // (1 << shift))
+        ents = ix.tensors()
+        assert sd["src"] == ents[o.tensor].begin            # whole rows from the first
+        # the unit map still points every group at the descriptor holding its first unit
+        ends = d["unit_end"].astype(np.int64)
+        starts = np.concatenate([[0], ends[:-1]])
+        for g, di in enumerate(m):
+            assert starts[di] <= g * _lib.UNITS_PER_GROUP < ends[di]
 
 
 @pytest.mark.parametrize("case", sorted(SIBLING_CASES))
-def test_sibling_column_slices_interleave_in_bands(case):
-    """8-way column shards of a weight (plus a row slice and a lone column slice): sibling column
-    slices of packed fp4 weights are placed band by band, other kinds keep the request order; each
-    slice's descriptors cover its units exactly once with the right element offsets, and the map
-    stays valid."""
+def test_shards_that_are_not_a_complete_set_interleave_or_keep_order(case):
+    """Shards listed in reverse order, or three of a weight, are not split: packed fp4 siblings
+    interleave band by band, other kinds keep the request order; each slice's units are covered
+    exactly once with the right element offsets."""
     from tests.test_index import _check_map
     ix = _header_index(SIBLING_CASES[case])
     o = ix.output(0)
     kind, cols = o.kind, o.shape[1]
-    q = 16 if kind == "NVFP4" else 32 if kind in ("MXFP8", "MXFP4") else 8
     step = cols // 8
-    slices = [(0, None, (c, c + step)) for c in range(0, cols, step)]
-    slices += [(0, (0, 3), None), (0, (1, 5), (0, q)), (1, None, None)]
+    for slices in ([(0, None, (c, c + step)) for c in range(0, cols, step)][::-1],
+                   [(0, None, (c, c + step)) for c in range(0, 3 * step, step)]):
+        slices = slices + [(1, None, None)]
+        raw, units = ix.table_slices(slices)
+        h, d, m = _table(raw)
+        numels = [ix.slice_shape(*sl)[0] * ix.slice_shape(*sl)[1] for sl in slices]
+        _check_map(d, m, units, numels)
+        assert not any(int(r["flags"]) & _lib.DESC_SPLIT for r in d)
+        outs = _descs_by_out(d)
+        nsh = len(slices) - 1
+        if kind in ("NVFP4", "MXFP4"):
+            assert outs[: 2 * nsh] == list(range(nsh)) * 2     # band 0 of every shard, then band 1
+            shard_units = -(-numels[0] // (1 << int(d[0]["unit_shift"])))
+            assert len(d) == nsh * -(-shard_units // 16) + 1
+        else:
+            assert outs == list(range(len(slices)))
+
+
+@pytest.mark.parametrize("case", ["block_fp8", "mxfp8", "bf16"])
+def test_other_kinds_keep_one_descriptor_per_shard(case):
+    """Complete shard sets of the kinds outside the split set (block FP8, MXFP8, bf16) keep one
+    descriptor per shard, in request order."""
+    spec = ([("w.weight", "F8_E4M3", (1024, 2048)), ("w.weight_scale_inv", "F32", (8, 16))] if case == "block_fp8"
+            else SIBLING_CASES[case])
+    ix = _header_index(spec)
+    C = ix.output(0).shape[1]
+    slices = [(0, None, (c, c + C // 8)) for c in range(0, C, C // 8)]
     raw, units = ix.table_slices(slices)
     h, d, m = _table(raw)
-    numels = [ix.slice_shape(*sl)[0] * ix.slice_shape(*sl)[1] for sl in slices]
-    _check_map(d, m, units, numels)
-    outs = [int(r["out"]) for r in d]
-    if kind in ("NVFP4", "MXFP4"):
-        assert outs[:16] == list(range(8)) * 2          # band 0 of every shard, then band 1, ...
-        shard_units = -(-numels[0] // (1 << int(d[0]["unit_shift"])))
-        assert len(d) == 8 * -(-shard_units // 16) + 3       # bands of 16 units, plus the 3 others
-        assert outs[-3:] == [8, 9, 10]                    # the other slices, whole, in request order
-    else:
-        assert outs == list(range(len(slices)))
+    assert len(d) == 8 and not any(int(r["flags"]) & _lib.DESC_SPLIT for r in d)
+    assert _descs_by_out(d) == list(range(8))
