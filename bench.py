@@ -135,6 +135,8 @@ def parse():
                     help="also measure, for the main config, the serial vs streamed end-to-end load, on-demand "
                          "per-layer loads and tensor-parallel shard decodes (they launch the kernel on other tables, "
                          "so a kernel-trace summary of the default command covers only the timed decode)")
+    ap.add_argument("--shards", action="store_true",
+                    help="also time the 8-way tensor-parallel shard decodes of the main config (part of --extras)")
     ap.add_argument("--out-types", action="store_true",
                     help="also time the fp16 and fp32 output types on the same checkpoint")
     ap.add_argument("--tmpdir", default=None)
@@ -271,7 +273,7 @@ def measure(k, d, args, rng, overrides=None):
     ok, checked, bad = sampled_parity(path, ix, ck, rng)
     log(f"[bench] sampled parity vs oracle: {'ok' if ok else 'MISMATCH in ' + str(bad)} ({checked} elements)")
     shards = None
-    if k == args.config and args.extras:
+    if k == args.config and (args.extras or args.shards):
         shards = tp_shards(ix, ck, max(3, args.steps // 5))
         log(f"[bench] tensor-parallel shards: {shards}")
     # timed region: K back-to-back launches, wall clock + per-launch HIP events on the same stream
