@@ -228,6 +228,33 @@ def test_split_shards_match_the_oracle(k, out_dtype):
             assert np.array_equal(g, w[:, c0:c1]), (outs[kk].name, c0, c1, strided_kernel)
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [1, 3])
+@pytest.mark.parametrize("k", [2, 4, 7])
+def test_split_shards_with_larger_units(k, scale, out_dtype):
+    """Complete shard sets planned with units 2^scale times the default: every unit of a split
+    descriptor takes the chunk-walking path (whole units of the default size take the other), against
+    the oracle's whole output."""
+    buf = _split_config(k)
+    want = oracle.materialize(buf, out_dtype)
+    ix = st.SafeTensorIndex.from_bytes(buf, unit_log2_scale=scale, out_dtype=out_dtype)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    ck.load_bytes(buf[ix.data_offset:])
+    outs = ix.outputs()
+    sets = [(kk, cols) for kk, o in enumerate(outs) for cols in _split_sets(o) if o.kind in SPLIT_KINDS][:60]
+    assert sets
+    slices = [(kk, None, c) for kk, cols in sets for c in cols]
+    raw, units = ix.table_slices(slices)
+    assert int(np.frombuffer(raw[:8], "<u4")[1]) == len(sets)
+    print(f"split c{k} units x{1 << scale} {out_dtype}: {len(sets)} sets, {len(slices)} shards", flush=True)
+    got = ck.materialize_slices(slices)
+    torch.cuda.synchronize()
+    bits = {"f32": torch.int32}.get(out_dtype, torch.int16)
+    for (kk, _, (c0, c1)), t in zip(slices, got):
+        w = want[outs[kk].name].reshape(outs[kk].shape[0], -1)
+        assert np.array_equal(t.view(bits).cpu().numpy().view(w.dtype), w[:, c0:c1]), (outs[kk].name, c0, c1)
+
+
 def test_split_shards_with_misaligned_outputs():
     """A shard whose output is 2 bytes off a 16-byte boundary takes the per-element path; the other
     shards of the set keep the fast path; all equal the oracle."""
