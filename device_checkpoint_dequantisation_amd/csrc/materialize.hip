@@ -889,24 +889,24 @@ __device__ __forceinline__ void split_store(const Ctx& c, const uint32_t* in, ui
 // Lane l loads shard (l mod 2^grid_cols)'s output pointer once; each chunk takes its shard's from
 // that lane.  Every lane of the wave is active here (the unit test is wave-uniform), as that
 // cross-lane read needs.  As in unit_full, chunks the fast path cannot take go element by element
-// after all the fast stores.
-template <class K, class O, bool ALIGNED>
+// after all the fast stores.  MUL: the unit is MUL times the default size (MUL * CH chunks a lane).
+template <class K, class O, bool ALIGNED, uint32_t MUL>
 __device__ __forceinline__ void unit_split_full(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
     using F = Fetch<K, ALIGNED>;
-    constexpr uint32_t NW = K::CE * O::BYTES / 4;
+    constexpr uint32_t NW = K::CE * O::BYTES / 4, CH = K::CH * MUL;
     const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
-    uint32_t raw[K::CH][F::RW];
+    uint32_t raw[CH][F::RW];
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
+    for (uint32_t j = 0; j < CH; ++j) F::load(base, j * stk::kWave + lane, raw[j]);
     const uint64_t mine =
         reinterpret_cast<uint64_t>(c0.outs[c0.D.out + (lane & ((1u << c0.D.grid_cols) - 1u))]);
     __builtin_amdgcn_sched_barrier(0);
     Ctx c = c0;
     uint8_t* first;
     (void)finish_ctx<K, O>(c, first);  // the scalar scale; the shards' pointers are checked below
-    bool ok[K::CH], vec = false;
+    bool ok[CH], vec = false;
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) {
+    for (uint32_t j = 0; j < CH; ++j) {
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
         const uint32_t s = late_sc<K>(c, e, e);
         // every shard 16-byte aligned; taken after the first scale load is issued, so that one wait
@@ -927,10 +927,10 @@ __device__ __forceinline__ void unit_split_full(const Ctx& c0, uint64_t e0, uint
     }
     bool all = true;
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) all &= ok[j];
+    for (uint32_t j = 0; j < CH; ++j) all &= ok[j];
     if (__builtin_amdgcn_ballot_w64(!all) == 0) return;  // the common case
 #pragma unroll
-    for (uint32_t j = 0; j < K::CH; ++j) {
+    for (uint32_t j = 0; j < CH; ++j) {
         if (ok[j]) continue;
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
         uint32_t which;
@@ -1021,17 +1021,28 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
         if (SLICES && (D.flags & (ST_DESC_SPLIT | ST_DESC_EXACT)) == ST_DESC_SPLIT && (cnt & 7u) == 0 &&
             stk::split_kind(D.kind)) {
             const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src)), sh = a & 3u;
-            const bool full = cnt == (1u << D.unit_shift) && D.unit_shift == stk::step_shift(D.kind, O::CODE);
+            // whole units of the default size, or of twice it (the 8-bit kinds' split units)
+            const uint32_t step = stk::step_shift(D.kind, O::CODE);
+            const uint32_t full = cnt != (1u << D.unit_shift) ? 0u : D.unit_shift == step ? 1u : D.unit_shift == step + 1 ? 2u : 0u;
             switch (D.kind) {
-#define ST_SPLIT_CASE(KIND_, K_)                                                           \
-    case KIND_:                                                                            \
-        if (!full) unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                           \
-        else if ((a & (K_<O>::LG - 1)) == 0) unit_split_full<K_<O>, O, true>(c, e0, 0, lane);  \
-        else unit_split_full<K_<O>, O, false>(c, e0, sh, lane);                              \
+#define ST_SPLIT_CASE(KIND_, K_)                                                                  \
+    case KIND_:                                                                                   \
+        static_assert(stk::split_kind(KIND_), "a split kind");                                    \
+        {                                                                                         \
+            const bool al_ = (a & (K_<O>::LG - 1)) == 0;                                          \
+            if (full == 1) al_ ? unit_split_full<K_<O>, O, true, 1>(c, e0, 0, lane)                \
+                               : unit_split_full<K_<O>, O, false, 1>(c, e0, sh, lane);             \
+            else if constexpr (stk::split_wide(KIND_)) {                                          \
+                if (full == 2) al_ ? unit_split_full<K_<O>, O, true, 2>(c, e0, 0, lane)            \
+                                   : unit_split_full<K_<O>, O, false, 2>(c, e0, sh, lane);         \
+                else unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                              \
+            } else unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                                \
+        }                                                                                         \
         break;
                 ST_SPLIT_CASE(ST_KIND_FP8_TENSOR, KFp8Tensor)
                 ST_SPLIT_CASE(ST_KIND_NVFP4, KFp4)
                 ST_SPLIT_CASE(ST_KIND_MXFP4, KMx4)
+                ST_SPLIT_CASE(ST_KIND_MXFP8, KMx8)
 #undef ST_SPLIT_CASE
                 default: break;  // not a split kind
             }

@@ -63,12 +63,15 @@ constexpr uint32_t load_word_bytes(uint32_t kind) {
 }
 // Kinds whose complete column-shard sets are planned as split descriptors (the source rows read
 // whole, each chunk stored to its shard).  On 8-way shards of the large checkpoints this beat one
-// descriptor per shard by 9% (NVFP4), 6% (MXFP4) and 5% (scaled FP8); it lost 1.5% (MXFP8) and 4%
-// (bf16), whose waves carry fewer chunks to spread the per-wave shard-pointer work over, and block
-// FP8's scale grid needs the shard's own columns.
+// descriptor per shard by 9% (NVFP4), 6% (MXFP4), 6% (scaled FP8) and 3% (MXFP8); it lost 4% on
+// bf16 (and far more with wide units), and block FP8's scale grid needs the shard's own columns.
 constexpr bool split_kind(uint32_t kind) {
-    return kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4 || kind == ST_KIND_FP8_TENSOR;
+    return kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4 || kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_MXFP8;
 }
+// Split descriptors of the 8-bit kinds take units of twice the default size: their waves carry half
+// the chunks per lane of the packed fp4 kinds, and the doubled unit spreads the per-wave shard-pointer
+// work over as many (MXFP8 at the default size lost 1% to per-shard descriptors; doubled it gains 3%).
+constexpr bool split_wide(uint32_t kind) { return kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_MXFP8; }
 // Source bits per element.
 constexpr uint32_t source_bits(uint32_t kind) {
     return kind == ST_KIND_CAST_F32 ? 32

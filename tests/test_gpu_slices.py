@@ -172,7 +172,7 @@ def test_interleaved_fp4_column_shards_match_the_whole_decode(kind):
     assert np.array_equal(g, want)
 
 
-SPLIT_KINDS = ("FP8_TENSOR", "NVFP4", "MXFP4")   # kinds whose complete shard sets become split descriptors
+SPLIT_KINDS = ("FP8_TENSOR", "NVFP4", "MXFP4", "MXFP8")   # kinds whose complete shard sets become split descriptors
 
 
 def _split_sets(o):
@@ -196,7 +196,7 @@ def _split_config(k):
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("k", [1, 2, 4, 5, 7])
+@pytest.mark.parametrize("k", [1, 2, 4, 5, 6, 7])
 def test_split_shards_match_the_oracle(k, out_dtype):
     """Complete shard sets of every 2-d output that allows them (one split descriptor each: the source
     read whole, each chunk stored to its shard), through the slices instance's fast path and through
@@ -230,7 +230,7 @@ def test_split_shards_match_the_oracle(k, out_dtype):
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [1, 3])
-@pytest.mark.parametrize("k", [2, 4, 7])
+@pytest.mark.parametrize("k", [2, 4, 6, 7])
 def test_split_shards_with_larger_units(k, scale, out_dtype):
     """Complete shard sets planned with units 2^scale times the default: every unit of a split
     descriptor takes the chunk-walking path (whole units of the default size take the other), against
