@@ -980,6 +980,16 @@ __device__ __forceinline__ void run_unit(const Ctx& c, uint64_t e0, uint32_t cnt
 
 // ------------------------------------------------------------------------- the kernel
 
+// The split kinds as a bit mask (bit k set when stk::split_kind(k)): the kernel tests a descriptor's
+// kind against it instead of calling the shared predicate, which the compiler left out of line in
+// the large kernels.
+constexpr uint32_t split_kind_mask() {
+    uint32_t m = 0;
+    for (uint32_t k = 0; k < 32; ++k) m |= uint32_t(stk::split_kind(k)) << k;
+    return m;
+}
+constexpr uint32_t kSplitKinds = split_kind_mask();
+
 // SLICES: the instance that runs column slices through the strided fast path.  The plain instance
 // sends them (and exact-only descriptors) through the per-element exact path; keeping the strided
 // code out of it was measured to matter (2-5% on the whole-checkpoint decode).  O: the output
@@ -1019,16 +1029,17 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     c.scale_al = (D.scale & 3u) == 0;
     if ((D.pitch | D.flags) != 0) {  // column slices, split descriptors and exact-only descriptors
         if (SLICES && (D.flags & (ST_DESC_SPLIT | ST_DESC_EXACT)) == ST_DESC_SPLIT && (cnt & 7u) == 0 &&
-            stk::split_kind(D.kind)) {
+            ((kSplitKinds >> D.kind) & 1u)) {
             const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src)), sh = a & 3u;
-            // whole units of the default size, or of twice it (the 8-bit kinds' split units)
-            const uint32_t step = stk::step_shift(D.kind, O::CODE);
-            const uint32_t full = cnt != (1u << D.unit_shift) ? 0u : D.unit_shift == step ? 1u : D.unit_shift == step + 1 ? 2u : 0u;
             switch (D.kind) {
+            // whole units of the default size (full_ 1), or of twice it (2: the 8-bit kinds' split units)
 #define ST_SPLIT_CASE(KIND_, K_)                                                                  \
     case KIND_:                                                                                   \
         static_assert(stk::split_kind(KIND_), "a split kind");                                    \
         {                                                                                         \
+            constexpr uint32_t step_ = stk::step_shift(KIND_, O::CODE);                           \
+            const uint32_t full = cnt != (1u << D.unit_shift) ? 0u : D.unit_shift == step_ ? 1u    \
+                                : D.unit_shift == step_ + 1 ? 2u : 0u;                            \
             const bool al_ = (a & (K_<O>::LG - 1)) == 0;                                          \
             if (full == 1) al_ ? unit_split_full<K_<O>, O, true, 1>(c, e0, 0, lane)                \
                                : unit_split_full<K_<O>, O, false, 1>(c, e0, sh, lane);             \
