@@ -452,6 +452,7 @@ def tp_shards(ix, ck, steps, n=8):
     of every 2-d output (and every other output whole), as one GPU of an n-way tensor-parallel
     group would; its GB/s counts that table's own algorithmic bytes."""
     import torch
+    import device_checkpoint_dequantisation_amd as st
     outs = ix.outputs()
     res = {}
     for label, axis in (("row_shards", 0), ("col_shards", 1), ("col_shard_one", 1)):
@@ -478,11 +479,11 @@ def tp_shards(ix, ck, steps, n=8):
         base = arena.data_ptr()
         ptrs = torch.tensor([base + o for o in offs], dtype=torch.int64).to(ck.device)
         raw, units = ix.table_slices(slices)
+        nt = st.table_stream_stores(raw)
         strided = axis == 1  # column shards need the strided kernel; row shards are contiguous
         table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(ck.device)
         stream = torch.cuda.current_stream(ck.device)
-        import device_checkpoint_dequantisation_amd as st
-        st.materialize(ck.blob, table, units, ptrs, stream, slices=strided)
+        st.materialize(ck.blob, table, units, ptrs, stream, slices=strided, stream_stores=nt)
         torch.cuda.synchronize()
         ok = True
         for (k, rows, cols), (r, c), off in zip(slices, shapes, offs):
@@ -495,7 +496,7 @@ def tp_shards(ix, ck, steps, n=8):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in evs:
             a.record(stream)
-            st.materialize(ck.blob, table, units, ptrs, stream, slices=strided)
+            st.materialize(ck.blob, table, units, ptrs, stream, slices=strided, stream_stores=nt)
             b.record(stream)
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))

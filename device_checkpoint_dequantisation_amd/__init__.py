@@ -18,7 +18,7 @@ import json
 import os
 from dataclasses import dataclass
 
-from ._lib import (DTYPES, KINDS, MAT_SLICES, OUT_DTYPES, PLAN_PACK, TABLE_MAGIC, Desc, OutputInfo,  # noqa: F401
+from ._lib import (DTYPES, KINDS, MAT_SLICES, MAT_STREAM_STORES, TABLE_STREAM_STORES, OUT_DTYPES, PLAN_PACK, TABLE_MAGIC, Desc, OutputInfo,  # noqa: F401
                    PlanOpts, Slice, StError, StreamStats, StreamStep, TableHeader, TensorMeta, check, lib)
 
 __all__ = ["SafeTensorIndex", "StreamPlan", "DeviceCheckpoint", "QuantizedWeight", "load", "materialize",
@@ -287,9 +287,16 @@ def _torch():
     return torch
 
 
-def check_table(raw: bytes, units: int, out_dtype: str):
+def table_stream_stores(raw, offset: int = 0) -> bool:
+    """Whether the work table at ``offset`` of the host bytes ``raw`` asks for non-temporal output
+    stores (ST_TABLE_STREAM_STORES: its outputs are larger than the last-level cache)."""
+    return bool(TableHeader.from_buffer_copy(bytes(raw[offset:offset + 64])).flags & TABLE_STREAM_STORES)
+
+
+def check_table(raw: bytes, units: int, out_dtype: str) -> bool:
     """Raise ValueError unless the host copy ``raw`` of a work table records ``units`` work units
-    and the output type ``out_dtype``: the kernel would leave every output unwritten otherwise."""
+    and the output type ``out_dtype``: the kernel would leave every output unwritten otherwise.
+    Returns the table's store policy (table_stream_stores)."""
     if len(raw) < 64:
         raise ValueError(f"work table of {len(raw)} bytes has no header")
     h = TableHeader.from_buffer_copy(bytes(raw[:64]))
@@ -299,6 +306,7 @@ def check_table(raw: bytes, units: int, out_dtype: str):
         raise ValueError(f"work table holds {h.units} units, the launch was given {units}")
     if h.out_dtype >= len(OUT_DTYPES) or OUT_DTYPES[h.out_dtype] != out_dtype:
         raise ValueError(f"work table was planned for output type code {h.out_dtype}, the launch asks for {out_dtype}")
+    return bool(h.flags & TABLE_STREAM_STORES)
 
 
 def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> float:
@@ -311,15 +319,18 @@ def stage_file(path: str, index: SafeTensorIndex, blob, pinned, side_stream) -> 
     return secs.value
 
 
-def materialize(blob, table, units: int, outs, stream=None, slices: bool = False, out_dtype: str = "bf16"):
+def materialize(blob, table, units: int, outs, stream=None, slices: bool = False, out_dtype: str = "bf16",
+                stream_stores: bool = False):
     """Enqueue the grouped kernel (st_materialize_as): ``blob`` (the staged data section),
     ``table`` (a work table) and ``outs`` (device pointers, int64) are device tensors; ``units`` is
     the table's work-unit count; ``out_dtype`` the output type the table was planned for;
-    ``slices`` selects the kernel with the strided path for column slices."""
+    ``slices`` selects the kernel with the strided path for column slices; ``stream_stores`` the
+    non-temporal stores its header asks for (table_stream_stores)."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(blob.device)
+    flags = (MAT_SLICES if slices else 0) | (MAT_STREAM_STORES if stream_stores else 0)
     check(lib().st_materialize_as(C.c_void_p(blob.data_ptr()), C.c_void_p(table.data_ptr()), units,
-                                  C.c_void_p(outs.data_ptr()), OUT_DTYPES.index(out_dtype), MAT_SLICES if slices else 0,
+                                  C.c_void_p(outs.data_ptr()), OUT_DTYPES.index(out_dtype), flags,
                                   C.c_void_p(s.cuda_stream)), "st_materialize_as")
 
 
@@ -444,7 +455,7 @@ class DeviceCheckpoint:
                 raise MemoryError(f"checkpoint needs {need} bytes of device memory; {free} of {total} are free")
         self.blob = torch.empty(index.blob_bytes, dtype=torch.uint8, device=self.device)
         table, units = index.table()
-        check_table(table, units, index.out_dtype)
+        self.stream_stores = check_table(table, units, index.out_dtype)
         self.units = units
         self.table = torch.frombuffer(bytearray(table), dtype=torch.uint8).to(self.device)
         dt = index.torch_dtype
@@ -535,7 +546,7 @@ class DeviceCheckpoint:
         shapes = [self.index.slice_shape(*((sl + (None, None))[:3] if isinstance(sl, tuple) else (sl,))) for sl in slices]
         outs = [torch.empty(shp, dtype=self.index.torch_dtype, device=self.device) for shp in shapes]
         raw, units = self.index.table_slices(slices)
-        check_table(raw, units, self.index.out_dtype)
+        stream_stores = check_table(raw, units, self.index.out_dtype)
         if strided_kernel is None:
             strided_kernel = self.index.has_column_slices(slices)
         table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
@@ -544,7 +555,8 @@ class DeviceCheckpoint:
             s = self._launch_stream(stream)
             for t in [table, ptrs] + outs:  # allocated on the current stream, used on s
                 t.record_stream(s)
-            materialize(self.blob, table, units, ptrs, s, slices=strided_kernel, out_dtype=self.index.out_dtype)
+            materialize(self.blob, table, units, ptrs, s, slices=strided_kernel, out_dtype=self.index.out_dtype,
+                        stream_stores=stream_stores)
         return outs
 
     def _launch_stream(self, stream):
@@ -560,7 +572,7 @@ class DeviceCheckpoint:
     def materialize(self, stream=None):
         if self.units:
             materialize(self.blob, self.table, self.units, self.outs, self._launch_stream(stream),
-                        out_dtype=self.index.out_dtype)
+                        out_dtype=self.index.out_dtype, stream_stores=self.stream_stores)
         return self.tensors
 
 

@@ -11,6 +11,8 @@ ST_MAX_NDIM = 8
 KINDS = ("PASS_BF16", "CAST_F16", "CAST_F32", "FP8_TENSOR", "FP8_BLOCK128", "NVFP4", "MXFP8", "MXFP4")
 OUT_DTYPES = ("bf16", "f16", "f32")   # st_out_dtype codes 0, 1, 2
 MAT_SLICES = 1
+MAT_STREAM_STORES = 2        # st_materialize_as flag: non-temporal output stores
+TABLE_STREAM_STORES = 1      # st_table_header.flags: outputs larger than the last-level cache
 DTYPES = ("BOOL", "U8", "I8", "F8_E4M3", "F8_E5M2", "F8_E8M0", "I16", "U16", "F16", "BF16", "I32", "U32", "F32",
           "I64", "U64", "F64", "F4", "F6_E2M3", "F6_E3M2")
 STATUS = {0: "ST_OK", -1: "ST_E_ARG", -2: "ST_E_IO", -3: "ST_E_HEADER", -4: "ST_E_JSON", -5: "ST_E_DTYPE",
@@ -40,7 +42,7 @@ assert C.sizeof(Desc) == 64
 
 class TableHeader(C.Structure):
     _fields_ = [("magic", C.c_uint32), ("n_desc", C.c_uint32), ("units", C.c_uint64), ("desc_offset", C.c_uint64),
-                ("map_offset", C.c_uint64), ("bytes", C.c_uint64), ("out_dtype", C.c_uint32), ("reserved0", C.c_uint32),
+                ("map_offset", C.c_uint64), ("bytes", C.c_uint64), ("out_dtype", C.c_uint32), ("flags", C.c_uint32),
                 ("reserved", C.c_uint64 * 2)]
 
 

@@ -618,7 +618,14 @@ namespace {
 
 // A work table from descriptors whose unit ranges are set, `units` in total: header, map,
 // descriptors.
-std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units, uint32_t out_dtype) {
+// Outputs larger than this (the MI355X's 256 MiB Infinity Cache) are written with non-temporal
+// stores.  Measured against plain stores: +1 to +3% on the large checkpoints and their row shards,
+// +6 to +9% on one rank's column shards; on the many-small checkpoint (211 MB of outputs) plain
+// stores leave the outputs in that cache and the launch 10% shorter after a flush.
+constexpr uint64_t kStreamStoreBytes = uint64_t(256) << 20;
+
+std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units, uint32_t out_dtype,
+                                    uint64_t out_bytes) {
     const size_t k = descs.size();
     const uint64_t groups = (units + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP;
     st_table_header h;
@@ -630,6 +637,7 @@ std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t 
     h.desc_offset = stk::table_desc_offset(groups);
     h.bytes = h.desc_offset + k * sizeof(st_desc);
     h.out_dtype = out_dtype;
+    h.flags = out_bytes > kStreamStoreBytes ? ST_TABLE_STREAM_STORES : 0u;
     std::vector<unsigned char> t(h.bytes, 0);
     memcpy(t.data(), &h, sizeof h);
     if (k) memcpy(t.data() + h.desc_offset, descs.data(), k * sizeof(st_desc));
@@ -737,7 +745,9 @@ std::vector<unsigned char> sti::build_table(const st_index& ix, const uint32_t* 
             pos += pc.count;
         }
     *units_out = pos;
-    return assemble(descs, pos, ix.out_dtype);
+    uint64_t out_bytes = 0;
+    for (size_t j = 0; j < k; ++j) out_bytes += ix.outputs[sel[j]].numel * sti::out_bytes(ix);
+    return assemble(descs, pos, ix.out_dtype, out_bytes);
 }
 
 namespace {
@@ -1228,8 +1238,10 @@ extern "C" st_status st_index_table_slices(const st_index* idx, const st_slice* 
             pos += nu[j];
             if (pos >= (uint64_t(1) << 32)) return st_fail(ST_E_SHAPE, "st_index_table_slices: 2^32 or more work units");
         }
+        uint64_t out_bytes = 0;
+        for (size_t j = 0; j < k; ++j) out_bytes += gs[j].rows() * gs[j].cols() * sti::out_bytes(*idx);
         descs = interleave_column_slices(*idx, descs, nu, gs, slices, &pos);
-        t = assemble(descs, pos, idx->out_dtype);
+        t = assemble(descs, pos, idx->out_dtype, out_bytes);
     } catch (const std::bad_alloc&) {
         return st_fail(ST_E_NOMEM, "out of host memory");
     } catch (const std::length_error& e) {

@@ -65,6 +65,8 @@ static __device__ __align__(256) uint8_t scratch[ST_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// A 16-byte word through an explicitly global pointer.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
@@ -189,6 +191,13 @@ struct OutF16 {
 struct OutF32 {
     static constexpr uint32_t BYTES = 4, CODE = ST_OUT_F32;
     static __device__ __forceinline__ uint32_t exact(float f) { return f32_canon(f); }
+};
+// An output type with the kernel instance's store policy: NT, non-temporal 16-byte output stores
+// (ST_MAT_STREAM_STORES).  A compile-time constant: a run-time choice between the two stores does
+// not survive compilation, as the compiler merges them into one plain store.
+template <class Base, bool NT_>
+struct Stored : Base {
+    static constexpr bool NT = NT_;
 };
 
 // Output words of a chunk: pair k of values goes to word k (2-byte types) or words 2k, 2k+1.
@@ -622,6 +631,15 @@ __device__ __forceinline__ void run_exact(const Ctx& c, uint8_t* __restrict__ ou
     for (uint32_t k = 0; k < n; ++k) store_elem<O>(out, e + k, kind_exact<KIND, O>(c.blob, c.D, e + k));
 }
 
+// One 16-byte output word.  NT: the table's outputs exceed the last-level cache, so they are stored
+// non-temporally instead of being kept there; smaller tables' outputs stay in that cache for
+// whatever reads them next.
+template <bool NT, class P>
+__device__ __forceinline__ void store_word(P* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // The output words of chunk ci of a unit whose output starts at ob, as 16-byte stores.  ob is
 // wave-uniform and the chunk's offset a 32-bit lane value, so the stores take a scalar base and a
 // 32-bit vector offset (a 64-bit address per lane costs measurably more store bandwidth).
@@ -631,7 +649,7 @@ __device__ __forceinline__ void store_chunk(uint8_t* __restrict__ ob, uint32_t c
     uint8_t* p = ob + ci * (K::CE * O::BYTES);
 #pragma unroll
     for (uint32_t k = 0; k < OW; ++k)
-        *reinterpret_cast<u32x4*>(p + 16 * k) = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+        store_word<O::NT>(reinterpret_cast<u32x4*>(p + 16 * k), u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
 }
 
 // A unit of exactly CH * 64 whole chunks (the default unit size): no per-chunk bounds checks.
@@ -719,8 +737,8 @@ __device__ __forceinline__ void unit_full_paired(const Ctx& c0, uint64_t e0, uin
         ok[j] = K::template quad<0>(c, x, sa, wa) & K::template quad<2>(c, x, sb, wb) & vec;
         if (ok[j]) {
             uint8_t* p = ob + (j * GE + 4 * lane) * O::BYTES;
-            *reinterpret_cast<u32x4*>(p) = u32x4{wa[0], wa[1], wa[2], wa[3]};
-            *reinterpret_cast<u32x4*>(p + GE / 2 * O::BYTES) = u32x4{wb[0], wb[1], wb[2], wb[3]};
+            store_word<O::NT>(reinterpret_cast<u32x4*>(p), u32x4{wa[0], wa[1], wa[2], wa[3]});
+            store_word<O::NT>(reinterpret_cast<u32x4*>(p + GE / 2 * O::BYTES), u32x4{wb[0], wb[1], wb[2], wb[3]});
         }
     }
     bool all = true;
@@ -857,8 +875,6 @@ __device__ __forceinline__ void unit_exact(const Ctx& c, uint64_t e0, uint32_t c
 #pragma unroll 1
     for (uint32_t t = lane; t < cnt; t += stk::kWave) store_elem<O>(out, e0 + t, kind_exact<KIND, O>(c.blob, c.D, e0 + t));
 }
-
-typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 
 // Stores one chunk of a split descriptor to its shard (p: the chunk's output address); chunks the fast
 // path cannot take (NaN inputs, non-finite scales, a shard not 16-byte aligned) go element by element.
@@ -1096,13 +1112,20 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     }
 }
 
-template <bool SLICES, class O>
-void launch(const void* blob, const void* descs, uint32_t n, uint32_t groups, void* const* outs, hipStream_t stream) {
+template <bool SLICES, class O, bool NT>
+void launch_as(const void* blob, const void* descs, uint32_t n, uint32_t groups, void* const* outs, hipStream_t stream) {
     const uint32_t gx = groups < kMaxGridX ? groups : kMaxGridX;
     const uint32_t gy = (groups + gx - 1) / gx;
-    hipLaunchKernelGGL((materialize_kernel<SLICES, O>), dim3(gx, gy), dim3(kBlock), 0, stream,
+    hipLaunchKernelGGL((materialize_kernel<SLICES, Stored<O, NT>>), dim3(gx, gy), dim3(kBlock), 0, stream,
                        static_cast<const uint8_t*>(blob), static_cast<const uint8_t*>(descs), n, groups,
                        uint32_t(stk::table_desc_offset(groups)), reinterpret_cast<uint8_t* const*>(outs));
+}
+
+template <bool SLICES, class O>
+void launch(const void* blob, const void* descs, uint32_t n, uint32_t groups, void* const* outs, hipStream_t stream,
+            bool nt) {
+    nt ? launch_as<SLICES, O, true>(blob, descs, n, groups, outs, stream)
+       : launch_as<SLICES, O, false>(blob, descs, n, groups, outs, stream);
 }
 
 }  // namespace
@@ -1117,22 +1140,22 @@ extern "C" st_status st_materialize_as(const void* blob, const void* descs, size
     if (reinterpret_cast<uintptr_t>(descs) % 64) return st_fail(ST_E_ARG, "%s: work table is not 64-byte aligned", who);
     if (uint64_t(n) >= (uint64_t(1) << 32)) return st_fail(ST_E_ARG, "%s: %zu work units (at most 2^32 - 1)", who, n);
     if (out_dtype > ST_OUT_F32) return st_fail(ST_E_ARG, "%s: unknown output type %u", who, out_dtype);
-    if (flags & ~uint32_t(ST_MAT_SLICES)) return st_fail(ST_E_ARG, "%s: unknown flags 0x%x", who, flags);
+    if (flags & ~uint32_t(ST_MAT_SLICES | ST_MAT_STREAM_STORES)) return st_fail(ST_E_ARG, "%s: unknown flags 0x%x", who, flags);
     const uint32_t groups = uint32_t((uint64_t(n) + ST_UNITS_PER_GROUP - 1) / ST_UNITS_PER_GROUP);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool slices = (flags & ST_MAT_SLICES) != 0;
+    const bool slices = (flags & ST_MAT_SLICES) != 0, nt = (flags & ST_MAT_STREAM_STORES) != 0;
     switch (out_dtype) {
         case ST_OUT_BF16:
-            slices ? launch<true, OutBf16>(blob, descs, uint32_t(n), groups, outs, s)
-                   : launch<false, OutBf16>(blob, descs, uint32_t(n), groups, outs, s);
+            slices ? launch<true, OutBf16>(blob, descs, uint32_t(n), groups, outs, s, nt)
+                   : launch<false, OutBf16>(blob, descs, uint32_t(n), groups, outs, s, nt);
             break;
         case ST_OUT_F16:
-            slices ? launch<true, OutF16>(blob, descs, uint32_t(n), groups, outs, s)
-                   : launch<false, OutF16>(blob, descs, uint32_t(n), groups, outs, s);
+            slices ? launch<true, OutF16>(blob, descs, uint32_t(n), groups, outs, s, nt)
+                   : launch<false, OutF16>(blob, descs, uint32_t(n), groups, outs, s, nt);
             break;
         default:
-            slices ? launch<true, OutF32>(blob, descs, uint32_t(n), groups, outs, s)
-                   : launch<false, OutF32>(blob, descs, uint32_t(n), groups, outs, s);
+            slices ? launch<true, OutF32>(blob, descs, uint32_t(n), groups, outs, s, nt)
+                   : launch<false, OutF32>(blob, descs, uint32_t(n), groups, outs, s, nt);
             break;
     }
     hipError_t e = hipGetLastError();
@@ -1206,6 +1229,7 @@ extern "C" st_status st_materialize_noalloc(const void* blob, const void* table_
     if (hipMemcpyAsync(ptr, table_host, table_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
         (n_outs && hipMemcpyAsync(ptr + outs_off, outs_host, 8 * n_outs, hipMemcpyHostToDevice, s) != hipSuccess))
         return st_fail(ST_E_HIP, "%s: copy into the scratch array failed", who);
+    if (h.flags & ST_TABLE_STREAM_STORES) flags |= ST_MAT_STREAM_STORES;  // the header's store policy
     return st_materialize_as(blob, ptr, n, reinterpret_cast<void* const*>(ptr + outs_off), out_dtype, flags, stream);
 }
 

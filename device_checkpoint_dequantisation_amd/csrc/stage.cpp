@@ -23,6 +23,7 @@
 #include <cerrno>
 #include <chrono>
 #include <condition_variable>
+#include <cstring>
 #include <memory>
 #include <mutex>
 #include <thread>
@@ -346,7 +347,7 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
     if (reinterpret_cast<uintptr_t>(blob_dev) % ST_BLOB_ALIGN)
         return st_fail(ST_E_ARG, "st_stream_file: blob is not %d-byte aligned", ST_BLOB_ALIGN);
     size_t table_bytes = 0, n_order = 0, n_ranges = 0;
-    (void)st_stream_plan_tables(plan, &table_bytes);
+    const unsigned char* tables_host = static_cast<const unsigned char*>(st_stream_plan_tables(plan, &table_bytes));
     (void)st_stream_plan_order(plan, &n_order);
     const st_stream_range* ranges = st_stream_plan_ranges(plan, &n_ranges);
     if (table_bytes && (!tables_dev || reinterpret_cast<uintptr_t>(tables_dev) % 64))
@@ -421,9 +422,11 @@ extern "C" st_status st_stream_file(const char* path, const st_index* idx, const
                 status = st_fail(ST_E_HIP, "st_stream_file: hipStreamWaitEvent failed");
                 break;
             }
+            st_table_header h;  // the step table's store policy, from the plan's host copy
+            memcpy(&h, tables_host + step.table_offset, sizeof h);
             status = st_materialize_as(blob_dev, static_cast<const char*>(tables_dev) + step.table_offset,
-                                       size_t(step.units), outs_dev + step.first_out, st_index_out_dtype(idx), 0,
-                                       compute_stream);
+                                       size_t(step.units), outs_dev + step.first_out, st_index_out_dtype(idx),
+                                       (h.flags & ST_TABLE_STREAM_STORES) ? ST_MAT_STREAM_STORES : 0u, compute_stream);
             if (status != ST_OK) break;
             if (st.launches++ == 0) st.seconds_first_launch = seconds_since(t_call);
         }

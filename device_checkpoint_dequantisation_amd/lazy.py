@@ -21,7 +21,8 @@ import time
 from collections.abc import Mapping
 from dataclasses import dataclass
 
-from . import SafeTensorIndex, StreamPlan, _quantized, _torch, materialize, read_plans, stream_file
+from . import (SafeTensorIndex, StreamPlan, _quantized, _torch, materialize, read_plans, stream_file,
+               table_stream_stores)
 
 _ONE_STEP = 1 << 60  # chunk size that keeps a whole selection in one staging step
 
@@ -475,7 +476,8 @@ class StreamStateDict(Mapping):
                 for step in e.plan.steps:
                     if step.units:
                         materialize(blob[off:], e.table_dev[step.table_offset:], step.units, ptrs[j:], s,
-                                    out_dtype=self.index.out_dtype)
+                                    out_dtype=self.index.out_dtype,
+                                    stream_stores=table_stream_stores(e.plan.tables, step.table_offset))
                         self.stats["launches"] += 1
 
             for m in metas:

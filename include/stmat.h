@@ -136,9 +136,14 @@ typedef struct st_table_header {
     uint64_t map_offset;     /* bytes from the table start to map[0] (always 64) */
     uint64_t bytes;          /* size of the whole table */
     uint32_t out_dtype;      /* st_out_dtype the outputs were planned for */
-    uint32_t reserved0;
+    uint32_t flags;          /* ST_TABLE_STREAM_STORES, or 0 */
     uint64_t reserved[2];
 } st_table_header;           /* 64 bytes */
+/* st_table_header.flags: the table's outputs are larger than the GPU's last-level (Infinity) cache
+ * (256 MiB on MI355X), so they are better written with non-temporal stores than kept there: a
+ * caller that holds the table passes ST_MAT_STREAM_STORES to st_materialize_as when it is set
+ * (st_stream_file and st_materialize_noalloc read it themselves).  Set by the planner. */
+#define ST_TABLE_STREAM_STORES 1u
 
 typedef struct st_desc {
     uint64_t src;            /* weight bytes */
@@ -470,11 +475,17 @@ st_status st_materialize_slices(const void* blob, const void* descs, size_t n, v
                                 void* stream);
 
 #define ST_MAT_SLICES 1u     /* st_materialize_as: the instance with the strided column-slice path */
+/* st_materialize_as: store the outputs with non-temporal stores.  Pass it when the table header
+ * carries ST_TABLE_STREAM_STORES (outputs larger than the last-level cache): measured on MI355X,
+ * 1-3% on whole checkpoints and 6-9% on one rank's column shards; on outputs that fit that cache,
+ * plain stores leave them there and measured faster. */
+#define ST_MAT_STREAM_STORES 2u
 
 /* The general entry point (source: as st_materialize): st_materialize for a table planned with
  * output type out_dtype
- * (st_out_dtype; outs then point to arrays of that type, aligned to it), flags 0 or
- * ST_MAT_SLICES.  One kernel instance per output type: a table planned for another type than
+ * (st_out_dtype; outs then point to arrays of that type, aligned to it), flags 0 or a combination
+ * of ST_MAT_SLICES and ST_MAT_STREAM_STORES.  One kernel instance per output type and flags: a
+ * table planned for another type than
  * out_dtype makes every wavefront return without writing.  ST_E_ARG for an unknown type or
  * flag.  st_materialize = (ST_OUT_BF16, 0); st_materialize_slices = (ST_OUT_BF16, ST_MAT_SLICES). */
 st_status st_materialize_as(const void* blob, const void* descs, size_t n, void* const* outs,
@@ -491,7 +502,8 @@ st_status st_materialize_as(const void* blob, const void* descs, size_t n, void*
  *   table_host  a work table in host memory (st_index_table, st_index_descs, st_index_table_subset or
  *               st_index_table_slices), table_bytes long, n its work-unit count
  *   outs_host   host array of n_outs device output pointers (descriptor d writes outs_host[desc.out])
- *   out_dtype, flags  as st_materialize_as
+ *   out_dtype, flags  as st_materialize_as (ST_MAT_STREAM_STORES is added when the table header
+ *               carries ST_TABLE_STREAM_STORES)
  * table_host and outs_host must stay valid and unchanged until `stream` has passed the launch (the
  * copies are asynchronous).  Limit: round_up(table_bytes, 256) + 8 * n_outs <= ST_NOALLOC_SCRATCH_BYTES
  * (the table takes 64 bytes per output plus 1 byte per work unit: about 32 G fp8 elements in one

@@ -74,7 +74,7 @@ DESC = np.dtype([("src", "<u8"), ("scale", "<u8"), ("scale2", "<u8"), ("pitch", 
                  ("unit_end", "<u4"), ("tail", "<u4"), ("out", "<u4"), ("cols", "<u4"), ("grid_cols", "<u4"),
                  ("div_magic", "<u4"), ("kind", "u1"), ("unit_shift", "u1"), ("div_shift", "u1"), ("r0", "u1")])
 HEADER = np.dtype([("magic", "<u4"), ("n_desc", "<u4"), ("units", "<u8"), ("desc_offset", "<u8"),
-                   ("map_offset", "<u8"), ("bytes", "<u8"), ("out_dtype", "<u4"), ("reserved0", "<u4"),
+                   ("map_offset", "<u8"), ("bytes", "<u8"), ("out_dtype", "<u4"), ("flags", "<u4"),
                    ("reserved", "<u8", 2)])
 
 
@@ -411,7 +411,7 @@ def test_launch_arguments_are_checked_before_any_gpu_call():
         ((ok, C.c_void_p((1 << 20) + 32), 5, ok, 0, 0), "work table is not 64-byte aligned"),
         ((ok, ok, 1 << 32, ok, 0, 0), "at most 2^32 - 1"),
         ((ok, ok, 5, ok, 3, 0), "unknown output type 3"),
-        ((ok, ok, 5, ok, 0, 2), "unknown flags 0x2"),
+        ((ok, ok, 5, ok, 0, 4), "unknown flags 0x4"),
     ]
     for (blob, descs, n, outs, dt, flags), msg in cases:
         assert L.st_materialize_as(blob, descs, n, outs, dt, flags, None) == -1, msg
@@ -449,3 +449,31 @@ def test_staging_refuses_a_file_of_the_wrong_size_before_any_gpu_call(delta, tmp
     assert want in L.st_last_error()
     assert L.st_stage_file(str(tmp_path / "missing").encode(), ix._h, ok, ok, 1 << 30, None, None, None) == -2
     assert b"cannot open" in L.st_last_error()
+
+
+def _header_only(k, out_dtype="bf16"):
+    from synth.st_writer import layout
+    lay = layout(*synth.configs.make_config(k))
+    return st.SafeTensorIndex.from_bytes(lay.header, file_size=len(lay.header) + lay.data_size, out_dtype=out_dtype)
+
+
+def test_tables_with_outputs_past_the_cache_ask_for_stream_stores():
+    """The planner sets ST_TABLE_STREAM_STORES exactly when a table's outputs exceed 256 MiB (the
+    MI355X's Infinity Cache): the large checkpoints, not the tiny or the many-small one (211 MB);
+    subset and slice tables by their own outputs; each streaming step by its own."""
+    limit = 256 << 20
+    for k in (1, 2, 3, 4, 5, 6, 7):
+        ix = _header_only(k)
+        out_bytes = sum(o.numel for o in ix.outputs()) * 2
+        flags = int(_table(ix.table()[0])[0]["flags"])
+        assert flags == (_lib.TABLE_STREAM_STORES if out_bytes > limit else 0), (k, out_bytes, flags)
+        assert st.table_stream_stores(ix.table()[0]) == (out_bytes > limit)
+    ix = _header_only(4)        # 80 weights of 25600 x 5120 (250 MiB each in bf16)
+    outs = ix.outputs()
+    assert outs[0].numel * 2 <= limit
+    assert int(_table(ix.table_subset([0])[0])[0]["flags"]) == 0
+    assert int(_table(ix.table_subset([0, 1])[0])[0]["flags"]) == _lib.TABLE_STREAM_STORES
+    assert int(_table(ix.table_slices([(0, None, (0, 640))])[0])[0]["flags"]) == 0
+    assert int(_table(ix.table_slices([(j, None, None) for j in range(3)])[0])[0]["flags"]) == _lib.TABLE_STREAM_STORES
+    ix32 = _header_only(4, "f32")    # the same weight is 500 MiB in fp32
+    assert int(_table(ix32.table_subset([0])[0])[0]["flags"]) == _lib.TABLE_STREAM_STORES
