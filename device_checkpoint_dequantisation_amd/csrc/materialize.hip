@@ -1045,7 +1045,7 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
     c.scale_al = (D.scale & 3u) == 0;
     if ((D.pitch | D.flags) != 0) {  // column slices, split descriptors and exact-only descriptors
         if (SLICES && (D.flags & (ST_DESC_SPLIT | ST_DESC_EXACT)) == ST_DESC_SPLIT && (cnt & 7u) == 0 &&
-            ((kSplitKinds >> D.kind) & 1u)) {
+            D.kind < 32u && ((kSplitKinds >> D.kind) & 1u)) {
             const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src)), sh = a & 3u;
             switch (D.kind) {
             // whole units of the default size (full_ 1), or of twice it (2: the 8-bit kinds' split units)
