@@ -618,10 +618,11 @@ namespace {
 
 // A work table from descriptors whose unit ranges are set, `units` in total: header, map,
 // descriptors.
-// Outputs larger than this (the MI355X's 256 MiB Infinity Cache) are written with non-temporal
-// stores.  Measured against plain stores: +1 to +3% on the large checkpoints and their row shards,
-// +6 to +9% on one rank's column shards; on the many-small checkpoint (211 MB of outputs) plain
-// stores leave the outputs in that cache and the launch 10% shorter after a flush.
+// Outputs larger than this (the MI355X's 256 MiB Infinity Cache) are written with streaming
+// (non-temporal, system-scope) stores.  Measured against plain stores: +2 to +4% on the large
+// checkpoints and their row shards, +7 to +11% on one rank's column shards; on the many-small
+// checkpoint (211 MB of outputs) plain stores leave the outputs in that cache and the launch 10%
+// shorter after a flush.
 constexpr uint64_t kStreamStoreBytes = uint64_t(256) << 20;
 
 std::vector<unsigned char> assemble(const std::vector<st_desc>& descs, uint64_t units, uint32_t out_dtype,

@@ -475,10 +475,10 @@ st_status st_materialize_slices(const void* blob, const void* descs, size_t n, v
                                 void* stream);
 
 #define ST_MAT_SLICES 1u     /* st_materialize_as: the instance with the strided column-slice path */
-/* st_materialize_as: store the outputs with non-temporal stores.  Pass it when the table header
- * carries ST_TABLE_STREAM_STORES (outputs larger than the last-level cache): measured on MI355X,
- * 1-3% on whole checkpoints and 6-9% on one rank's column shards; on outputs that fit that cache,
- * plain stores leave them there and measured faster. */
+/* st_materialize_as: stream the outputs past the caches (non-temporal, system-scope stores).  Pass
+ * it when the table header carries ST_TABLE_STREAM_STORES (outputs larger than the last-level
+ * cache): measured on MI355X, 2-4% on whole checkpoints and 7-11% on one rank's column shards; on
+ * outputs that fit that cache, plain stores leave them there and measured faster. */
 #define ST_MAT_STREAM_STORES 2u
 
 /* The general entry point (source: as st_materialize): st_materialize for a table planned with
