@@ -51,7 +51,7 @@ struct Piece {
 // pread on the pool's threads and the calling thread; every thread takes part in every batch, so
 // a batch is over once all of them have checked in.  One pool serves the whole process (see
 // Readers below): starting eight threads per call cost a 113 MB per-layer load about 0.1 ms
-// (measured on the GPU machine's host, 2.72-2.82 ms per layer against 2.66).
+// (measured on an MI355X host, 2.72-2.82 ms per layer against 2.66).
 class ReaderPool {
   public:
     ReaderPool() {
