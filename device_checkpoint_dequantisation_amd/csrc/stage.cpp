@@ -14,6 +14,7 @@
 //  * st_read_plan: a plan's ranges straight into host memory (the RAM tier), no GPU calls.
 #include <fcntl.h>
 #include <sys/stat.h>
+#include <sys/uio.h>
 #include <unistd.h>
 
 #include <hip/hip_runtime.h>
@@ -65,11 +66,17 @@ class ReaderPool {
         cv_.notify_all();
         for (auto& t : threads_) t.join();
     }
-    // False if a read failed or hit the end of the file.
+    // False if a read failed or hit the end of the file.  Pieces: ranges whose pages are in the page
+    // cache are memory copies, which the threads share best in pieces of about a (2 * readers)-th of
+    // the batch; ranges still on disk are read in pieces of kColdPiece, since the kernel submits a
+    // read's missing pages together and larger reads keep more of the disk's queue busy (measured
+    // on MI355X hosts, cold 128 MiB batches: 3.3 GB/s in 7 MiB pieces, 6.8 in 32 MiB, 7.3 in 64 MiB).
     bool read(int fd, const std::vector<Piece>& ranges) {
         size_t total = 0;
         for (const Piece& r : ranges) total += r.len;
-        const size_t piece = std::max<size_t>(size_t(1) << 20, (total / (2 * (kReaders + 1)) + 4095) & ~size_t(4095));
+        const size_t piece = in_page_cache(fd, ranges)
+                                 ? std::max<size_t>(size_t(1) << 20, (total / (2 * (kReaders + 1)) + 4095) & ~size_t(4095))
+                                 : kColdPiece;
         std::vector<Piece> pieces;
         for (const Piece& r : ranges)
             for (size_t b = 0; b < r.len; b += piece)
@@ -91,6 +98,25 @@ class ReaderPool {
     }
 
   private:
+    static constexpr size_t kColdPiece = size_t(64) << 20;
+    // Whether the first, middle and last byte of the batch's ranges (the first 16 of them) are in
+    // the page cache: a one-byte preadv2 with RWF_NOWAIT returns EAGAIN instead of waiting for the
+    // disk.  Any other failure (a kernel without RWF_NOWAIT for buffered reads) counts as cached,
+    // which keeps the smaller pieces; the reads themselves report real errors.
+    static bool in_page_cache(int fd, const std::vector<Piece>& ranges) {
+        size_t probed = 0;
+        for (const Piece& r : ranges) {
+            if (r.len == 0) continue;
+            const uint64_t at[3] = {r.off, r.off + r.len / 2, r.off + r.len - 1};
+            for (uint64_t o : at) {
+                char b;
+                struct iovec v = {&b, 1};
+                if (preadv2(fd, &v, 1, off_t(o), RWF_NOWAIT) < 0 && errno == EAGAIN) return false;
+            }
+            if (++probed == 16) break;
+        }
+        return true;
+    }
     void drain() {
         for (size_t i = next_.fetch_add(1); i < pieces_.size(); i = next_.fetch_add(1)) {
             const Piece& p = pieces_[i];

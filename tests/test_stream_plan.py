@@ -337,3 +337,41 @@ def test_read_plans_from_several_threads_and_files(tmp_path):
     for t in threads:
         t.join()
     assert not errors, errors
+
+
+def test_read_plans_after_dropping_the_page_cache(tmp_path):
+    """Ranges whose pages are not in the page cache are read in larger pieces than cached ones
+    (the reader pool asks the kernel, without waiting for the disk, whether the range's first, middle
+    and last bytes are cached).  Both ways land the same bytes: read the file with its pages dropped
+    from the cache (advisory: fsync, then POSIX_FADV_DONTNEED), then again with them cached, and
+    compare every byte.  Three tensors, two of them longer than one cold piece (64 MiB)."""
+    import os
+    import torch
+    rng = np.random.default_rng(11)
+    sizes = [(70 << 20) + 3, 5, (130 << 20) + 1]   # bf16 element counts x 2 bytes, odd offsets after the second
+    tensors = []
+    for k, n in enumerate(sizes):
+        raw = rng.integers(0, 256, size=2 * n, dtype=np.uint8)
+        tensors.append((f"t{k}", "BF16", (n,), raw))
+    buf = make_file(tensors)
+    path = tmp_path / "big.safetensors"
+    path.write_bytes(buf)
+    ix = st.SafeTensorIndex.open(str(path))
+    data = np.frombuffer(buf, np.uint8)[ix.data_offset:]
+    plans = [st.StreamPlan(ix, 96 << 20), st.StreamPlan(ix, 96 << 20, select=[2, 0], pack=True)]
+    for cached in (False, True):
+        for plan in plans:
+            if not cached:   # drop the file's pages before each read
+                fd = os.open(str(path), os.O_RDONLY)
+                try:
+                    os.fsync(fd)
+                    os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+                finally:
+                    os.close(fd)
+            host = torch.full((plan.blob_bytes,), 0xEE, dtype=torch.uint8)
+            st.read_plans(str(path), ix, [plan], [host])
+            hb = host.numpy()
+            for b, e in plan.ranges:
+                d = plan.tensor_offset(b)
+                assert np.array_equal(hb[d: d + e - b], data[b:e])
+    del buf, data
