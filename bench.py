@@ -421,6 +421,46 @@ def end_to_end_loads(path, ix, ck, side, stream, args, rng):
                              "before the whole data section is staged (serial_load_s)"}
 
 
+def cold_loads(path, args, rng):
+    """The serial and the streamed end-to-end load once each after dropping the file's pages from
+    the page cache (run last: reading the file back leaves its pages cached in another state than
+    writing it did, which would change the warm figures measured after it)."""
+    import torch
+    import device_checkpoint_dequantisation_amd as st
+    ix = st.SafeTensorIndex.open(path)
+    dev = torch.device("cuda:0")
+    ck = st.DeviceCheckpoint(ix, None, dev)
+    pinned = torch.empty(512 << 20, dtype=torch.uint8, pin_memory=True)
+    side = torch.cuda.Stream(dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = st.StreamPlan(ix, args.stream_chunk_mb << 20)
+    ck.stream(path, stream=stream, plan=plan)  # allocates the pinned ring once
+    ck.synchronize()
+    out = {}
+    if not drop_page_cache(path):
+        return {"page_cache": "could not be dropped on this host"}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.stage_file(path, ix, ck.blob, pinned, side)
+    side.synchronize()
+    ck.materialize(stream)
+    torch.cuda.synchronize()
+    out["serial_load_GBps"] = round(ix.data_size / (time.perf_counter() - t0) / 1e9, 2)
+    drop_page_cache(path)
+    ck.arena.view(torch.int16).fill_(0x7FBF)   # poison: the streamed load must write every output
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ck.stream(path, stream=stream, plan=plan)
+    ck.synchronize()
+    out["streamed_load_GBps"] = round(ix.data_size / (time.perf_counter() - t0) / 1e9, 2)
+    ok, _, bad = sampled_parity(path, ix, ck, rng)
+    out["streamed_parity"] = "sampled-bit-exact" if ok else f"MISMATCH:{bad}"
+    out["page_cache"] = "dropped before each load (fsync + POSIX_FADV_DONTNEED, advisory)"
+    del pinned, ck
+    torch.cuda.empty_cache()
+    return out
+
+
 SOURCE_BYTES = {"PASS_BF16": 2, "CAST_F16": 2, "CAST_F32": 4, "FP8_TENSOR": 1, "FP8_BLOCK128": 1,
                 "NVFP4": 0.5 + 1 / 16, "MXFP8": 1 + 1 / 32, "MXFP4": 0.5 + 1 / 32}
 
@@ -596,6 +636,9 @@ def main():
         if k == args.config and not args.no_cpu:
             cpu = cpu_baseline(results[k]["path"], args.cpu_seconds)
             log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+        if k == args.config and args.extras:
+            results[k]["cold_loads"] = cold_loads(results[k]["path"], args, rng)
+            log(f"[bench] loads after dropping the page cache: {results[k]['cold_loads']}")
         if not args.keep:
             os.remove(results[k]["path"])
     aligned = None
@@ -629,6 +672,8 @@ def main():
     }
     if "lazy" in r:
         line["lazy_loads"] = r["lazy"]
+    if "cold_loads" in r:
+        line["loads_page_cache_dropped"] = r["cold_loads"]
     if r.get("shards"):
         line["tp_shards"] = r["shards"]
     if r.get("out_types"):
