@@ -424,7 +424,9 @@ def end_to_end_loads(path, ix, ck, side, stream, args, rng):
 def cold_loads(path, args, rng):
     """The serial and the streamed end-to-end load once each after dropping the file's pages from
     the page cache (run last: reading the file back leaves its pages cached in another state than
-    writing it did, which would change the warm figures measured after it)."""
+    writing it did, which would change the warm figures measured after it), and the on-demand
+    per-layer loads without a RAM tier the same way."""
+    import re
     import torch
     import device_checkpoint_dequantisation_amd as st
     ix = st.SafeTensorIndex.open(path)
@@ -455,9 +457,24 @@ def cold_loads(path, args, rng):
     out["streamed_load_GBps"] = round(ix.data_size / (time.perf_counter() - t0) / 1e9, 2)
     ok, _, bad = sampled_parity(path, ix, ck, rng)
     out["streamed_parity"] = "sampled-bit-exact" if ok else f"MISMATCH:{bad}"
-    out["page_cache"] = "dropped before each load (fsync + POSIX_FADV_DONTNEED, advisory)"
     del pinned, ck
     torch.cuda.empty_cache()
+    # on-demand loads, one layer per load, no RAM tier (as lazy_loads' "file")
+    sd = st.StreamStateDict(path, dev, index=ix)
+    groups = {}
+    for k in sd:
+        m = re.match(r"^(.*?\.\d+)\.", k)
+        groups.setdefault(m.group(1) if m else k.split(".")[0], []).append(k)
+    src = sum(sd.meta(k).source_bytes for k in sd)
+    drop_page_cache(path)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for keys in groups.values():
+        got = sd.load(keys)
+        torch.cuda.synchronize()
+        del got
+    out["lazy_per_layer_GBps"] = round(src / (time.perf_counter() - t0) / 1e9, 2)
+    out["page_cache"] = "dropped before each load (fsync + POSIX_FADV_DONTNEED, advisory)"
     return out
 
 
