@@ -304,11 +304,14 @@ class StreamStateDict(Mapping):
     ``keys()``, ``len()``, ``in`` and :meth:`meta` read nothing but the header.  Indexing decodes one
     tensor on the GPU; :meth:`load` decodes several with one read and one upload.  With
     ``ram_cache_bytes`` > 0 the checkpoint bytes of recently loaded outputs stay in pinned host
-    memory (LRU) and later loads of them skip the file; ``ram_preallocate`` pins that memory (up to
-    the checkpoint's size) when the mapping is created instead of while loads fill the tier."""
+    memory (LRU) and later loads of them skip the file.  By default (``ram_preallocate``) that memory is
+    pinned and touched when the mapping is created, up to the checkpoint's size or the bound if smaller:
+    creating pinned memory holds up the process's other HIP calls, and done while loads fill the tier it
+    made filling about 3x slower than reading into memory already pinned (measured on MI355X hosts:
+    9-13 against 35-38 GB/s); ``ram_preallocate=False`` pins slabs as loads need them instead."""
 
     def __init__(self, path: str, device="cuda", ram_cache_bytes: int = 0, index: SafeTensorIndex | None = None,
-                 out_dtype: str = "bf16", steps_per_load: int = 8, ram_preallocate: bool = False):
+                 out_dtype: str = "bf16", steps_per_load: int = 8, ram_preallocate: bool = True):
         self.path = path
         self.index = index if index is not None else SafeTensorIndex.open(path, out_dtype=out_dtype)
         self.device = _torch().device(device)

@@ -67,7 +67,7 @@ def test_ram_tier_hits_and_evictions(k, tmp_path):
         assert np.array_equal(_bits(got[name]).reshape(w.shape), w), name
     # a bound of a third of the bytes: evictions, and still exact results in mixed hit/miss loads
     total = sd.ram.bytes
-    small = st.StreamStateDict(path, DEV, ram_cache_bytes=total // 3)
+    small = st.StreamStateDict(path, DEV, ram_cache_bytes=total // 3, ram_preallocate=False)  # slabs on demand
     rng = np.random.default_rng(k)
     for _ in range(4):
         pick = [names[i] for i in rng.choice(len(names), size=max(1, len(names) // 2), replace=False)]
