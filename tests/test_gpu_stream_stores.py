@@ -65,3 +65,32 @@ def test_column_slices_with_stream_stores(k):
         w = want[outs[j].name].reshape(outs[j].shape[0], -1)
         assert np.array_equal(t.view(torch.int16).cpu().numpy().view(np.uint16), w[:, c0:c1]), (outs[j].name, c0, c1)
 
+
+
+def _every_code_files():
+    from tests.test_gpu_parity import (block_fp8_file, float_every_code_file, fp8_every_code_file, mx_every_code_file,
+                                       nvfp4_every_code_file)
+    return {"fp8": fp8_every_code_file, "nvfp4": nvfp4_every_code_file, "block": lambda s: block_fp8_file(257, 129, s),
+            "float": float_every_code_file, "mxfp8": lambda s: mx_every_code_file("MXFP8", s),
+            "mxfp4": lambda s: mx_every_code_file("MXFP4", s)}
+
+
+@pytest.mark.parametrize("shift", [0, 1, 3, 9])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("name", ["fp8", "nvfp4", "block", "float", "mxfp8", "mxfp4"])
+def test_every_code_with_stream_stores(name, out_dtype, shift):
+    """The every-code files of each kind (NaN codes, special scales, ragged tails) behind a leading
+    tensor that shifts every source off its natural alignment, through the streaming-store instance:
+    its whole units of bf16 copies and MXFP8 load with non-temporal buffer loads, aligned and not."""
+    buf = _every_code_files()[name](shift)
+    want = oracle.materialize(buf, out_dtype)
+    ix = st.SafeTensorIndex.from_bytes(buf, out_dtype=out_dtype)
+    ck = st.DeviceCheckpoint(ix, None, DEV)
+    ck.load_bytes(buf[ix.data_offset:])
+    ck.arena.view(torch.int16).fill_(0x5A5A)
+    print(f"stream stores, every code: {name} {out_dtype} shift {shift}", flush=True)
+    st.materialize(ck.blob, ck.table, ck.units, ck.outs, out_dtype=out_dtype, stream_stores=True)
+    torch.cuda.synchronize()
+    for n, w in want.items():
+        g = ck.tensors[n].view(BITS[out_dtype]).cpu().numpy().view(w.dtype)
+        assert np.array_equal(g.reshape(w.shape), w), n
