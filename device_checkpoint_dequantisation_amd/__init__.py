@@ -598,5 +598,8 @@ def load(path: str, device="cuda", unit_log2_scale: int = 0, streamed: bool = Tr
 from .lazy import (DiskRef, FilterViewStateDict, LazyModuleLoader, OutputMeta, PrefixViewStateDict,  # noqa: E402,F401
                    RamCache, RenameViewStateDict, StreamStateDict)
 
+from .shards import (ShardedStateDict, ShardError, index_shards, load_checkpoint, shard_files)  # noqa: E402,F401
+
 __all__ += ["StreamStateDict", "PrefixViewStateDict", "FilterViewStateDict", "RenameViewStateDict", "RamCache",
-            "LazyModuleLoader", "DiskRef", "OutputMeta"]
+            "LazyModuleLoader", "DiskRef", "OutputMeta", "ShardedStateDict", "ShardError", "index_shards",
+            "load_checkpoint", "shard_files"]
