@@ -211,3 +211,72 @@ def test_other_kinds_keep_one_descriptor_per_shard(case):
     h, d, m = _table(raw)
     assert len(d) == 8 and not any(int(r["flags"]) & _lib.DESC_SPLIT for r in d)
     assert _descs_by_out(d) == list(range(8))
+
+
+def _full_header_index(k):
+    """The index of benchmark config k at full size, built from its header alone."""
+    from synth.st_writer import layout
+    groups, meta, pad = synth.make_config(k)
+    lay = layout(groups, meta, pad)
+    return st.SafeTensorIndex.from_bytes(lay.header, file_size=len(lay.header) + lay.data_size)
+
+
+SOURCE_BITS = {0: 16, 1: 16, 2: 32, 3: 8, 4: 8, 5: 4, 6: 8, 7: 4}
+
+
+def _eighth_bytes(d, units):
+    """Bytes (source + 2-byte output per element) of each eighth of the unit sequence."""
+    ends = d["unit_end"].astype(np.int64)
+    starts = np.concatenate([[0], ends[:-1]])
+    e = np.zeros(8)
+    for row, a, b in zip(d, starts, ends):
+        per = (1 << int(row["unit_shift"])) * (SOURCE_BITS[int(row["kind"])] / 8 + 2)
+        for x in range(8):
+            lo, hi = max(a, units * x // 8), min(b, units * (x + 1) // 8)
+            if hi > lo:
+                e[x] += per * (hi - lo)
+    return e
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_slice_tables_balance_the_xcd_eighths(axis):
+    """8-way shards of every 2-d output of the block-FP8 checkpoint (fp8 layers and a bf16 embedding
+    of more bytes per unit): in request order one eighth would carry the embedding's shards; the
+    planner cuts every large slice into 8 pieces, one per eighth, so the eighths carry equal bytes,
+    and every slice's units are still covered once with the kernel's unit offsets intact."""
+    from tests.test_index import _check_map
+    ix = _full_header_index(3)
+    slices = []
+    for k, o in enumerate(ix.outputs()):
+        if len(o.shape) != 2:
+            slices.append((k, None, None))
+            continue
+        dim = o.shape[axis]
+        q = 128 if o.kind == "FP8_BLOCK128" else 1
+        step = max(q, -(-dim // 8 // q) * q)
+        for b in range(0, dim, step):
+            part = (b, min(dim, b + step))
+            slices.append((k, part, None) if axis == 0 else (k, None, part))
+    raw, units = ix.table_slices(slices)
+    h, d, m = _table(raw)
+    assert len(d) > len(slices)                      # large slices were cut into pieces
+    numels = [int(np.prod(ix.slice_shape(*sl))) for sl in slices]
+    _check_map(d, m, units, numels)
+    e = _eighth_bytes(d, units)
+    assert e.max() / e.mean() < 1.01, e / e.mean()
+
+
+def test_balanced_slice_tables_keep_request_order():
+    """Homogeneous shard tables (the scaled-FP8 checkpoint's row shards) are balanced already and keep
+    one descriptor per slice in request order."""
+    ix = _full_header_index(2)
+    slices = []
+    for k, o in enumerate(ix.outputs()):
+        if len(o.shape) != 2:
+            slices.append((k, None, None))
+            continue
+        R = o.shape[0]
+        slices += [(k, (b, min(R, b + R // 8)), None) for b in range(0, R, R // 8)]
+    raw, units = ix.table_slices(slices)
+    h, d, m = _table(raw)
+    assert len(d) == len(slices) and [int(r["out"]) for r in d] == list(range(len(slices)))
