@@ -314,7 +314,10 @@ typedef struct {
  * scaled-FP8 or MXFP8 output (2, 4, ... 64 shards of equal width, in column order, each below 2^32
  * bytes) become one ST_DESC_SPLIT descriptor that reads those rows whole; other column slices of
  * packed-fp4 outputs that share rows are interleaved in bands of work units so that they read the
- * rows' shared cache lines together; every other slice keeps its own descriptor in request order. */
+ * rows' shared cache lines together; every other slice keeps its own descriptor in request order,
+ * except that when the descriptors' bytes fall unevenly on the GPU's eight XCDs (each takes one
+ * contiguous eighth of the work units), slices of 16,384 units or more are cut into eight pieces,
+ * one per eighth. */
 st_status st_index_table_slices(const st_index* idx, const st_slice* slices, size_t k, void* dst,
                                 size_t dst_bytes, size_t* bytes, uint64_t* units);
 /* Elements of slice `s` once its bounds are resolved (rows * cols), or ST_E_ARG.  Source: as the
