@@ -898,14 +898,6 @@ bool split_desc(const st_index& ix, size_t j, const std::vector<Slice>& gs, cons
     whole.c0 = 0;
     whole.c1 = C;
     *d = make_slice_desc(ix, o, whole, uint32_t(j), 0, units);
-    if (stk::split_wide(o.kind) && ix.unit_log2_scale == 0) {  // units of twice the default size
-        const uint32_t shift = ((d->meta >> 8) & 0xFFu) + 1;
-        const uint64_t numel = whole.rows() * C;
-        *units = (numel + (uint64_t(1) << shift) - 1) >> shift;
-        d->meta = (d->meta & 0xFFFF00FFu) | shift << 8;
-        d->unit_end = uint32_t(*units);
-        d->tail = uint32_t(numel - ((*units ? *units - 1 : 0) << shift));
-    }
     d->flags = ST_DESC_SPLIT;
     d->pitch = uint32_t(C);
     d->cols = uint32_t(W);

@@ -987,11 +987,11 @@ __device__ __forceinline__ void split_store(const Ctx& c, const uint32_t* in, ui
 // Lane l loads shard (l mod 2^grid_cols)'s output pointer once; each chunk takes its shard's from
 // that lane.  Every lane of the wave is active here (the unit test is wave-uniform), as that
 // cross-lane read needs.  As in unit_full, chunks the fast path cannot take go element by element
-// after all the fast stores.  MUL: the unit is MUL times the default size (MUL * CH chunks a lane).
-template <class K, class O, bool ALIGNED, uint32_t MUL>
+// after all the fast stores.
+template <class K, class O, bool ALIGNED>
 __device__ __forceinline__ void unit_split_full(const Ctx& c0, uint64_t e0, uint32_t sh, uint32_t lane) {
     using F = Fetch<K, ALIGNED>;
-    constexpr uint32_t NW = K::CE * O::BYTES / 4, CH = K::CH * MUL;
+    constexpr uint32_t NW = K::CE * O::BYTES / 4, CH = K::CH;
     const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
     uint32_t raw[CH][F::RW];
 #pragma unroll
@@ -1130,28 +1130,20 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(const uint8_t* __re
             D.kind < 32u && ((kSplitKinds >> D.kind) & 1u)) {
             const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(c.blob + c.D.src)), sh = a & 3u;
             switch (D.kind) {
-            // whole units of the default size (full_ 1), or of twice it (2: the 8-bit kinds' split units)
+            // whole units of the default size take the unrolled form, the others walk their chunks
 #define ST_SPLIT_CASE(KIND_, K_)                                                                  \
     case KIND_:                                                                                   \
         static_assert(stk::split_kind(KIND_), "a split kind");                                    \
         {                                                                                         \
-            constexpr uint32_t step_ = stk::step_shift(KIND_, O::CODE);                           \
-            const uint32_t full = cnt != (1u << D.unit_shift) ? 0u : D.unit_shift == step_ ? 1u    \
-                                : D.unit_shift == step_ + 1 ? 2u : 0u;                            \
+            const bool full_ = cnt == (1u << D.unit_shift) && D.unit_shift == stk::step_shift(KIND_, O::CODE); \
             const bool al_ = (a & (K_<O>::LG - 1)) == 0;                                          \
-            if (full == 1) al_ ? unit_split_full<K_<O>, O, true, 1>(c, e0, 0, lane)                \
-                               : unit_split_full<K_<O>, O, false, 1>(c, e0, sh, lane);             \
-            else if constexpr (stk::split_wide(KIND_)) {                                          \
-                if (full == 2) al_ ? unit_split_full<K_<O>, O, true, 2>(c, e0, 0, lane)            \
-                                   : unit_split_full<K_<O>, O, false, 2>(c, e0, sh, lane);         \
-                else unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                              \
-            } else unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                                \
+            if (full_) al_ ? unit_split_full<K_<O>, O, true>(c, e0, 0, lane)                      \
+                           : unit_split_full<K_<O>, O, false>(c, e0, sh, lane);                   \
+            else unit_split_any<K_<O>, O>(c, e0, cnt, sh, lane);                                  \
         }                                                                                         \
         break;
-                ST_SPLIT_CASE(ST_KIND_FP8_TENSOR, KFp8Tensor)
                 ST_SPLIT_CASE(ST_KIND_NVFP4, KFp4)
                 ST_SPLIT_CASE(ST_KIND_MXFP4, KMx4)
-                ST_SPLIT_CASE(ST_KIND_MXFP8, KMx8)
 #undef ST_SPLIT_CASE
                 default: break;  // not a split kind
             }

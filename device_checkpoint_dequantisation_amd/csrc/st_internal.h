@@ -62,16 +62,12 @@ constexpr uint32_t load_word_bytes(uint32_t kind) {
                                                                                                : 16;
 }
 // Kinds whose complete column-shard sets are planned as split descriptors (the source rows read
-// whole, each chunk stored to its shard).  On 8-way shards of the large checkpoints this beat one
-// descriptor per shard by 9% (NVFP4), 6% (MXFP4), 6% (scaled FP8) and 3% (MXFP8); it lost 4% on
-// bf16 (and far more with wide units), and block FP8's scale grid needs the shard's own columns.
-constexpr bool split_kind(uint32_t kind) {
-    return kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4 || kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_MXFP8;
-}
-// Split descriptors of the 8-bit kinds take units of twice the default size: their waves carry half
-// the chunks per lane of the packed fp4 kinds, and the doubled unit spreads the per-wave shard-pointer
-// work over as many (MXFP8 at the default size lost 1% to per-shard descriptors; doubled it gains 3%).
-constexpr bool split_wide(uint32_t kind) { return kind == ST_KIND_FP8_TENSOR || kind == ST_KIND_MXFP8; }
+// whole, each chunk stored to its shard): the packed fp4 kinds.  On 8-way shards of the large
+// checkpoints this beat one descriptor per shard by 14% (NVFP4) and 10% (MXFP4), measured on MI355X
+// with the column-slice path's non-temporal loads; with those loads one descriptor per shard is the
+// faster plan for the 8-bit kinds (MXFP8 +12%, scaled FP8 +3% over split descriptors), for bf16 (4%),
+// and block FP8, whose scale grid needs the shard's own columns.
+constexpr bool split_kind(uint32_t kind) { return kind == ST_KIND_NVFP4 || kind == ST_KIND_MXFP4; }
 // Source bits per element.
 constexpr uint32_t source_bits(uint32_t kind) {
     return kind == ST_KIND_CAST_F32 ? 32

@@ -167,8 +167,8 @@ typedef struct st_desc {
 /* st_desc.flags: a split descriptor decodes every column shard of some rows of one output at once:
  * the source rows are read whole (pitch = their length C), cut into 2^grid_cols shards of cols
  * elements each, and shard s is written to outs[out + s] as a [rows, cols] row-major array.  Planned
- * by st_index_table_slices for a request that lists all column shards of an NVFP4, MXFP4, scaled-FP8
- * or MXFP8 weight in column order; other kinds take the per-element path for it. */
+ * by st_index_table_slices for a request that lists all column shards of an NVFP4 or MXFP4 weight
+ * in column order; other kinds take the per-element path for it. */
 #define ST_DESC_SPLIT 2u
 
 /* Planning options; pass NULL for the defaults. */
@@ -310,9 +310,9 @@ typedef struct {
 /* Work table for slices[0..k) over the data-section blob; slice j is written to outs[j].  Same
  * size-query convention as st_index_table_subset.  ST_E_ARG for an out-of-range output or
  * bounds, ST_E_SHAPE for a cut that splits a scale block or a column slice too large.
- * Planning: consecutive slices that are every column shard of the same rows of one NVFP4, MXFP4,
- * scaled-FP8 or MXFP8 output (2, 4, ... 64 shards of equal width, in column order, each below 2^32
- * bytes) become one ST_DESC_SPLIT descriptor that reads those rows whole; other column slices of
+ * Planning: consecutive slices that are every column shard of the same rows of one NVFP4 or MXFP4
+ * output (2, 4, ... 64 shards of equal width, in column order, each below 2^32 bytes) become one
+ * ST_DESC_SPLIT descriptor that reads those rows whole; other column slices of
  * packed-fp4 outputs that share rows are interleaved in bands of work units so that they read the
  * rows' shared cache lines together; every other slice keeps its own descriptor in request order,
  * except that when the descriptors' bytes fall unevenly on the GPU's eight XCDs (each takes one

@@ -131,8 +131,7 @@ SIBLING_CASES = {
     "mxfp8": [("w.weight", "F8_E4M3", (2048, 4096)), ("w.weight_scale", "F8_E8M0", (2048, 128)), ("b.weight", "BF16", (100,))],
     "bf16": [("w.weight", "BF16", (1024, 2048)), ("b.weight", "BF16", (100,))],
 }
-SPLIT_CASES = ("fp8", "mxfp4", "mxfp8", "nvfp4")   # the kinds whose complete shard sets are split
-WIDE_CASES = ("fp8", "mxfp8")   # split with units twice the default size
+SPLIT_CASES = ("mxfp4", "nvfp4")   # the kinds whose complete shard sets are split
 
 
 def _descs_by_out(d):
@@ -159,7 +158,7 @@ def test_complete_shard_sets_become_split_descriptors(case):
         R = o.shape[0]
         shift = int(sd["unit_shift"])
         _, whole, _ = _table(ix.table_slices([(0, None, None)])[0])
-        assert shift == int(whole[0]["unit_shift"]) + (1 if case in WIDE_CASES else 0)
+        assert shift == int(whole[0]["unit_shift"])
         assert int(sd["unit_end"]) - int(sd["unit_begin"]) == -(-R * C // (1 << shift))
         ents = ix.tensors()
         assert sd["src"] == ents[o.tensor].begin            # whole rows from the first
@@ -198,10 +197,10 @@ def test_shards_that_are_not_a_complete_set_interleave_or_keep_order(case):
             assert outs == list(range(len(slices)))
 
 
-@pytest.mark.parametrize("case", ["block_fp8", "bf16"])
+@pytest.mark.parametrize("case", ["block_fp8", "bf16", "fp8", "mxfp8"])
 def test_other_kinds_keep_one_descriptor_per_shard(case):
-    """Complete shard sets of the kinds outside the split set (block FP8, bf16) keep one descriptor
-    per shard, in request order."""
+    """Complete shard sets of the kinds outside the split set (block FP8, bf16, scaled FP8, MXFP8)
+    keep one descriptor per shard, in request order."""
     spec = ([("w.weight", "F8_E4M3", (1024, 2048)), ("w.weight_scale_inv", "F32", (8, 16))] if case == "block_fp8"
             else SIBLING_CASES[case])
     ix = _header_index(spec)
