@@ -321,7 +321,8 @@ __device__ __forceinline__ void store_elem(uint8_t* out, uint64_t e, uint32_t bi
 // is issued before the decode waits for the chunk's data.  Measured on MI355X: loading early gains
 // about 1% for block FP8 into 2-byte outputs and loses 0.5-1.5% for the others (single-byte scale
 // codes that mostly hit in cache); letting the compiler place the late load after the data wait
-// cost MXFP8 3%.
+// cost MXFP8 3%.  Whole units of packed fp4 into 2-byte outputs fetch all their codes at once
+// instead (UnitCodes).
 
 // Per-unit context.  `s` and `vec` are filled in by finish_ctx, after the data loads are issued;
 // whether the scale folds into the fast path is decided in the decode.
@@ -353,6 +354,9 @@ struct Geom {
     static constexpr bool SC_LOAD = KIND_ == ST_KIND_FP8_BLOCK128 || KIND_ == ST_KIND_NVFP4 || KIND_ == ST_KIND_MXFP8 ||
                                     KIND_ == ST_KIND_MXFP4;
     static constexpr bool EARLY_SC = false;
+    // Packed fp4 whole units (unit_full) fetch their scale codes once per unit (unit_codes); the
+    // elements one code covers, 0 for the other kinds
+    static constexpr uint32_t UNIT_SB = KIND_ == ST_KIND_NVFP4 ? 16 : KIND_ == ST_KIND_MXFP4 ? 32 : 0;
     static_assert(O::BYTES == 4 || (CE == stk::chunk_elems(KIND_) && LG == stk::load_word_bytes(KIND_)),
                   "2-byte outputs use the host planner's geometry");
 };
@@ -653,6 +657,34 @@ __device__ __forceinline__ uint32_t late_sc(const Ctx& c, uint64_t e, uint64_t x
     return s;
 }
 
+// Scale codes of a whole unit of packed fp4 (unit_full).  A unit's codes are contiguous, one byte per
+// 16 (NVFP4) or 32 (MXFP4) elements: 128 or 64 bytes for its 2048 elements.  Lane l fetches word
+// l mod W of them (W: the unit's 4-byte words of codes), as the 8 bytes from the 4-byte boundary at
+// or below it, issued ahead of the data loads; unit_code_word realigns it behind the scheduling
+// barrier and unit_code hands each chunk its code from the lane that holds it (ds_bpermute: every
+// lane of the wavefront is active in unit_full).  Up to 4 bytes past the unit's codes are read,
+// within the blob's tail padding; their values are not used.
+template <class K>
+struct UnitCodes {
+    static constexpr uint32_t W = K::CE * K::CH * stk::kWave / K::UNIT_SB / 4;
+    u32x2_a4 raw;
+    uint32_t sh;
+    __device__ __forceinline__ void load(const Ctx& c, uint64_t e0, uint32_t lane) {
+        const uint8_t* p = c.blob + c.D.scale + e0 / K::UNIT_SB;
+        sh = uint32_t(reinterpret_cast<uintptr_t>(p)) & 3u;
+        raw = *reinterpret_cast<const u32x2_a4*>(p - sh + 4 * (lane % W));
+    }
+    __device__ __forceinline__ uint32_t word() const { return __builtin_amdgcn_alignbyte(raw.y, raw.x, sh); }
+};
+template <class K>
+__device__ __forceinline__ uint32_t unit_code(uint32_t word, uint32_t j, uint32_t lane) {
+    const uint32_t b = (j * stk::kWave + lane) * K::CE / K::UNIT_SB;  // the chunk's code in the unit
+    const uint32_t w = uint32_t(__builtin_amdgcn_ds_bpermute(int((b >> 2) * 4), int(word)));
+    return (w >> (8 * (b & 3))) & 0xFFu;
+}
+// s_waitcnt vmcnt(0), leaving expcnt and lgkmcnt at their maxima (gfx9 encoding)
+constexpr int kWaitVmem0 = 0x0F70;
+
 // The output pointer and the kind's scalar scale, loaded after the unit's data loads are issued.
 // False: the output address is not aligned to the output type, and nothing is written.
 template <class K, class O>
@@ -734,6 +766,8 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
     constexpr uint32_t NW = K::CE * O::BYTES / 4;
     const uint8_t* base = c0.blob + c0.D.src + K::src_off(e0) - sh;
     uint32_t raw[K::CH][F::RW], sc[K::CH];
+    UnitCodes<K> codes;
+    if constexpr (K::UNIT_SB != 0) codes.load(c0, e0, lane);
     if constexpr (load_policy<K, O>() != 0) {
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 0x7FFFFFFF, kRawBufferWord3);
@@ -761,15 +795,27 @@ __device__ __forceinline__ void unit_full(const Ctx& c0, uint64_t e0, uint32_t s
     const bool valid = finish_ctx<K, O>(c, out);
     const bool vec = valid & c.vec;
     uint8_t* const ob = out + e0 * O::BYTES;
+    uint32_t code_word = 0;
+    if constexpr (K::UNIT_SB != 0) code_word = codes.word();
     bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
         const uint64_t e = e0 + uint64_t(j * stk::kWave + lane) * K::CE;
-        const uint32_t s = K::EARLY_SC ? sc[j] : late_sc<K>(c, e, e);
+        uint32_t s;
+        if constexpr (K::UNIT_SB != 0) s = unit_code<K>(code_word, j, lane);
+        else s = K::EARLY_SC ? sc[j] : late_sc<K>(c, e, e);
         uint32_t in[F::N], w[NW];
         F::align(raw[j], sh, in);
         ok[j] = K::fast(c, in, s, w) & vec;
         if (ok[j]) store_chunk<K, O>(ob, j * stk::kWave + lane, w);
+        // Packed fp4: each chunk's store completes before the next chunk's is issued.  Measured on
+        // MI355X, NVFP4 / MXFP4 checkpoints: with this wait the unit-wide code fetch gains 1.0% /
+        // 0.7% over per-chunk code loads (whose own waits spaced the stores the same way); without
+        // it, it loses 2-3%.  Waits that leave one or two stores in flight, or a single wait after
+        // the second chunk, lost 0.8-2%; the same wait on the 8-bit and 2-byte kinds lost 1-2%.
+        if constexpr (K::UNIT_SB != 0) {
+            if (j + 1 < K::CH) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+        }
     }
     bool all = true;
 #pragma unroll

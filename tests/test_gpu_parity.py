@@ -162,6 +162,33 @@ def test_mx_every_code_every_scale(kind, storage, shift):
     assert_parity(mx_every_code_file(kind, shift, storage or "U8"))
 
 
+@pytest.mark.parametrize("kind", ["NVFP4", "MXFP4"])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+def test_fp4_block_scales_last_in_the_file(kind, shift):
+    """Whole packed-fp4 units fetch their block-scale codes as one word per lane, from the 4-byte
+    boundary below them, reading up to 4 bytes past a unit's codes.  With the scale tensor last in
+    the data section, at each alignment, those bytes are the blob's tail padding; NaN codes among
+    the scales send their chunks down the exact path."""
+    rng = np.random.default_rng(40 + shift)
+    M, K = 64, 256                                        # 16,384 elements: 8 whole units
+    packed = rng.integers(0, 256, size=M * K // 2, dtype=np.uint64).astype(np.uint8)
+    tensors = list(_pad(shift))
+    if kind == "NVFP4":
+        sc = rng.integers(0x08, 0x60, size=M * K // 16, dtype=np.uint64).astype(np.uint8)  # e4m3, finite
+        sc[[3, 500, 1023]] = [0x7F, 0xFF, 0x7F]          # NaN codes
+        tensors += [("w.weight_scale_2", "F32", (), f32_bytes(0.75)), ("w.weight", "U8", (M, K // 2), packed),
+                    ("w.weight_scale", "F8_E4M3", (M, K // 16), sc)]
+    else:
+        sc = rng.integers(100, 150, size=M * K // 32, dtype=np.uint64).astype(np.uint8)     # e8m0
+        sc[[5, 300]] = 0xFF                                # NaN codes
+        tensors += [("w.weight", "U8", (M, K // 2), packed), ("w.weight_scale", "F8_E8M0", (M, K // 32), sc)]
+    buf = make_file(tensors)
+    ix = st.SafeTensorIndex.from_bytes(buf)
+    last = max(ix.tensors(), key=lambda t: t.begin)
+    assert last.name == "w.weight_scale" and last.begin % 4 == shift and last.end == ix.data_size
+    assert_parity(buf)
+
+
 def test_many_small_full_stress_config():
     assert_parity(synth.config_bytes(5, count=6000))
 
