@@ -321,8 +321,7 @@ __device__ __forceinline__ void store_elem(uint8_t* out, uint64_t e, uint32_t bi
 // is issued before the decode waits for the chunk's data.  Measured on MI355X: loading early gains
 // about 1% for block FP8 into 2-byte outputs and loses 0.5-1.5% for the others (single-byte scale
 // codes that mostly hit in cache); letting the compiler place the late load after the data wait
-// cost MXFP8 3%.  Whole units of packed fp4 into 2-byte outputs fetch all their codes at once
-// instead (UnitCodes).
+// cost MXFP8 3%.  Whole units of packed fp4 fetch all their codes at once instead (UnitCodes).
 
 // Per-unit context.  `s` and `vec` are filled in by finish_ctx, after the data loads are issued;
 // whether the scale folds into the fast path is decided in the decode.
@@ -354,8 +353,8 @@ struct Geom {
     static constexpr bool SC_LOAD = KIND_ == ST_KIND_FP8_BLOCK128 || KIND_ == ST_KIND_NVFP4 || KIND_ == ST_KIND_MXFP8 ||
                                     KIND_ == ST_KIND_MXFP4;
     static constexpr bool EARLY_SC = false;
-    // Packed fp4 whole units (unit_full) fetch their scale codes once per unit (unit_codes); the
-    // elements one code covers, 0 for the other kinds
+    // Packed fp4 whole units (unit_full, unit_full_paired) fetch their scale codes once per unit
+    // (UnitCodes); the elements one code covers, 0 for the other kinds
     static constexpr uint32_t UNIT_SB = KIND_ == ST_KIND_NVFP4 ? 16 : KIND_ == ST_KIND_MXFP4 ? 32 : 0;
     static_assert(O::BYTES == 4 || (CE == stk::chunk_elems(KIND_) && LG == stk::load_word_bytes(KIND_)),
                   "2-byte outputs use the host planner's geometry");
@@ -657,12 +656,13 @@ __device__ __forceinline__ uint32_t late_sc(const Ctx& c, uint64_t e, uint64_t x
     return s;
 }
 
-// Scale codes of a whole unit of packed fp4 (unit_full).  A unit's codes are contiguous, one byte per
-// 16 (NVFP4) or 32 (MXFP4) elements: 128 or 64 bytes for its 2048 elements.  Lane l fetches word
-// l mod W of them (W: the unit's 4-byte words of codes), as the 8 bytes from the 4-byte boundary at
-// or below it, issued ahead of the data loads; unit_code_word realigns it behind the scheduling
-// barrier and unit_code hands each chunk its code from the lane that holds it (ds_bpermute: every
-// lane of the wavefront is active in unit_full).  Up to 4 bytes past the unit's codes are read,
+// Scale codes of a whole unit of packed fp4 (unit_full, unit_full_paired).  A unit's codes are
+// contiguous, one byte per 16 (NVFP4) or 32 (MXFP4) elements: 128 or 64 bytes for the 2048 elements
+// of a unit into 2-byte outputs, half that into fp32.  Lane l fetches word l mod W of them (W: the
+// unit's 4-byte words of codes), as the 8 bytes from the 4-byte boundary at or below it, issued
+// ahead of the data loads; word() realigns it behind the scheduling barrier and code_at hands each
+// chunk its code from the lane that holds it (ds_bpermute: every lane of the wavefront is active in
+// both unit forms).  Up to 4 bytes past the unit's codes are read,
 // within the blob's tail padding; their values are not used.
 template <class K>
 struct UnitCodes {
@@ -676,11 +676,15 @@ struct UnitCodes {
     }
     __device__ __forceinline__ uint32_t word() const { return __builtin_amdgcn_alignbyte(raw.y, raw.x, sh); }
 };
-template <class K>
-__device__ __forceinline__ uint32_t unit_code(uint32_t word, uint32_t j, uint32_t lane) {
-    const uint32_t b = (j * stk::kWave + lane) * K::CE / K::UNIT_SB;  // the chunk's code in the unit
+// Code b of the unit, from the lane whose word holds it
+__device__ __forceinline__ uint32_t code_at(uint32_t word, uint32_t b) {
     const uint32_t w = uint32_t(__builtin_amdgcn_ds_bpermute(int((b >> 2) * 4), int(word)));
     return (w >> (8 * (b & 3))) & 0xFFu;
+}
+// The code of chunk j * 64 + lane of unit_full
+template <class K>
+__device__ __forceinline__ uint32_t unit_code(uint32_t word, uint32_t j, uint32_t lane) {
+    return code_at(word, (j * stk::kWave + lane) * K::CE / K::UNIT_SB);
 }
 // s_waitcnt vmcnt(0), leaving expcnt and lgkmcnt at their maxima (gfx9 encoding)
 constexpr int kWaitVmem0 = 0x0F70;
@@ -841,6 +845,11 @@ __device__ __forceinline__ void unit_full_paired(const Ctx& c0, uint64_t e0, uin
     const bool odd = (lane & 1u) != 0;
     const uint32_t mine = (lane >> 1) + (odd ? stk::kWave / 2 : 0u);  // the chunk this lane loads
     uint32_t raw[K::CH][F::RW];
+    // The unit's scale codes as in unit_full; here without waits between the stores.  Measured on
+    // MI355X into fp32 against per-chunk code loads: NVFP4 +1.3%, MXFP4 +2.8% (same process); with
+    // the waits, no change.
+    UnitCodes<K> codes;
+    codes.load(c0, e0, lane);
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) F::load(base, j * stk::kWave + mine, raw[j]);
     __builtin_amdgcn_sched_barrier(0);
@@ -849,11 +858,13 @@ __device__ __forceinline__ void unit_full_paired(const Ctx& c0, uint64_t e0, uin
     const bool valid = finish_ctx<K, O>(c, out);  // as in unit_full: no branch before the decode
     const bool vec = valid & c.vec;
     uint8_t* const ob = out + e0 * O::BYTES;
+    const uint32_t code_word = codes.word();
     bool ok[K::CH];
 #pragma unroll
     for (uint32_t j = 0; j < K::CH; ++j) {
         const uint64_t ea = e0 + j * GE + 4 * lane, eb = ea + GE / 2;
-        const uint32_t sa = K::sc(c, ea, ea), sb = late_sc<K>(c, eb, eb);
+        const uint32_t sa = code_at(code_word, (j * GE + 4 * lane) / K::UNIT_SB),
+                       sb = code_at(code_word, (j * GE + GE / 2 + 4 * lane) / K::UNIT_SB);
         uint32_t in[1];
         F::align(raw[j], sh, in);
         // quad_perm(1, 0, 3, 2): the value of lane l ^ 1

@@ -10,8 +10,8 @@ import torch
 import oracle
 import synth
 import device_checkpoint_dequantisation_amd as st
-from tests.test_gpu_parity import (block_fp8_file, float_every_code_file, fp8_every_code_file, mx_every_code_file,
-                                   nvfp4_every_code_file, pieces_file)
+from tests.test_gpu_parity import (block_fp8_file, float_every_code_file, fp4_scales_last_file, fp8_every_code_file,
+                                   mx_every_code_file, nvfp4_every_code_file, pieces_file)
 from tests.test_gpu_slices import _slices_for, _view
 from tests.st_files import make_file
 
@@ -97,6 +97,15 @@ def test_float_sources_every_code(shift, out_dtype):
 @pytest.mark.parametrize("shift", [0, 3])
 def test_mx_every_code(kind, shift, out_dtype):
     assert_parity(mx_every_code_file(kind, shift), out_dtype)
+
+
+@pytest.mark.parametrize("out_dtype", TYPES)
+@pytest.mark.parametrize("kind", ["NVFP4", "MXFP4"])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+def test_fp4_block_scales_last_in_the_file(kind, shift, out_dtype):
+    """The unit-wide scale-code fetch of both fp4 unit forms (fp32: the paired-lane unit) at every
+    alignment of a scale tensor that ends the data section."""
+    assert_parity(fp4_scales_last_file(kind, shift), out_dtype)
 
 
 @pytest.mark.parametrize("out_dtype", TYPES)

@@ -162,15 +162,11 @@ def test_mx_every_code_every_scale(kind, storage, shift):
     assert_parity(mx_every_code_file(kind, shift, storage or "U8"))
 
 
-@pytest.mark.parametrize("kind", ["NVFP4", "MXFP4"])
-@pytest.mark.parametrize("shift", [0, 1, 2, 3])
-def test_fp4_block_scales_last_in_the_file(kind, shift):
-    """Whole packed-fp4 units fetch their block-scale codes as one word per lane, from the 4-byte
-    boundary below them, reading up to 4 bytes past a unit's codes.  With the scale tensor last in
-    the data section, at each alignment, those bytes are the blob's tail padding; NaN codes among
-    the scales send their chunks down the exact path."""
+def fp4_scales_last_file(kind, shift):
+    """Packed fp4 [64, 256] (8 whole units into 2-byte outputs, 16 into fp32) with its block-scale
+    tensor last in the data section, at offset shift mod 4, and NaN codes among the scales."""
     rng = np.random.default_rng(40 + shift)
-    M, K = 64, 256                                        # 16,384 elements: 8 whole units
+    M, K = 64, 256
     packed = rng.integers(0, 256, size=M * K // 2, dtype=np.uint64).astype(np.uint8)
     tensors = list(_pad(shift))
     if kind == "NVFP4":
@@ -186,7 +182,17 @@ def test_fp4_block_scales_last_in_the_file(kind, shift):
     ix = st.SafeTensorIndex.from_bytes(buf)
     last = max(ix.tensors(), key=lambda t: t.begin)
     assert last.name == "w.weight_scale" and last.begin % 4 == shift and last.end == ix.data_size
-    assert_parity(buf)
+    return buf
+
+
+@pytest.mark.parametrize("kind", ["NVFP4", "MXFP4"])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+def test_fp4_block_scales_last_in_the_file(kind, shift):
+    """Whole packed-fp4 units fetch their block-scale codes as one word per lane, from the 4-byte
+    boundary below them, reading up to 4 bytes past a unit's codes.  With the scale tensor last in
+    the data section, at each alignment, those bytes are the blob's tail padding; NaN codes among
+    the scales send their chunks down the exact path."""
+    assert_parity(fp4_scales_last_file(kind, shift))
 
 
 def test_many_small_full_stress_config():
