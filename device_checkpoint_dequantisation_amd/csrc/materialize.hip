@@ -662,11 +662,11 @@ __device__ __forceinline__ uint32_t late_sc(const Ctx& c, uint64_t e, uint64_t x
 // unit's 4-byte words of codes), as the 8 bytes from the 4-byte boundary at or below it, issued
 // ahead of the data loads; word() realigns it behind the scheduling barrier and code_at hands each
 // chunk its code from the lane that holds it (ds_bpermute: every lane of the wavefront is active in
-// both unit forms).  Up to 4 bytes past the unit's codes are read,
-// within the blob's tail padding; their values are not used.
+// both unit forms).  Up to 4 bytes past the unit's codes are read, within the blob's tail padding;
+// their values are not used.
 template <class K>
 struct UnitCodes {
-    static constexpr uint32_t W = K::CE * K::CH * stk::kWave / K::UNIT_SB / 4;
+    static constexpr uint32_t W = K::UNIT_SB ? K::CE * K::CH * stk::kWave / K::UNIT_SB / 4 : 1;
     u32x2_a4 raw;
     uint32_t sh;
     __device__ __forceinline__ void load(const Ctx& c, uint64_t e0, uint32_t lane) {
